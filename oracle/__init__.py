@@ -1,0 +1,26 @@
+"""CPU oracle for the ResidualQuant hot path (test infrastructure only).
+
+Only the tests, the smoke entry point and the benchmark's CPU-baseline leg may
+import this package; the GPU path shares no code with it.
+"""
+from .rq_oracle import (  # noqa: F401
+    GROUP,
+    assign_codes,
+    attention,
+    bf16_to_f64,
+    decode_attn,
+    dequantize,
+    encode,
+    f16_to_f64,
+    f64_to_bf16,
+    f64_to_f16,
+    hadamard,
+    level_offset,
+    ls_scale,
+    pack_codes,
+    quantize_groups,
+    reconstruct,
+    reconstruction_error,
+    rotate,
+    unpack_codes,
+)

@@ -1,0 +1,73 @@
+"""Pins for the oracle's decode attention: brute force on tiny shapes, the
+special cases S=1, equal keys and zero query, permutation invariance and the
+GQA head mapping."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _brute(q, k, v):
+    """Explicit softmax with Python floats, scale 1/sqrt(D)."""
+    d = len(q)
+    z = [sum(q[i] * kt[i] for i in range(d)) / math.sqrt(d) for kt in k]
+    e = [math.exp(zt) for zt in z]
+    tot = sum(e)
+    return [sum(e[t] * v[t][i] for t in range(len(k))) / tot for i in range(d)]
+
+
+@pytest.mark.parametrize("s", [1, 2, 5, 8])
+def test_matches_brute_force(s):
+    rng = np.random.default_rng(s)
+    d = 8
+    q = rng.standard_normal((3, d))
+    k = rng.standard_normal((s, d)) * 2
+    v = rng.standard_normal((s, d))
+    out = oracle.attention(q, k, v, 1.0 / math.sqrt(d))
+    for r in range(3):
+        np.testing.assert_allclose(out[r], _brute(list(q[r]), k.tolist(), v.tolist()), rtol=1e-12, atol=1e-14)
+
+
+def test_special_cases():
+    rng = np.random.default_rng(0)
+    d = 16
+    v = rng.standard_normal((6, d))
+    k = rng.standard_normal((6, d))
+    q = rng.standard_normal((2, d))
+    # one position: the output is that position's value
+    np.testing.assert_allclose(oracle.attention(q, k[:1], v[:1], 0.25), np.repeat(v[:1], 2, 0), atol=1e-15)
+    # all keys equal, or a zero query: the mean of the values
+    kk = np.repeat(k[:1], 6, 0)
+    np.testing.assert_allclose(oracle.attention(q, kk, v, 0.25), np.repeat(v.mean(0, keepdims=True), 2, 0), atol=1e-14)
+    np.testing.assert_allclose(oracle.attention(np.zeros((1, d)), k, v, 0.25), v.mean(0, keepdims=True), atol=1e-14)
+    # permutation of positions does not change the result
+    perm = rng.permutation(6)
+    np.testing.assert_allclose(oracle.attention(q, k[perm], v[perm], 0.25), oracle.attention(q, k, v, 0.25), atol=1e-14)
+
+
+def test_gqa_head_mapping():
+    """Query head h reads kv head h // G (consecutive query heads share a kv head)."""
+    n_loops, batch, hkv, g, d = 1, 1, 3, 2, 8
+    k = [np.zeros((batch, hkv, 1, d))]
+    v = [np.zeros((batch, hkv, 1, d))]
+    for h in range(hkv):
+        v[0][0, h, 0, :] = h + 1
+    q = np.zeros((n_loops, batch, hkv * g, d), dtype=np.uint16)
+    out = oracle.decode_attn(q, k, v)
+    for h in range(hkv * g):
+        assert np.all(out[0, 0, h] == h // g + 1)
+
+
+def test_decode_scale_and_loops():
+    rng = np.random.default_rng(4)
+    n_loops, batch, hkv, g, d, s = 2, 1, 1, 2, 8, 5
+    q_bits = (rng.integers(0x3C00, 0x4000, size=(n_loops, batch, hkv * g, d))).astype(np.uint16)
+    k = [rng.standard_normal((batch, hkv, s, d)) for _ in range(n_loops)]
+    v = [rng.standard_normal((batch, hkv, s, d)) for _ in range(n_loops)]
+    out = oracle.decode_attn(q_bits, k, v)
+    q = oracle.bf16_to_f64(q_bits)
+    for l in range(n_loops):
+        for h in range(hkv * g):
+            np.testing.assert_allclose(out[l, 0, h], _brute(list(q[l, 0, h]), k[l][0, 0].tolist(), v[l][0, 0].tolist()), rtol=1e-12)
