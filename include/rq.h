@@ -1,0 +1,159 @@
+/*
+ * rq.h - C ABI of librq, the MI355X (gfx950) ResidualQuant hot path.
+ *
+ * ResidualQuant (newx.sg page, Abstract) stores the KV cache of a looped
+ * Transformer like this: the final loop's K/V is kept as the reference, and
+ * every earlier loop is kept only as a low-precision residual against it. The
+ * residual is rotated and scaled by a least-squares fit. A loop-wise
+ * mixed-precision table picks INT2 or INT4 per loop. The paperaft JSON page
+ * (`summary`) adds that a serving stack must encode, decode and attend over
+ * this custom format. This library provides exactly those operations:
+ *
+ *   rq_encode          rotate + quantize + pack the residuals of one tensor
+ *   rq_reconstruct     materialise one loop's K or V from ref + residual
+ *   rq_decode_attn     fused reconstruct + single-query decode attention
+ *   rq_decode_attn_bf16  the same decode attention over plain bf16 K/V per
+ *                        loop (the uncompressed baseline)
+ *
+ * FORMAT (RQ_FORMAT_VERSION 1)
+ *   Dense tensors are [batch][n_kv_heads][seq_len][head_dim], head_dim
+ *   contiguous. bf16 and fp16 travel as uint16_t bit patterns.
+ *   Rotation: y = H r, where H is the normalised Sylvester Walsh-Hadamard
+ *   matrix of order head_dim and r = x_loop - x_ref.
+ *   Groups: 32 consecutive coordinates of y share one scale.
+ *   Codes: one pass at the absmax step s0 = max|y_g| / (2^(b-1) - 1/2):
+ *   c = clamp(floor(y / s0) + 2^(b-1), 0, 2^b - 1). The level is
+ *   q = c - (2^(b-1) - 1/2), so INT2 levels are {-1.5, -0.5, 0.5, 1.5}.
+ *   Scale: s = <y_g, q_g> / <q_g, q_g>, stored as IEEE fp16 (round to nearest
+ *   even, saturated at 65504). An all-zero group stores codes 2^(b-1) and
+ *   s = 0, so a zero residual reconstructs the reference exactly.
+ *   codes:  [batch][n_kv_heads][seq_len][head_dim*bits/32] uint32. Word w
+ *           holds coordinates [(32/b)w, (32/b)(w+1)); coordinate j of the word
+ *           sits at bits [b*j, b*j+b).
+ *   scales: [batch][n_kv_heads][seq_len][head_dim/32] fp16.
+ *   Reconstruction: x_hat = x_ref + H (s * q).
+ *
+ * CONVENTIONS
+ *   Every tensor pointer is a device pointer owned by the caller, and must be
+ *   16-byte aligned. The library allocates nothing and keeps no pointer after
+ *   a call returns. Kernels are enqueued on `stream` (a hipStream_t; NULL
+ *   means the default stream) and the library never synchronises. Inputs must
+ *   stay valid until the stream has run the work. Outputs must not alias
+ *   inputs. The library holds no state, so calls on different streams may run
+ *   concurrently.
+ *   Every call returns an rq_status. All checks except RQ_EHIP run on the host
+ *   before any HIP call, and a failed check enqueues nothing. RQ_EHIP reports
+ *   a launch error; faults inside a kernel show up at the caller's next
+ *   synchronisation.
+ */
+#ifndef RQ_H
+#define RQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RQ_FORMAT_VERSION 1
+#define RQ_GROUP 32
+#define RQ_MAX_LOOPS 8
+
+typedef enum rq_status {
+  RQ_OK = 0,
+  RQ_EINVAL = -1,        /* null pointer, non-positive size, n_q_heads % n_kv_heads != 0,
+                            n_loops outside [1, RQ_MAX_LOOPS], non-finite softmax scale */
+  RQ_EUNSUPPORTED = -2,  /* head_dim not in {64, 128}, bits not in {0, 2, 4} (not 0 for
+                            rq_encode), query heads per kv head above 32, bad out_dtype */
+  RQ_EALIGN = -3,        /* a pointer is not 16-byte aligned */
+  RQ_EWORKSPACE = -4,    /* workspace NULL or smaller than the size query returned */
+  RQ_EHIP = -5           /* the HIP runtime reported an error at launch */
+} rq_status;
+
+enum { RQ_OUT_F32 = 0, RQ_OUT_BF16 = 1 };
+
+typedef struct rq_shape {
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t seq_len;
+  int32_t head_dim; /* 64 or 128 */
+} rq_shape;
+
+/* One loop of the cache as rq_decode_attn reads it. bits = 0 marks the final
+   loop (the reference itself; code and scale pointers are ignored and may be
+   NULL). bits = 2 or 4 is a residual loop in the format above. */
+typedef struct rq_loop_view {
+  int32_t bits;
+  const uint32_t* k_codes;
+  const uint16_t* k_scales;
+  const uint32_t* v_codes;
+  const uint16_t* v_scales;
+} rq_loop_view;
+
+/* Encode the residuals of n_loops loops of one tensor (K or V) against the
+ * final-loop reference (ResidualQuant, newx.sg page, Abstract: the earlier
+ * loops are stored as rotated, least-squares-scaled low-bit residuals).
+ * The reference is read once for all loops.
+ *   x[i]      bf16 [B][Hkv][S][D], loop i's states (host array of n_loops device pointers)
+ *   bits[i]   2 or 4 (host array)
+ *   ref       bf16 [B][Hkv][S][D], the final loop
+ *   codes[i]  out: uint32 [B][Hkv][S][D*bits[i]/32]
+ *   scales[i] out: fp16  [B][Hkv][S][D/32]
+ * The output is deterministic: it depends only on the inputs. */
+int rq_encode(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
+              const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, void* stream);
+
+/* Materialise one loop: out = ref + H (s * q) (ResidualQuant, newx.sg page,
+ * Abstract: the residual format keeps reconstruction cheap).
+ *   bits 0 copies ref. out_dtype RQ_OUT_F32 writes float [B][Hkv][S][D];
+ *   RQ_OUT_BF16 writes bf16 bits rounded to nearest even. */
+int rq_reconstruct(const rq_shape* shape, int32_t bits, const uint16_t* ref, const uint32_t* codes,
+                   const uint16_t* scales, int32_t out_dtype, void* out, void* stream);
+
+/* Split count rq_decode_attn / rq_decode_attn_bf16 will use for a request of
+ * n_splits (0 = automatic). Host only. Returns <= 0 on invalid arguments. */
+int32_t rq_decode_attn_splits(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits);
+
+/* Workspace bytes needed by rq_decode_attn and rq_decode_attn_bf16 for these
+ * arguments (host only; 0 on invalid arguments). The caller allocates it. */
+size_t rq_decode_attn_workspace(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits);
+
+/* Fused decode attention over the residual cache (ResidualQuant, newx.sg
+ * page, Abstract: a smaller cache means less KV memory traffic per decode
+ * step). For each loop i, batch b and query head h, with kv = h / (Hq/Hkv):
+ *   k_hat_t = k_ref_t + H (s_k * q_k)_t   (k_ref_t alone when bits = 0)
+ *   v_hat_t likewise,
+ *   out[i][b][h] = sum_t softmax_t(scale * q[i][b][h] . k_hat_t) v_hat_t
+ * over all seq_len cached positions, with no mask. The reference is streamed
+ * once for all loops of the call.
+ *   q        bf16 [n_loops][B][Hq][D]
+ *   k_ref, v_ref  bf16 [B][Hkv][S][D]
+ *   loops    host array [n_loops]
+ *   out      float [n_loops][B][Hq][D]
+ *   softmax_scale: usually 1/sqrt(D); n_splits: 0 = automatic.
+ * Results are identical from run to run for the same n_splits. */
+int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                   const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
+                   float softmax_scale, int32_t n_splits, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* The uncompressed baseline: the same decode attention where loop i attends
+ * over its own bf16 K/V, k[i] and v[i] (host arrays of device pointers, each
+ * bf16 [B][Hkv][S][D]). Same q / out layout, workspace query and split rule. */
+int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                        const uint16_t* const* k, const uint16_t* const* v, float softmax_scale,
+                        int32_t n_splits, float* out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Static description of a status code. */
+const char* rq_status_str(int status);
+
+/* RQ_FORMAT_VERSION of the library as built. */
+int32_t rq_format_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RQ_H */

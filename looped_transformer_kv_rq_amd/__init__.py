@@ -1,0 +1,289 @@
+"""Python face of librq, the MI355X ResidualQuant hot path.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI declared in include/rq.h. PyTorch provides device memory and streams.
+The names follow the C entry points (rq_encode -> encode, ...).
+
+bf16 tensors are torch.bfloat16, fp16 scales torch.float16, packed code
+words torch.int32 (the bit patterns of the uint32 words).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import NamedTuple, Optional, Sequence
+
+import torch
+
+__all__ = [
+    "LoopView", "RQError", "encode", "encode_into", "reconstruct", "decode_attn", "decode_attn_bf16",
+    "decode_workspace_bytes", "decode_splits", "format_version", "library_path",
+    "RQ_OK", "RQ_EINVAL", "RQ_EUNSUPPORTED", "RQ_EALIGN", "RQ_EWORKSPACE", "RQ_EHIP", "MAX_LOOPS",
+]
+
+RQ_OK, RQ_EINVAL, RQ_EUNSUPPORTED, RQ_EALIGN, RQ_EWORKSPACE, RQ_EHIP = 0, -1, -2, -3, -4, -5
+RQ_OUT_F32, RQ_OUT_BF16 = 0, 1
+MAX_LOOPS = 8
+GROUP = 32
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "librq.so")
+_lib = None
+
+
+class RQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_lib.rq_status_str(status).decode() if _lib else status} (status {status})")
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class _LoopView(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+                ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p)]
+
+
+class LoopView(NamedTuple):
+    """One loop of the cache for decode_attn. bits = 0: the reference loop."""
+    bits: int
+    k_codes: Optional[torch.Tensor] = None
+    k_scales: Optional[torch.Tensor] = None
+    v_codes: Optional[torch.Tensor] = None
+    v_scales: Optional[torch.Tensor] = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"librq.so is not built ({_LIB_PATH}); run `python -m looped_transformer_kv_rq_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "rq_encode": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, ctypes.POINTER(I32), P, PP, PP, P]),
+        "rq_reconstruct": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, P, P, P, I32, P, P]),
+        "rq_decode_attn_splits": (I32, [ctypes.POINTER(_Shape), I32, I32, I32]),
+        "rq_decode_attn_workspace": (SZ, [ctypes.POINTER(_Shape), I32, I32, I32]),
+        "rq_decode_attn": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, P, P, ctypes.POINTER(_LoopView),
+                                          F, I32, P, P, SZ, P]),
+        "rq_decode_attn_bf16": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, PP, PP, F, I32, P, P, SZ, P]),
+        "rq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "rq_format_version": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def format_version() -> int:
+    return _load().rq_format_version()
+
+
+# ---------------------------------------------------------------------------
+# argument checks (dtype / device / layout) before the FFI call
+# ---------------------------------------------------------------------------
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shape_of(t: torch.Tensor) -> _Shape:
+    if t.dim() != 4:
+        raise ValueError("KV tensors are [batch, n_kv_heads, seq_len, head_dim]")
+    b, h, s, d = t.shape
+    return _Shape(b, h, s, d)
+
+
+def _stream(device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def _check(status: int, what: str):
+    if status != RQ_OK:
+        raise RQError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def encode_into(xs: Sequence[torch.Tensor], ref: torch.Tensor, bits: Sequence[int],
+                codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor], stream=None) -> None:
+    """rq_encode into caller-provided outputs."""
+    lib = _load()
+    shp = _shape_of(ref)
+    b, h, s, d = ref.shape
+    _need(ref, "ref", torch.bfloat16, ref.shape)
+    n = len(xs)
+    if not (len(bits) == len(codes) == len(scales) == n):
+        raise ValueError("xs, bits, codes and scales must have one entry per loop")
+    for i in range(n):
+        _need(xs[i], f"xs[{i}]", torch.bfloat16, ref.shape, ref.device)
+        _need(codes[i], f"codes[{i}]", torch.int32, (b, h, s, d * int(bits[i]) // 32), ref.device)
+        _need(scales[i], f"scales[{i}]", torch.float16, (b, h, s, d // GROUP), ref.device)
+    bits_arr = (ctypes.c_int32 * n)(*[int(x) for x in bits])
+    st = lib.rq_encode(ctypes.byref(shp), n, _ptr_array(xs), bits_arr, _ptr(ref), _ptr_array(codes),
+                       _ptr_array(scales), _stream(ref.device, stream))
+    _check(st, "rq_encode")
+
+
+def encode(xs: Sequence[torch.Tensor], ref: torch.Tensor, bits: Sequence[int], stream=None):
+    """Encode loops xs[i] (bf16 [B,Hkv,S,D]) against the final-loop ref.
+    Returns (codes, scales): per loop int32 [B,Hkv,S,D*bits/32] and fp16 [B,Hkv,S,D/32]."""
+    if ref.dim() != 4:
+        raise ValueError("ref must be [batch, n_kv_heads, seq_len, head_dim]")
+    b, h, s, d = ref.shape
+    for x in bits:
+        if int(x) not in (2, 4):
+            raise ValueError("encode bit widths must be 2 or 4")
+    codes = [torch.empty((b, h, s, d * int(x) // 32), dtype=torch.int32, device=ref.device) for x in bits]
+    scales = [torch.empty((b, h, s, d // GROUP), dtype=torch.float16, device=ref.device) for _ in bits]
+    encode_into(xs, ref, bits, codes, scales, stream)
+    return codes, scales
+
+
+def reconstruct(ref: torch.Tensor, codes: Optional[torch.Tensor], scales: Optional[torch.Tensor], bits: int,
+                out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None, stream=None):
+    """x_hat = ref + H (s * q); bits = 0 returns a copy of ref. float32 or bfloat16 output."""
+    lib = _load()
+    shp = _shape_of(ref)
+    _need(ref, "ref", torch.bfloat16, ref.shape)
+    b, h, s, d = ref.shape
+    if bits:
+        _need(codes, "codes", torch.int32, (b, h, s, d * bits // 32), ref.device)
+        _need(scales, "scales", torch.float16, (b, h, s, d // GROUP), ref.device)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty(ref.shape, dtype=out_dtype, device=ref.device)
+    _need(out, "out", out_dtype, ref.shape, ref.device)
+    kind = RQ_OUT_F32 if out_dtype == torch.float32 else RQ_OUT_BF16
+    st = lib.rq_reconstruct(ctypes.byref(shp), int(bits), _ptr(ref), _ptr(codes if bits else None),
+                            _ptr(scales if bits else None), kind, _ptr(out), _stream(ref.device, stream))
+    _check(st, "rq_reconstruct")
+    return out
+
+
+def decode_splits(batch: int, n_kv_heads: int, seq_len: int, head_dim: int, n_q_heads: int, n_loops: int,
+                  n_splits: int = 0) -> int:
+    shp = _Shape(batch, n_kv_heads, seq_len, head_dim)
+    return _load().rq_decode_attn_splits(ctypes.byref(shp), n_q_heads, n_loops, n_splits)
+
+
+def decode_workspace_bytes(batch: int, n_kv_heads: int, seq_len: int, head_dim: int, n_q_heads: int,
+                           n_loops: int, n_splits: int = 0) -> int:
+    shp = _Shape(batch, n_kv_heads, seq_len, head_dim)
+    return _load().rq_decode_attn_workspace(ctypes.byref(shp), n_q_heads, n_loops, n_splits)
+
+
+def _workspace(ref, n_q_heads, n_loops, n_splits, workspace):
+    b, h, s, d = ref.shape
+    need = decode_workspace_bytes(b, h, s, d, n_q_heads, n_loops, n_splits)
+    if need == 0:
+        raise RQError(RQ_EINVAL, "decode workspace query")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=ref.device)
+    return workspace
+
+
+def decode_attn(q: torch.Tensor, k_ref: torch.Tensor, v_ref: torch.Tensor, loops: Sequence[LoopView],
+                softmax_scale: Optional[float] = None, n_splits: int = 0, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Fused reconstruct + single-query decode attention over the residual cache.
+    q: bf16 [n_loops, B, Hq, D]; returns float32 [n_loops, B, Hq, D]."""
+    lib = _load()
+    shp = _shape_of(k_ref)
+    b, h, s, d = k_ref.shape
+    if q.dim() != 4:
+        raise ValueError("q must be [n_loops, batch, n_q_heads, head_dim]")
+    n_loops, _, hq, _ = q.shape
+    _need(q, "q", torch.bfloat16, (n_loops, b, hq, d), k_ref.device)
+    _need(k_ref, "k_ref", torch.bfloat16, k_ref.shape)
+    _need(v_ref, "v_ref", torch.bfloat16, k_ref.shape, k_ref.device)
+    if len(loops) != n_loops:
+        raise ValueError("one LoopView per loop of q")
+    views = (_LoopView * n_loops)()
+    for i, lv in enumerate(loops):
+        views[i].bits = int(lv.bits)
+        if lv.bits:
+            _need(lv.k_codes, f"loops[{i}].k_codes", torch.int32, (b, h, s, d * lv.bits // 32), k_ref.device)
+            _need(lv.v_codes, f"loops[{i}].v_codes", torch.int32, (b, h, s, d * lv.bits // 32), k_ref.device)
+            _need(lv.k_scales, f"loops[{i}].k_scales", torch.float16, (b, h, s, d // GROUP), k_ref.device)
+            _need(lv.v_scales, f"loops[{i}].v_scales", torch.float16, (b, h, s, d // GROUP), k_ref.device)
+            views[i].k_codes = lv.k_codes.data_ptr()
+            views[i].k_scales = lv.k_scales.data_ptr()
+            views[i].v_codes = lv.v_codes.data_ptr()
+            views[i].v_scales = lv.v_scales.data_ptr()
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((n_loops, b, hq, d), dtype=torch.float32, device=k_ref.device)
+    _need(out, "out", torch.float32, (n_loops, b, hq, d), k_ref.device)
+    workspace = _workspace(k_ref, hq, n_loops, n_splits, workspace)
+    st = lib.rq_decode_attn(ctypes.byref(shp), hq, n_loops, _ptr(q), _ptr(k_ref), _ptr(v_ref), views,
+                            float(softmax_scale), int(n_splits), _ptr(out), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(k_ref.device, stream))
+    _check(st, "rq_decode_attn")
+    return out
+
+
+def decode_attn_bf16(q: torch.Tensor, k: Sequence[torch.Tensor], v: Sequence[torch.Tensor],
+                     softmax_scale: Optional[float] = None, n_splits: int = 0, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The uncompressed baseline: loop i attends over its own bf16 K/V (k[i], v[i])."""
+    lib = _load()
+    n_loops, _, hq, _ = q.shape
+    if len(k) != n_loops or len(v) != n_loops:
+        raise ValueError("one K and one V per loop of q")
+    shp = _shape_of(k[0])
+    b, h, s, d = k[0].shape
+    _need(q, "q", torch.bfloat16, (n_loops, b, hq, d), k[0].device)
+    for i in range(n_loops):
+        _need(k[i], f"k[{i}]", torch.bfloat16, k[0].shape, k[0].device)
+        _need(v[i], f"v[{i}]", torch.bfloat16, k[0].shape, k[0].device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((n_loops, b, hq, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (n_loops, b, hq, d), q.device)
+    workspace = _workspace(k[0], hq, n_loops, n_splits, workspace)
+    st = lib.rq_decode_attn_bf16(ctypes.byref(shp), hq, n_loops, _ptr(q), _ptr_array(k), _ptr_array(v),
+                                 float(softmax_scale), int(n_splits), _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(q.device, stream))
+    _check(st, "rq_decode_attn_bf16")
+    return out

@@ -1,0 +1,254 @@
+// C ABI of librq: argument checks (host only, before any HIP call), split
+// planning, and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "rq.h"
+#include "rq_internal.h"
+
+namespace {
+
+using namespace rq;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// RQ_OK, RQ_EINVAL or RQ_EUNSUPPORTED
+int check_shape(const rq_shape* s) {
+  if (s == nullptr) return RQ_EINVAL;
+  if (s->batch <= 0 || s->n_kv_heads <= 0 || s->seq_len <= 0 || s->head_dim <= 0) return RQ_EINVAL;
+  if (s->head_dim != 64 && s->head_dim != 128) return RQ_EUNSUPPORTED;
+  return RQ_OK;
+}
+
+int64_t n_vectors(const rq_shape* s) { return (int64_t)s->batch * s->n_kv_heads * s->seq_len; }
+
+int check_heads(const rq_shape* s, int32_t n_q_heads, int32_t n_loops) {
+  int st = check_shape(s);
+  if (st != RQ_OK) return st;
+  if (n_q_heads <= 0 || n_q_heads % s->n_kv_heads != 0) return RQ_EINVAL;
+  if (n_loops < 1 || n_loops > kMaxLoops) return RQ_EINVAL;
+  if (n_q_heads / s->n_kv_heads > 32) return RQ_EUNSUPPORTED;
+  return RQ_OK;
+}
+
+// Target number of partial blocks per launch; a split never holds fewer
+// tokens than one tile.
+constexpr int64_t kTargetBlocks = 2048;
+
+struct SplitPlan {
+  int32_t n_splits;
+  int32_t tokens_per_split;
+};
+
+SplitPlan plan_splits(const rq_shape* s, int32_t requested) {
+  const int64_t rows = (int64_t)s->batch * s->n_kv_heads;
+  const int64_t max_splits = (s->seq_len + kDecodeTile - 1) / kDecodeTile;
+  int64_t n = requested > 0 ? requested : (kTargetBlocks + rows - 1) / rows;
+  if (n < 1) n = 1;
+  if (n > max_splits) n = max_splits;
+  int64_t tps = (s->seq_len + n - 1) / n;
+  tps = (tps + kDecodeTile - 1) / kDecodeTile * kDecodeTile;
+  n = (s->seq_len + tps - 1) / tps;
+  return {(int32_t)n, (int32_t)tps};
+}
+
+size_t workspace_bytes_for(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int32_t n_splits) {
+  return (size_t)n_loops * s->batch * n_q_heads * n_splits * (s->head_dim + 2) * sizeof(float);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RQ_OK : RQ_EHIP; }
+
+int run_combine(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int32_t n_splits, const float* ws,
+                float* out, hipStream_t stream) {
+  CombineArgs c{};
+  c.ws = ws;
+  c.out = out;
+  c.n_out = (int64_t)n_loops * s->batch * n_q_heads;
+  c.n_splits = n_splits;
+  return hip_status(launch_combine(c, s->head_dim, stream));
+}
+
+void fill_common(DecodeArgs& a, const rq_shape* s, int32_t n_q_heads, const uint16_t* q, float softmax_scale,
+                 const SplitPlan& p, void* workspace) {
+  a.q = q;
+  a.ws = static_cast<float*>(workspace);
+  a.group = n_q_heads / s->n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = s->n_kv_heads;
+  a.batch = s->batch;
+  a.seq_len = s->seq_len;
+  a.n_splits = p.n_splits;
+  a.tokens_per_split = p.tokens_per_split;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rq_encode(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
+              const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, void* stream) {
+  int st = check_shape(shape);
+  if (st != RQ_OK) return st;
+  if (n_loops < 1 || n_loops > kMaxLoops) return RQ_EINVAL;
+  if (x == nullptr || bits == nullptr || ref == nullptr || codes == nullptr || scales == nullptr) return RQ_EINVAL;
+  for (int i = 0; i < n_loops; ++i) {
+    if (x[i] == nullptr || codes[i] == nullptr || scales[i] == nullptr) return RQ_EINVAL;
+  }
+  for (int i = 0; i < n_loops; ++i) {
+    if (bits[i] != 2 && bits[i] != 4) return RQ_EUNSUPPORTED;
+  }
+  if (!aligned16(ref)) return RQ_EALIGN;
+  for (int i = 0; i < n_loops; ++i) {
+    if (!aligned16(x[i]) || !aligned16(codes[i]) || !aligned16(scales[i])) return RQ_EALIGN;
+  }
+  EncodeArgs a{};
+  for (int i = 0; i < n_loops; ++i) {
+    a.x[i] = x[i];
+    a.codes[i] = codes[i];
+    a.scales[i] = scales[i];
+    a.bits[i] = bits[i];
+  }
+  a.ref = ref;
+  a.n_loops = n_loops;
+  a.n_vec = n_vectors(shape);
+  return hip_status(launch_encode(a, shape->head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int rq_reconstruct(const rq_shape* shape, int32_t bits, const uint16_t* ref, const uint32_t* codes,
+                   const uint16_t* scales, int32_t out_dtype, void* out, void* stream) {
+  int st = check_shape(shape);
+  if (st != RQ_OK) return st;
+  if (ref == nullptr || out == nullptr) return RQ_EINVAL;
+  if (bits != 0 && bits != 2 && bits != 4) return RQ_EUNSUPPORTED;
+  if (out_dtype != RQ_OUT_F32 && out_dtype != RQ_OUT_BF16) return RQ_EUNSUPPORTED;
+  if (bits != 0 && (codes == nullptr || scales == nullptr)) return RQ_EINVAL;
+  if (!aligned16(ref) || !aligned16(out)) return RQ_EALIGN;
+  if (bits != 0 && (!aligned16(codes) || !aligned16(scales))) return RQ_EALIGN;
+  ReconstructArgs a{};
+  a.ref = ref;
+  a.codes = codes;
+  a.scales = scales;
+  a.out = out;
+  a.n_vec = n_vectors(shape);
+  return hip_status(launch_reconstruct(a, shape->head_dim, bits, out_dtype == RQ_OUT_BF16,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int32_t rq_decode_attn_splits(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits) {
+  if (check_heads(shape, n_q_heads, n_loops) != RQ_OK || n_splits < 0) return 0;
+  return plan_splits(shape, n_splits).n_splits;
+}
+
+size_t rq_decode_attn_workspace(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits) {
+  if (check_heads(shape, n_q_heads, n_loops) != RQ_OK || n_splits < 0) return 0;
+  return workspace_bytes_for(shape, n_q_heads, n_loops, plan_splits(shape, n_splits).n_splits);
+}
+
+int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                   const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
+                   float softmax_scale, int32_t n_splits, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int st = check_heads(shape, n_q_heads, n_loops);
+  if (st != RQ_OK) return st;
+  if (q == nullptr || k_ref == nullptr || v_ref == nullptr || loops == nullptr || out == nullptr) return RQ_EINVAL;
+  if (n_splits < 0 || !isfinite(softmax_scale)) return RQ_EINVAL;
+  for (int i = 0; i < n_loops; ++i) {
+    const rq_loop_view& lv = loops[i];
+    if (lv.bits != 0 && lv.bits != 2 && lv.bits != 4) return RQ_EUNSUPPORTED;
+    if (lv.bits != 0 && (lv.k_codes == nullptr || lv.k_scales == nullptr || lv.v_codes == nullptr ||
+                         lv.v_scales == nullptr))
+      return RQ_EINVAL;
+  }
+  if (!aligned16(q) || !aligned16(k_ref) || !aligned16(v_ref) || !aligned16(out)) return RQ_EALIGN;
+  for (int i = 0; i < n_loops; ++i) {
+    const rq_loop_view& lv = loops[i];
+    if (lv.bits != 0 && (!aligned16(lv.k_codes) || !aligned16(lv.k_scales) || !aligned16(lv.v_codes) ||
+                         !aligned16(lv.v_scales)))
+      return RQ_EALIGN;
+  }
+  const SplitPlan plan = plan_splits(shape, n_splits);
+  if (workspace == nullptr || workspace_bytes < workspace_bytes_for(shape, n_q_heads, n_loops, plan.n_splits))
+    return RQ_EWORKSPACE;
+  if (!aligned16(workspace)) return RQ_EALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int G = n_q_heads / shape->n_kv_heads;
+  const int loops_per_launch = 32 / G < 1 ? 1 : 32 / G;
+  for (int base = 0; base < n_loops; base += loops_per_launch) {
+    const int nl = n_loops - base < loops_per_launch ? n_loops - base : loops_per_launch;
+    DecodeArgs a{};
+    fill_common(a, shape, n_q_heads, q, softmax_scale, plan, workspace);
+    a.k[0] = k_ref;
+    a.v[0] = v_ref;
+    a.loop_base = base;
+    a.n_loops_launch = nl;
+    a.n_rows = nl * G;
+    bool residual = false;
+    for (int li = 0; li < nl; ++li) {
+      const rq_loop_view& lv = loops[base + li];
+      a.bits[li] = lv.bits;
+      a.kc[li] = lv.k_codes;
+      a.ks[li] = lv.k_scales;
+      a.vc[li] = lv.v_codes;
+      a.vs[li] = lv.v_scales;
+      residual = residual || lv.bits != 0;
+    }
+    st = hip_status(launch_decode_partial(a, shape->head_dim, 1, residual, s));
+    if (st != RQ_OK) return st;
+  }
+  return run_combine(shape, n_q_heads, n_loops, plan.n_splits, static_cast<const float*>(workspace), out, s);
+}
+
+int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                        const uint16_t* const* k, const uint16_t* const* v, float softmax_scale,
+                        int32_t n_splits, float* out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  int st = check_heads(shape, n_q_heads, n_loops);
+  if (st != RQ_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return RQ_EINVAL;
+  if (n_splits < 0 || !isfinite(softmax_scale)) return RQ_EINVAL;
+  for (int i = 0; i < n_loops; ++i) {
+    if (k[i] == nullptr || v[i] == nullptr) return RQ_EINVAL;
+  }
+  if (!aligned16(q) || !aligned16(out)) return RQ_EALIGN;
+  for (int i = 0; i < n_loops; ++i) {
+    if (!aligned16(k[i]) || !aligned16(v[i])) return RQ_EALIGN;
+  }
+  const SplitPlan plan = plan_splits(shape, n_splits);
+  if (workspace == nullptr || workspace_bytes < workspace_bytes_for(shape, n_q_heads, n_loops, plan.n_splits))
+    return RQ_EWORKSPACE;
+  if (!aligned16(workspace)) return RQ_EALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int G = n_q_heads / shape->n_kv_heads;
+  DecodeArgs a{};
+  fill_common(a, shape, n_q_heads, q, softmax_scale, plan, workspace);
+  for (int i = 0; i < n_loops; ++i) {
+    a.k[i] = k[i];
+    a.v[i] = v[i];
+  }
+  a.loop_base = 0;
+  a.n_loops_launch = 1;
+  a.n_rows = G;
+  st = hip_status(launch_decode_partial(a, shape->head_dim, n_loops, false, s));
+  if (st != RQ_OK) return st;
+  return run_combine(shape, n_q_heads, n_loops, plan.n_splits, static_cast<const float*>(workspace), out, s);
+}
+
+const char* rq_status_str(int status) {
+  switch (status) {
+    case RQ_OK: return "ok";
+    case RQ_EINVAL: return "invalid argument";
+    case RQ_EUNSUPPORTED: return "unsupported head_dim, bit width, head grouping or output type";
+    case RQ_EALIGN: return "pointer not 16-byte aligned";
+    case RQ_EWORKSPACE: return "workspace missing or too small";
+    case RQ_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int32_t rq_format_version(void) { return RQ_FORMAT_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Internal declarations shared by the librq HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rq.h"
+
+namespace rq {
+
+constexpr int kMaxLoops = RQ_MAX_LOOPS;
+constexpr int kGroup = RQ_GROUP;
+
+// ---------------------------------------------------------------------------
+// launch parameters
+// ---------------------------------------------------------------------------
+
+struct EncodeArgs {
+  const uint16_t* x[kMaxLoops];
+  uint32_t* codes[kMaxLoops];
+  uint16_t* scales[kMaxLoops];
+  int32_t bits[kMaxLoops];
+  const uint16_t* ref;
+  int32_t n_loops;
+  int64_t n_vec;  // batch * n_kv_heads * seq_len
+};
+
+struct ReconstructArgs {
+  const uint16_t* ref;
+  const uint32_t* codes;
+  const uint16_t* scales;
+  void* out;
+  int64_t n_vec;
+};
+
+// One decode launch covers `n_rows` query rows per (batch, kv head): rows
+// r = li * G + j for li in [0, n_loops_launch) and j in [0, G). Row r reads
+// the query of loop loop_base + li, query head kvh * G + j. In the bf16
+// baseline each launch has n_loops_launch = 1 and blockIdx.z picks the loop.
+struct DecodeArgs {
+  const uint16_t* q;                    // [n_loops_total][B][Hq][D]
+  const uint16_t* k[kMaxLoops];         // per blockIdx.z: the K this block streams
+  const uint16_t* v[kMaxLoops];
+  int32_t bits[kMaxLoops];              // per li: 0 (reference only), 2 or 4
+  const uint32_t* kc[kMaxLoops];
+  const uint16_t* ks[kMaxLoops];
+  const uint32_t* vc[kMaxLoops];
+  const uint16_t* vs[kMaxLoops];
+  float* ws;                            // partials [n_loops_total][B][Hq][n_splits][D + 2]
+  int32_t loop_base;
+  int32_t n_loops_launch;               // loops whose rows this launch holds
+  int32_t n_rows;                       // n_loops_launch * G
+  int32_t group;                        // G = Hq / Hkv
+  int32_t n_q_heads, n_kv_heads, batch, seq_len;
+  int32_t n_splits, tokens_per_split;
+  float scale_log2;                     // softmax scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* ws;
+  float* out;
+  int64_t n_out;       // n_loops * B * Hq
+  int32_t n_splits;
+};
+
+// ---------------------------------------------------------------------------
+// launchers (defined in the .hip files); return hipGetLastError()
+// ---------------------------------------------------------------------------
+
+hipError_t launch_encode(const EncodeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_reconstruct(const ReconstructArgs& a, int head_dim, int bits, int out_bf16, hipStream_t stream);
+hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, int n_z, bool residual, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
+
+// tile of tokens one decode block iteration covers; split boundaries are multiples of it
+constexpr int kDecodeTile = 64;
+
+}  // namespace rq

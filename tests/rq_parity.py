@@ -1,0 +1,88 @@
+"""Helpers for comparing the GPU path with the CPU oracle.
+
+Tolerances:
+* packed codes are bit-exact, except for a coordinate whose rotated value y
+  (fp64, normalised transform) lies within 1e-5 of a decision threshold
+  k * s0. A group holding such a differing coordinate is also exempt from the
+  scale check;
+* fp16 scales agree within one fp16 ulp, because the GPU rounds fp32 -> fp16
+  and the oracle rounds fp64 -> fp16;
+* attention rows: max_i |o_gpu - o_ref| / max_i |o_ref| <= 2e-3 per
+  (loop, batch, query head);
+* reconstruction error e = |X_hat - X|_F / |X - X_ref|_F agrees within 1e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+BOUNDARY_EPS = 1e-5
+ATTN_TOL = 2e-3
+RECON_TOL = 1e-3
+
+
+def to_dev(bits_u16: np.ndarray, dtype=torch.bfloat16, device="cuda") -> torch.Tensor:
+    """uint16 bit patterns -> device tensor of a 16-bit dtype (bit copy)."""
+    return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).to(device).view(dtype)
+
+
+def words_to_dev(words: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(device)
+
+
+def to_host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_host_words(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint32)
+
+
+def exempt_mask(x_bits: np.ndarray, ref_bits: np.ndarray, bits: int) -> np.ndarray:
+    """Coordinates within BOUNDARY_EPS of a code decision threshold (fp64)."""
+    r = oracle.bf16_to_f64(x_bits) - oracle.bf16_to_f64(ref_bits)
+    y = oracle.rotate(r)
+    d = y.shape[-1]
+    yg = y.reshape(y.shape[:-1] + (d // 32, 32))
+    _, s0 = oracle.assign_codes(yg, bits)
+    ks = np.arange(-(2 ** (bits - 1) - 1), 2 ** (bits - 1))  # -1..1 (INT2), -7..7 (INT4)
+    dist = np.min(np.abs(yg[..., None] - s0[..., None, None] * ks), axis=-1)
+    return (dist <= BOUNDARY_EPS).reshape(y.shape)
+
+
+def compare_codes(gpu_words, gpu_scales, orc_words, orc_scales, x_bits, ref_bits, bits):
+    """Assert parity of one encoded tensor (any leading shape, [..., D] coords).
+    Returns the number of exempt coordinates that differed."""
+    d = x_bits.shape[-1]
+    cg = oracle.unpack_codes(gpu_words, bits)
+    co = oracle.unpack_codes(orc_words, bits)
+    diff = cg != co
+    n_diff = int(diff.sum())
+    bad_groups = np.zeros(gpu_scales.shape, dtype=bool)
+    if n_diff:
+        ex = exempt_mask(x_bits, ref_bits, bits)
+        unexplained = diff & ~ex
+        assert not unexplained.any(), f"{int(unexplained.sum())} code(s) differ away from a decision boundary"
+        bad_groups = diff.reshape(diff.shape[:-1] + (d // 32, 32)).any(axis=-1)
+    sg = gpu_scales.astype(np.int32)
+    so = orc_scales.astype(np.int32)
+    ulp = np.abs(sg - so)
+    ok = (ulp <= 1) | bad_groups
+    assert ok.all(), f"{int((~ok).sum())} scale(s) differ by more than one fp16 ulp (max {int(ulp.max())})"
+    return n_diff
+
+
+def row_rel_err(gpu: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row (last axis) max |gpu - ref| / max |ref|."""
+    num = np.max(np.abs(gpu - ref), axis=-1)
+    den = np.maximum(np.max(np.abs(ref), axis=-1), 1e-30)
+    return num / den
+
+
+def assert_attn_close(gpu: np.ndarray, ref: np.ndarray, tol: float = ATTN_TOL):
+    e = row_rel_err(np.asarray(gpu, dtype=np.float64), ref)
+    assert np.all(np.isfinite(gpu)), "non-finite attention output"
+    assert e.max() <= tol, f"attention row error {e.max():.3e} > {tol} at row {np.unravel_index(e.argmax(), e.shape)}"
+    return float(e.max())

@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI: the library loads and exports every entry
+point include/rq.h declares, size queries work, and every argument check
+fails before any HIP call (no GPU is touched: each call below is rejected by
+validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import looped_transformer_kv_rq_amd as rq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rq.library_path()), reason="librq.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(rq.library_path())
+    names = declared_functions()
+    assert {"rq_encode", "rq_reconstruct", "rq_decode_attn", "rq_decode_attn_bf16",
+            "rq_decode_attn_workspace", "rq_decode_attn_splits", "rq_status_str", "rq_format_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in rq.h but not exported"
+
+
+def test_status_strings_and_version():
+    lib = rq._load()
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.rq_status_str(st)
+    assert lib.rq_status_str(123) == b"unknown status"
+    assert rq.format_version() == 1
+
+
+def test_workspace_and_split_queries():
+    # 16 x 8 rows of 4096 tokens: enough splits for ~2048 blocks, each a multiple of 64 tokens
+    n = rq.decode_splits(16, 8, 4096, 128, 32, 4)
+    assert n == 16
+    assert rq.decode_workspace_bytes(16, 8, 4096, 128, 32, 4) == 4 * 16 * 32 * n * 130 * 4
+    assert rq.decode_splits(1, 1, 1, 64, 1, 1) == 1
+    assert rq.decode_splits(1, 1, 1000, 64, 1, 1, n_splits=3) == 3
+    assert rq.decode_splits(1, 1, 100, 64, 1, 1, n_splits=50) == 2  # never below one 64-token tile
+    assert rq.decode_workspace_bytes(1, 1, 1, 96, 1, 1) == 0       # unsupported head_dim
+    assert rq.decode_workspace_bytes(1, 2, 1, 64, 3, 1) == 0       # Hq % Hkv != 0
+    assert rq.decode_workspace_bytes(1, 1, 1, 64, 1, 9) == 0       # too many loops
+
+
+def _shape(b=1, h=1, s=4, d=64):
+    return rq._Shape(b, h, s, d)
+
+
+FAKE = 0x10000  # never dereferenced: each call fails validation first
+
+
+def _ptrs(*vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+def test_encode_argument_checks():
+    lib = rq._load()
+    bits = (ctypes.c_int32 * 1)(2)
+    x, c, s = _ptrs(FAKE), _ptrs(FAKE), _ptrs(FAKE)
+    ok = dict(x=x, bits=bits, ref=FAKE, codes=c, scales=s)
+
+    def call(shape=_shape(), n=1, **kw):
+        a = {**ok, **kw}
+        return lib.rq_encode(shape if shape is None else ctypes.byref(shape), n, a["x"], a["bits"], a["ref"],
+                             a["codes"], a["scales"], None)
+
+    assert call(shape=None) == rq.RQ_EINVAL
+    assert call(shape=_shape(s=0)) == rq.RQ_EINVAL
+    assert call(shape=_shape(d=96)) == rq.RQ_EUNSUPPORTED
+    assert call(n=0) == rq.RQ_EINVAL
+    assert call(n=9) == rq.RQ_EINVAL
+    assert call(ref=None) == rq.RQ_EINVAL
+    assert call(x=_ptrs(0)) == rq.RQ_EINVAL
+    assert call(bits=(ctypes.c_int32 * 1)(3)) == rq.RQ_EUNSUPPORTED
+    assert call(bits=(ctypes.c_int32 * 1)(0)) == rq.RQ_EUNSUPPORTED
+    assert call(ref=FAKE + 8) == rq.RQ_EALIGN
+    assert call(scales=_ptrs(FAKE + 2)) == rq.RQ_EALIGN
+
+
+def test_reconstruct_argument_checks():
+    lib = rq._load()
+    sh = ctypes.byref(_shape())
+    assert lib.rq_reconstruct(None, 2, FAKE, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EINVAL
+    assert lib.rq_reconstruct(sh, 3, FAKE, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EUNSUPPORTED
+    assert lib.rq_reconstruct(sh, 2, FAKE, FAKE, FAKE, 7, FAKE, None) == rq.RQ_EUNSUPPORTED
+    assert lib.rq_reconstruct(sh, 2, FAKE, None, FAKE, 0, FAKE, None) == rq.RQ_EINVAL
+    assert lib.rq_reconstruct(sh, 2, FAKE, FAKE, FAKE, 0, None, None) == rq.RQ_EINVAL
+    assert lib.rq_reconstruct(sh, 2, FAKE + 4, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EALIGN
+
+
+def test_decode_argument_checks():
+    lib = rq._load()
+    sh = _shape(b=1, h=2, s=64, d=64)
+    need = lib.rq_decode_attn_workspace(ctypes.byref(sh), 4, 2, 0)
+    assert need > 0
+    views = (rq._LoopView * 2)()
+    views[0].bits, views[0].k_codes, views[0].k_scales, views[0].v_codes, views[0].v_scales = 2, FAKE, FAKE, FAKE, FAKE
+    views[1].bits = 0
+
+    def call(hq=4, n=2, q=FAKE, v=views, scale=0.125, splits=0, out=FAKE, ws=FAKE, wsb=need):
+        return lib.rq_decode_attn(ctypes.byref(sh), hq, n, q, FAKE, FAKE, v, scale, splits, out, ws, wsb, None)
+
+    assert call(hq=3) == rq.RQ_EINVAL            # Hq % Hkv != 0
+    assert call(hq=2 * 33) == rq.RQ_EUNSUPPORTED  # more than 32 query heads per kv head
+    assert call(n=9) == rq.RQ_EINVAL
+    assert call(q=None) == rq.RQ_EINVAL
+    assert call(scale=float("nan")) == rq.RQ_EINVAL
+    assert call(splits=-1) == rq.RQ_EINVAL
+    assert call(ws=None) == rq.RQ_EWORKSPACE
+    assert call(wsb=need - 1) == rq.RQ_EWORKSPACE
+    assert call(out=FAKE + 4) == rq.RQ_EALIGN
+    bad = (rq._LoopView * 2)()
+    bad[0].bits = 3
+    assert call(v=bad) == rq.RQ_EUNSUPPORTED
+    bad[0].bits = 2  # residual loop without its code pointers
+    assert call(v=bad) == rq.RQ_EINVAL
+    bf = lib.rq_decode_attn_bf16
+    k = _ptrs(FAKE, FAKE)
+    assert bf(ctypes.byref(sh), 4, 2, FAKE, k, _ptrs(FAKE, 0), 0.125, 0, FAKE, FAKE, need, None) == rq.RQ_EINVAL
+    assert bf(ctypes.byref(sh), 4, 2, FAKE, k, k, 0.125, 0, FAKE, FAKE, 16, None) == rq.RQ_EWORKSPACE
+
+
+def test_python_side_rejects_cpu_tensors():
+    import torch
+    ref = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rq.encode([ref], ref, [2])
+    with pytest.raises(ValueError):
+        rq.encode([ref], ref, [3])
