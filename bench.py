@@ -1,0 +1,350 @@
+"""Benchmark of the ResidualQuant hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the hot path over one batch of synthetic input:
+rq_encode of K and of V (every non-final loop against the bf16 final-loop
+reference), then rq_decode_attn for every loop over the just-encoded cache.
+K steps are timed between two device synchronisations. `value` is KV tokens
+through the hot path per second: batch * seq_len * n_loops / step time.
+
+Timed in the same run, each alone and outside the timed steps, with the
+256 MB last-level cache flushed before every repetition:
+* rq_decode_attn alone: KV tokens/s, algorithmic GB/s and the fraction of the
+  8 TB/s HBM peak;
+* the bf16-KV baseline decode (rq_decode_attn_bf16) over the same loops;
+* one call per loop (per-loop mode);
+* rq_reconstruct of one loop.
+
+`roofline` covers the kernel that takes the largest share of the step (the
+encoder). Its achieved rate is algorithmic bytes per launch divided by the
+launch's average duration, timed with HIP events on the stream the kernel
+runs on. `traffic` comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+under profiles/, but only while the kernel source still matches the hash
+recorded there. Otherwise it is null.
+
+`cpu_baseline` is the fp64 NumPy oracle on the host cores, timed on a fixed
+sample of (batch, kv_head) rows of the same workload. It is a reported
+baseline, not a target.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import multiprocessing as mp
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode-attn KV tokens/s & achieved HBM GB/s (% of peak); encode GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+KERNEL_SOURCES = {
+    "encode": os.path.join(ROOT, "looped_transformer_kv_rq_amd", "csrc", "rq_codec.hip"),
+}
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes (what the method must move; nothing it avoids)
+# ---------------------------------------------------------------------------
+
+def encode_bytes(w, bits):
+    """One rq_encode launch (one tensor): ref once + per loop x_l, codes, scales."""
+    n = w.batch * w.n_kv_heads * w.seq_len * w.head_dim
+    return n * (2 + sum(2 + b / 8 + 2 / 32 for b in bits))
+
+
+def decode_bytes(w, bits_per_loop):
+    """One rq_decode_attn call over the given loops: bf16 K/V ref once, each
+    residual loop's K and V codes + scales, the queries and the outputs."""
+    th = w.batch * w.n_kv_heads * w.seq_len
+    d = w.head_dim
+    per = 4 * d + sum(2 * (d * b / 8 + d / 32 * 2) for b in bits_per_loop if b)
+    return th * per + len(bits_per_loop) * w.batch * w.n_q_heads * d * (2 + 4)
+
+
+def bf16_decode_bytes(w, n_loops):
+    th = w.batch * w.n_kv_heads * w.seq_len
+    return n_loops * th * 4 * w.head_dim + n_loops * w.batch * w.n_q_heads * w.head_dim * (2 + 4)
+
+
+def reconstruct_bytes(w, bits):
+    n = w.batch * w.n_kv_heads * w.seq_len * w.head_dim
+    return n * (2 + bits / 8 + 2 / 32 + 4)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on host cores (run before the GPU is touched)
+# ---------------------------------------------------------------------------
+
+def _oracle_row(args):
+    """Encode every non-final loop of K and V and decode all loops, for one
+    (batch, kv_head) row, with the fp64 oracle."""
+    name, b, h = args
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    w = workloads.WORKLOADS[name]
+    with threadpool_limits(1):
+        khat, vhat = [], []
+        for tensor, sink in ((workloads.TENSOR_K, khat), (workloads.TENSOR_V, vhat)):
+            xs = workloads.kv_rows_all_loops(w, b, h, tensor)
+            for l in range(w.n_loops):
+                if w.bits[l]:
+                    words, scales = oracle.encode(xs[l], xs[-1], w.bits[l])
+                    sink.append(oracle.reconstruct(xs[-1], words, scales, w.bits[l]))
+                else:
+                    sink.append(oracle.bf16_to_f64(xs[-1]))
+        g = w.group_size
+        scale = 1.0 / math.sqrt(w.head_dim)
+        for l in range(w.n_loops):
+            q = np.stack([oracle.bf16_to_f64(workloads.q_row(w, b, h * g + j, l)) for j in range(g)])
+            oracle.attention(q, khat[l], vhat[l], scale)
+    return 1
+
+
+def cpu_baseline(w, rows_per_worker=4):
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    workers = max(1, min(16, avail))
+    all_rows = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    n = min(len(all_rows), workers * rows_per_worker)
+    sample = [(w.name, b, h) for (b, h) in all_rows[:n]]
+    ctx = mp.get_context("fork")  # before any GPU use in this process
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_row, sample[:workers])  # warm the workers (imports)
+        t0 = time.perf_counter()
+        pool.map(_oracle_row, sample)
+        dt = time.perf_counter() - t0
+    kv_tokens = n * w.seq_len * w.n_loops / w.n_kv_heads  # same unit as `value`
+    return {
+        "value": kv_tokens / dt, "unit": "KV tokens/s", "cores": workers, "kind": "oracle",
+        "sample": f"{n} of {len(all_rows)} (batch, kv_head) rows of {w.name}: oracle encode of K and V "
+                  f"(all non-final loops) + decode of all {w.n_loops} loops, {dt:.1f} s wall on {workers} "
+                  f"processes x 1 BLAS thread",
+    }
+
+
+# ---------------------------------------------------------------------------
+# GPU measurement
+# ---------------------------------------------------------------------------
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel_key, workload_name):
+    """HBM bytes per launch from the committed PMC summary, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("workload") != workload_name or rec.get("source_sha") != _sha(KERNEL_SOURCES[kernel_key]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="l4_b16_s4k", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--reps", type=int, default=20, help="repetitions of each side measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-step", action="store_true", help="time the step only (for profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: the ResidualQuant hot path has no cross-GPU step; "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    w = workloads.WORKLOADS[args.workload]
+    if w.name == "peak_batch":
+        print("the peak-batch workload does not fit bf16 loop states for encode on one GPU; "
+              "it is covered by the parity tests", file=sys.stderr)
+        sys.exit(2)
+    cpu = None if (args.no_cpu_baseline or args.only_step) else cpu_baseline(w)
+
+    import torch
+
+    import looped_transformer_kv_rq_amd as rq
+
+    rq._load()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(bits_u16):
+        return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    res_loops = [l for l in range(w.n_loops) if w.bits[l]]
+    bits = [w.bits[l] for l in res_loops]
+    kx = [up(x) for x in workloads.kv_tensors(w, workloads.TENSOR_K)]
+    vx = [up(x) for x in workloads.kv_tensors(w, workloads.TENSOR_V)]
+    q = up(workloads.q_tensor(w))
+    shp = (w.batch, w.n_kv_heads, w.seq_len)
+    kc = [torch.empty(shp + (w.head_dim * b // 32,), dtype=torch.int32, device=dev) for b in bits]
+    vc = [torch.empty_like(t) for t in kc]
+    ks = [torch.empty(shp + (w.head_dim // 32,), dtype=torch.float16, device=dev) for _ in bits]
+    vs = [torch.empty_like(t) for t in ks]
+    views = []
+    for l in range(w.n_loops):
+        if w.bits[l]:
+            i = res_loops.index(l)
+            views.append(rq.LoopView(w.bits[l], kc[i], ks[i], vc[i], vs[i]))
+        else:
+            views.append(rq.LoopView(0))
+    out = torch.empty((w.n_loops, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(rq.decode_workspace_bytes(w.batch, w.n_kv_heads, w.seq_len, w.head_dim, w.n_q_heads,
+                                               w.n_loops), dtype=torch.uint8, device=dev)
+    kref, vref = kx[-1], vx[-1]
+    stream = torch.cuda.current_stream(dev)
+
+    def enc_k():
+        rq.encode_into([kx[l] for l in res_loops], kref, bits, kc, ks, stream=stream)
+
+    def enc_v():
+        rq.encode_into([vx[l] for l in res_loops], vref, bits, vc, vs, stream=stream)
+
+    def dec():
+        rq.decode_attn(q, kref, vref, views, out=out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        enc_k(); enc_v(); dec()
+    torch.cuda.synchronize()
+
+    Ev = torch.cuda.Event
+    marks = [[Ev(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = Ev(enable_timing=True), Ev(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for k in range(args.steps):
+        m = marks[k]
+        m[0].record(stream); enc_k()
+        m[1].record(stream); enc_v()
+        m[2].record(stream); dec()
+        m[3].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    step_ms = start.elapsed_time(stop) / args.steps
+    enc_ms = statistics.mean([m[0].elapsed_time(m[1]) for m in marks] + [m[1].elapsed_time(m[2]) for m in marks])
+    dec_in_step_ms = statistics.mean([m[2].elapsed_time(m[3]) for m in marks])
+
+    kv_tokens = w.batch * w.seq_len * w.n_loops
+    enc_b = encode_bytes(w, bits)
+    dec_b = decode_bytes(w, list(w.bits))
+    result = {
+        "metric": METRIC,
+        "value": kv_tokens / (step_ms * 1e-3),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "n_loops": w.n_loops, "batch": w.batch, "n_kv_heads": w.n_kv_heads,
+            "n_q_heads": w.n_q_heads, "head_dim": w.head_dim, "seq_len": w.seq_len, "bits": list(w.bits),
+            "step": "rq_encode(K) + rq_encode(V) + rq_decode_attn(all loops)",
+            "storage": "bf16 reference, int2/int4 residual codes, fp16 scales per 32",
+        },
+    }
+    enc_gbps = enc_b / (enc_ms * 1e-3) / 1e9
+    result["roofline"] = {
+        "kernel": f"rq_encode_kernel<{w.head_dim}> ({len(bits)} loops per launch)",
+        "bound": "hbm", "achieved": enc_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": enc_gbps / HBM_PEAK_GBPS, "traffic": _traffic("encode", w.name),
+        "algorithmic_bytes_per_launch": enc_b, "launch_ms": enc_ms,
+    }
+    result["wall_s_timed"] = wall_s
+
+    if not args.only_step:
+        flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+
+        def timed(fn, reps):
+            ts = []
+            for _ in range(reps):
+                flush.zero_()
+                a, b = Ev(enable_timing=True), Ev(enable_timing=True)
+                a.record(stream); fn(); b.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            return statistics.median(ts)
+
+        dec_ms = timed(dec, args.reps)
+        dec_gbps = dec_b / (dec_ms * 1e-3) / 1e9
+        result["roofline_decode"] = {
+            "kernel": "rq_decode_attn (split-S partial + combine), all loops, cache flushed",
+            "bound": "hbm", "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": None, "algorithmic_bytes_per_call": dec_b,
+        }
+        out_b = torch.empty_like(out)
+        ws_b = torch.empty_like(ws)
+
+        def dec_bf16():
+            rq.decode_attn_bf16(q, kx, vx, out=out_b, workspace=ws_b, stream=stream)
+
+        bf_ms = timed(dec_bf16, args.reps)
+        bf_b = bf16_decode_bytes(w, w.n_loops)
+        per_loop = []
+        for l in range(w.n_loops):
+            ql = q[l:l + 1].contiguous()
+            ol = torch.empty_like(out[:1])
+
+            def dec_one(ql=ql, ol=ol, l=l):
+                rq.decode_attn(ql, kref, vref, [views[l]], out=ol, stream=stream)
+
+            ms = timed(dec_one, max(5, args.reps // 2))
+            per_loop.append({"loop": l, "bits": w.bits[l], "ms": ms,
+                             "GBps": decode_bytes(w, [w.bits[l]]) / (ms * 1e-3) / 1e9})
+        rec = torch.empty(kref.shape, dtype=torch.float32, device=dev)
+
+        def recon():
+            rq.reconstruct(kref, kc[0], ks[0], bits[0], out=rec, stream=stream)
+
+        rc_ms = timed(recon, max(5, args.reps // 2))
+        per_loop_total = sum(p["ms"] for p in per_loop)
+        result["decode_attn"] = {
+            "kv_tokens_per_s": kv_tokens / (dec_ms * 1e-3), "ms": dec_ms, "GBps": dec_gbps,
+            "frac_peak": dec_gbps / HBM_PEAK_GBPS, "ms_in_step": dec_in_step_ms,
+        }
+        result["encode"] = {"GBps": enc_gbps, "ms_per_launch": enc_ms, "launches_per_step": 2}
+        result["bf16_baseline"] = {
+            "kv_tokens_per_s": kv_tokens / (bf_ms * 1e-3), "ms": bf_ms,
+            "GBps": bf_b / (bf_ms * 1e-3) / 1e9, "frac_peak": bf_b / (bf_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        }
+        result["rq_vs_bf16_decode_tokens_per_s"] = bf_ms / dec_ms
+        result["per_loop_mode"] = {"calls": per_loop, "total_ms": per_loop_total,
+                                   "vs_bf16_all_loop": bf_ms / per_loop_total}
+        result["reconstruct"] = {"loop": res_loops[0], "bits": bits[0], "ms": rc_ms,
+                                 "GBps": reconstruct_bytes(w, bits[0]) / (rc_ms * 1e-3) / 1e9}
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
