@@ -34,7 +34,7 @@ int check_heads(const rq_shape* s, int32_t n_q_heads, int32_t n_loops) {
 
 // Target number of partial blocks per launch; a split never holds fewer
 // tokens than one tile.
-constexpr int64_t kTargetBlocks = 2048;
+constexpr int64_t kTargetBlocks = 1024;
 
 struct SplitPlan {
   int32_t n_splits;

@@ -1,0 +1,49 @@
+// Log-sum-exp merge of the split-S decode partials.
+//
+// Each partial holds, for one query row and one token range, the running
+// maximum of the scores (log2 units), the sum of exp2(score - max) and the
+// unnormalised output. The merge rescales every split to the common maximum
+// and divides by the total weight, in a fixed split order, so the result does
+// not depend on scheduling.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "rq_internal.h"
+
+namespace rq {
+
+// One wave per output row: merge the splits by log-sum-exp and normalise.
+template <int D>
+__global__ __launch_bounds__(256) void rq_combine_kernel(CombineArgs a) {
+  constexpr int DJ = D / 64;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.n_out) return;
+  const float* src = a.ws + row * a.n_splits * (D + 2);
+  float mm = -INFINITY;
+  for (int s = 0; s < a.n_splits; ++s) mm = fmaxf(mm, src[s * (D + 2)]);
+  float lsum = 0.0f, o[DJ];
+#pragma unroll
+  for (int j = 0; j < DJ; ++j) o[j] = 0.0f;
+  for (int s = 0; s < a.n_splits; ++s) {
+    const float* p = src + s * (D + 2);
+    const float w = (p[0] == -INFINITY) ? 0.0f : exp2f(p[0] - mm);
+    lsum = fmaf(w, p[1], lsum);
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) o[j] = fmaf(w, p[2 + lane + 64 * j], o[j]);
+  }
+  const float inv = 1.0f / lsum;
+  float* dst = a.out + row * D;
+#pragma unroll
+  for (int j = 0; j < DJ; ++j) dst[lane + 64 * j] = o[j] * inv;
+}
+
+hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.n_out + 3) / 4));
+  if (head_dim == 128) hipLaunchKernelGGL(rq_combine_kernel<128>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(rq_combine_kernel<64>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace rq

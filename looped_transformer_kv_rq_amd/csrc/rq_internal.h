@@ -54,6 +54,7 @@ struct DecodeArgs {
   int32_t n_q_heads, n_kv_heads, batch, seq_len;
   int32_t n_splits, tokens_per_split;
   float scale_log2;                     // softmax scale * log2(e)
+  int32_t lds_wave_bytes;               // per-wave LDS stride (set by the launcher)
 };
 
 struct CombineArgs {

@@ -40,9 +40,9 @@ def test_status_strings_and_version():
 
 
 def test_workspace_and_split_queries():
-    # 16 x 8 rows of 4096 tokens: enough splits for ~2048 blocks, each a multiple of 64 tokens
+    # 16 x 8 rows of 4096 tokens: enough splits for ~1024 blocks, each a multiple of 64 tokens
     n = rq.decode_splits(16, 8, 4096, 128, 32, 4)
-    assert n == 16
+    assert n == 8
     assert rq.decode_workspace_bytes(16, 8, 4096, 128, 32, 4) == 4 * 16 * 32 * n * 130 * 4
     assert rq.decode_splits(1, 1, 1, 64, 1, 1) == 1
     assert rq.decode_splits(1, 1, 1000, 64, 1, 1, n_splits=3) == 3
