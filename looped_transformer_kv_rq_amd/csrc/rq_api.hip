@@ -53,19 +53,28 @@ SplitPlan plan_splits(const rq_shape* s, int32_t requested) {
   return {(int32_t)n, (int32_t)tps};
 }
 
+// Workspace: split partials [n_loops][B][Hq][n_splits][2D + 2] floats, padded
+// to 256 bytes, then one rotated-query record per query row.
+size_t partial_bytes(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int32_t n_splits) {
+  const size_t b = (size_t)n_loops * s->batch * n_q_heads * n_splits * (2 * s->head_dim + 2) * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
 size_t workspace_bytes_for(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int32_t n_splits) {
-  return (size_t)n_loops * s->batch * n_q_heads * n_splits * (s->head_dim + 2) * sizeof(float);
+  return partial_bytes(s, n_q_heads, n_loops, n_splits) +
+         (size_t)n_loops * s->batch * n_q_heads * query_prep_bytes(s->head_dim);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RQ_OK : RQ_EHIP; }
 
 int run_combine(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int32_t n_splits, const float* ws,
-                float* out, hipStream_t stream) {
+                float* out, bool residual, hipStream_t stream) {
   CombineArgs c{};
   c.ws = ws;
   c.out = out;
   c.n_out = (int64_t)n_loops * s->batch * n_q_heads;
   c.n_splits = n_splits;
+  c.residual = residual ? 1 : 0;
   return hip_status(launch_combine(c, s->head_dim, stream));
 }
 
@@ -175,11 +184,36 @@ int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, co
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int G = n_q_heads / shape->n_kv_heads;
-  const int loops_per_launch = 32 / G < 1 ? 1 : 32 / G;
-  for (int base = 0; base < n_loops; base += loops_per_launch) {
-    const int nl = n_loops - base < loops_per_launch ? n_loops - base : loops_per_launch;
+  unsigned char* prep = static_cast<unsigned char*>(workspace) + partial_bytes(shape, n_q_heads, n_loops, plan.n_splits);
+  bool any_residual = false;
+  for (int i = 0; i < n_loops; ++i) any_residual = any_residual || loops[i].bits != 0;
+  if (any_residual) {
+    QueryPrepArgs qa{};
+    qa.q = q;
+    qa.out = prep;
+    for (int i = 0; i < n_loops; ++i) qa.bits[i] = loops[i].bits;
+    qa.n_rows = (int64_t)n_loops * shape->batch * n_q_heads;
+    qa.batch = shape->batch;
+    qa.n_q_heads = n_q_heads;
+    st = hip_status(launch_query_prep(qa, shape->head_dim, s));
+    if (st != RQ_OK) return st;
+  }
+  // A launch holds at most 32 query rows per kv head and what its waves stage
+  // per tile must fit the block's LDS; further loops go to further launches
+  // (each streams the reference again).
+  int base = 0;
+  while (base < n_loops) {
+    int nl = 0;
+    int32_t bits[kMaxLoops];
+    while (base + nl < n_loops && (nl + 1) * G <= 32) {
+      bits[nl] = loops[base + nl].bits;
+      if (nl > 0 && 4 * decode_wave_lds_bytes(shape->head_dim, bits, nl + 1) > kMaxBlockLds) break;
+      ++nl;
+    }
+    if (nl == 0) nl = 1;  // G == 32: one loop per launch
     DecodeArgs a{};
     fill_common(a, shape, n_q_heads, q, softmax_scale, plan, workspace);
+    a.qprep = prep;
     a.k[0] = k_ref;
     a.v[0] = v_ref;
     a.loop_base = base;
@@ -195,10 +229,13 @@ int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, co
       a.vs[li] = lv.v_scales;
       residual = residual || lv.bits != 0;
     }
+    a.zero_residual = any_residual && !residual;
     st = hip_status(launch_decode_partial(a, shape->head_dim, 1, residual, s));
     if (st != RQ_OK) return st;
+    base += nl;
   }
-  return run_combine(shape, n_q_heads, n_loops, plan.n_splits, static_cast<const float*>(workspace), out, s);
+  return run_combine(shape, n_q_heads, n_loops, plan.n_splits, static_cast<const float*>(workspace), out,
+                     any_residual, s);
 }
 
 int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
@@ -234,7 +271,7 @@ int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loop
   a.n_rows = G;
   st = hip_status(launch_decode_partial(a, shape->head_dim, n_loops, false, s));
   if (st != RQ_OK) return st;
-  return run_combine(shape, n_q_heads, n_loops, plan.n_splits, static_cast<const float*>(workspace), out, s);
+  return run_combine(shape, n_q_heads, n_loops, plan.n_splits, static_cast<const float*>(workspace), out, false, s);
 }
 
 const char* rq_status_str(int status) {

@@ -1,37 +1,64 @@
 // Log-sum-exp merge of the split-S decode partials.
 //
-// Each partial holds, for one query row and one token range, the running
-// maximum of the scores (log2 units), the sum of exp2(score - max) and the
-// unnormalised output. The merge rescales every split to the common maximum
-// and divides by the total weight, in a fixed split order, so the result does
-// not depend on scheduling.
+// A partial holds, for one query row and one token range, the running maximum
+// of the scores (log2 units), the sum of exp2(score - max), the unnormalised
+// reference output and, for residual loops, the unnormalised residual output
+// in the rotated domain. The merge rescales every split to the common maximum
+// in a fixed split order, so the result does not depend on scheduling. It
+// then applies the normalised Walsh-Hadamard rotation to the merged residual
+// accumulator once, because H sum(p (s*lev)) = sum(p H (s*lev)), and divides
+// by the total weight.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
+#include "rq_device.h"
 #include "rq_internal.h"
 
 namespace rq {
 
-// One wave per output row: merge the splits by log-sum-exp and normalise.
+// One wave per output row; lane owns coordinates lane + 64 j.
 template <int D>
 __global__ __launch_bounds__(256) void rq_combine_kernel(CombineArgs a) {
   constexpr int DJ = D / 64;
+  constexpr int REC = 2 * D + 2;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= a.n_out) return;
-  const float* src = a.ws + row * a.n_splits * (D + 2);
+  const float* src = a.ws + row * a.n_splits * REC;
   float mm = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) mm = fmaxf(mm, src[s * (D + 2)]);
-  float lsum = 0.0f, o[DJ];
+  for (int s = 0; s < a.n_splits; ++s) mm = fmaxf(mm, src[s * REC]);
+  float lsum = 0.0f, o[DJ], r[DJ];
 #pragma unroll
-  for (int j = 0; j < DJ; ++j) o[j] = 0.0f;
+  for (int j = 0; j < DJ; ++j) o[j] = r[j] = 0.0f;
   for (int s = 0; s < a.n_splits; ++s) {
-    const float* p = src + s * (D + 2);
+    const float* p = src + s * REC;
     const float w = (p[0] == -INFINITY) ? 0.0f : exp2f(p[0] - mm);
     lsum = fmaf(w, p[1], lsum);
 #pragma unroll
-    for (int j = 0; j < DJ; ++j) o[j] = fmaf(w, p[2 + lane + 64 * j], o[j]);
+    for (int j = 0; j < DJ; ++j) {
+      o[j] = fmaf(w, p[2 + lane + 64 * j], o[j]);
+      if (a.residual) r[j] = fmaf(w, p[2 + D + lane + 64 * j], r[j]);
+    }
+  }
+  if (a.residual) {
+    // unnormalised transform: index bit 6 in the lane, bits 0..5 across lanes
+    if constexpr (DJ == 2) {
+      const float x = r[0], y = r[1];
+      r[0] = x + y;
+      r[1] = x - y;
+    }
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const bool upper = (lane & s) != 0;
+#pragma unroll
+      for (int j = 0; j < DJ; ++j) {
+        const float p = __shfl_xor(r[j], s);
+        r[j] = upper ? p - r[j] : r[j] + p;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < DJ; ++j) o[j] = fmaf(r[j], RsqrtD<D>::v, o[j]);
   }
   const float inv = 1.0f / lsum;
   float* dst = a.out + row * D;

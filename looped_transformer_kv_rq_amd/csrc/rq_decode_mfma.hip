@@ -7,29 +7,35 @@
 // (normalised Walsh-Hadamard) is symmetric, so
 //   score  = q . k_ref + (H q) . (s * lev)
 //   output = sum_t p_t v_ref,t + H sum_t p_t (s * lev)_t.
-// Each query is rotated once. The residual terms stay in the rotated domain,
-// and a split applies H to its residual accumulator a single time.
+// rq_query_prep rotates each query once. The partial kernel keeps the residual
+// terms in the rotated domain, and the combine kernel applies H to the merged
+// residual accumulator of each query row once.
 //
-// One block is four independent waves over one split of one (batch, kv head)
-// row. A wave takes 32-token tiles (tiles w, w+4, ...). Every query row of the
-// kv head (all loops x the G query heads, at most 32 = two 16-row blocks) is
-// one MFMA column. All products run on v_mfma_f32_16x16x32:
+// Partial kernel: one block is four independent waves over one split of one
+// (batch, kv head) row. A wave takes 32-token tiles (tiles w, w+4, ...). Every
+// query row of the kv head (loops x G query heads, at most 32 = two 16-row
+// blocks) is one MFMA column. All products run on v_mfma_f32_16x16x32:
 //  * reference scores S^T = K_ref Q^T (bf16; exact products, fp32 sums). The
-//    K tile is loaded straight into the A operand with 16-byte loads;
-//  * residual scores per loop and scale group (fp16). Codes become the fp16
-//    value 1 + c / 2^b by masking them into the mantissa of 1.0 (one shift
-//    and one and-or per two codes). The per-row constant of that offset is
-//    taken out exactly afterwards: q.(c - o) = 2^b (q.val) - (2^b + o) sum(q);
+//    K tile is loaded straight into the A operand;
+//  * residual scores per loop and scale group (fp16). A code becomes the fp16
+//    value 1 + c / 2^b when it is masked into the mantissa of 1.0. The per-row
+//    constant of that offset is taken out afterwards:
+//    q . (c - o) = 2^b (q . val) - (2^b + o) sum(q);
 //  * reference PV, O_ref^T += V^T P^T (bf16). P is split into bf16 hi + lo
-//    halves (error ~2^-16), and V^T is read from a per-wave LDS tile;
+//    halves (error ~2^-16), and V^T is read from the LDS tile;
 //  * residual PV, O_res^T += lev^T (P s)^T (fp16). Levels decode exactly
-//    through a v_perm byte lookup table (INT2: {-1.5,-0.5,0.5,1.5}; INT4 as
-//    4 lev_hi + lev_lo, two table lookups). The rows of other loops carry
-//    P s = 0, so every loop shares one accumulator.
+//    through a v_perm byte table (INT2: {-1.5,-0.5,0.5,1.5}; INT4 as
+//    4 lev_hi + lev_lo). Rows of other loops carry P s = 0, so every loop
+//    shares one accumulator.
 // The MFMA output layout (lane l holds rows 4 (l / 16) + i of column l % 16)
 // gives each lane one query row and four tokens per 16-token block. The
-// online-softmax statistics of a row therefore stay within the row's four
-// lanes, and the P fragment is already the B operand of the PV products.
+// softmax statistics of a row therefore stay within the row's four lanes,
+// and the P fragment is already the B operand of the PV products.
+//
+// Each tile's loads go out together at its start. The K reference goes to
+// registers. The V tile and every residual loop's codes and scales go to LDS
+// by DMA (global_load_lds). A tile therefore costs one memory round trip
+// however many loops it carries.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -43,6 +49,8 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
 __device__ __forceinline__ f32x4_t mma_bf16(uint4 a, uint4 b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
@@ -58,9 +66,23 @@ __device__ __forceinline__ uint32_t vperm(uint32_t s0, uint32_t s1, uint32_t sel
 __device__ __forceinline__ uint32_t pack_rtz(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) * __builtin_bit_cast(f16x2_t, b));
+}
 __device__ __forceinline__ float half_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
 __device__ __forceinline__ float half_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
 
+// LDS DMA (gfx950 global_load_lds): every active lane fetches `bytes` from its
+// own global address; lane l's data lands at dst + l * bytes (dst uniform).
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 4, 0, 0);
+}
+// s_waitcnt vmcnt(0) / lgkmcnt(0) (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8])
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -70,26 +92,311 @@ __device__ __forceinline__ void wave_sync_lds() {
 constexpr uint32_t kLutInt2 = 0x3E38B8BEu;    // fp16 high bytes of -1.5, -0.5, 0.5, 1.5
 constexpr uint32_t kLutInt4Hi = 0x4640C0C6u;  // fp16 high bytes of -6, -2, 2, 6 (4 * INT2 level)
 constexpr int kTile = 32;
-constexpr int kCodeStride = 36;  // dwords per code-word row (32 tokens + pad) in LDS
 
 template <int D>
 struct MfmaGeom {
   static constexpr int NG = D / 32;    // scale groups = k-steps of the score products
   static constexpr int NH = D / 64;    // 64-coordinate halves of the reference PV
-  static constexpr int VTS = D + 8;    // bf16 elements per V tile row in LDS
-  static constexpr int VTILE_BYTES = kTile * VTS * 2;
+  // V tile: one DMA instruction writes 1 KB (VT_TOK tokens); a 128-byte pad
+  // after each keeps the transposed reads of neighbouring lane groups apart.
+  static constexpr int VT_TOK = 1024 / (2 * D);
+  static constexpr int VT_INSTR = kTile / VT_TOK;
+  static constexpr int VT_STRIDE = 1024 + 128;
+  static constexpr int VT_BYTES = VT_INSTR * VT_STRIDE;
+  static __device__ __forceinline__ int vt_offset(int tok) {
+    return (tok / VT_TOK) * VT_STRIDE + (tok % VT_TOK) * 2 * D;
+  }
+  static constexpr int PREP_BYTES = (2 * D + 4 * NG + 15) / 16 * 16;  // rotated query record
 };
 
-// LDS bytes one wave needs during the token loop (V tile + one loop's code words)
-__host__ __device__ constexpr int mfma_wave_lds_bytes(int d, int max_bits) {
-  return kTile * (d + 8) * 2 + (d * max_bits / 32) * kCodeStride * 4;
+// LDS bytes of one residual loop's tile data: K code words [token][W],
+// K scales [token][NG], V code words transposed [word][token], V scales
+__host__ __device__ constexpr int loop_lds_bytes(int d, int bits) {
+  return bits == 0 ? 0 : 256 * (d * bits / 32) + 128 * (d / 32);
+}
+
+// ---------------------------------------------------------------------------
+// query prep: rotated query in residual-score B-operand order + offsets
+// ---------------------------------------------------------------------------
+
+// Coordinate that lane group g, k-step ks, element e (0..7) of the residual
+// score products stands for. Code words are unpacked to match it: element 2i
+// comes from field 4(g&1) + i of word 2ks + (g>>1) (INT2) and element 2i+1
+// from the field 8 positions later.
+__host__ __device__ constexpr int rs_coord(int ks, int g, int e) {
+  return 32 * ks + 16 * (g >> 1) + 4 * (g & 1) + (e >> 1) + 8 * (e & 1);
+}
+
+// One wave per query row (loop, b, hq): writes the fp16 normalised rotation
+// H q in operand order (16 bytes per (ks, g)) and
+// qoff[ks] = -(2^b + 2^(b-1) - 1/2) * (sum of the group's fp16 values).
+template <int D>
+__global__ __launch_bounds__(256) void rq_query_prep(QueryPrepArgs a) {
+  constexpr int NG = D / 32;
+  constexpr int PER = D / 64;  // coordinates per lane: lane + 64 j
+  __shared__ float buf[4][D];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const bool active = row < a.n_rows;
+  const int64_t rr = active ? row : 0;
+  const int loop = (int)(rr / ((int64_t)a.batch * a.n_q_heads));
+  const int bits = a.bits[loop];
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) v[j] = __uint_as_float((uint32_t)a.q[rr * D + lane + 64 * j] << 16);
+  // butterflies on bit 6 (in lane) and bits 0..5 (across lanes)
+  if constexpr (PER == 2) {
+    const float x = v[0], y = v[1];
+    v[0] = x + y;
+    v[1] = x - y;
+  }
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const bool upper = (lane & s) != 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const float p = __shfl_xor(v[j], s);
+      v[j] = upper ? p - v[j] : v[j] + p;
+    }
+  }
+  // fp16 of the normalised value; the offsets sum exactly these values
+#pragma unroll
+  for (int j = 0; j < PER; ++j) buf[wave][lane + 64 * j] = (float)(_Float16)(v[j] * RsqrtD<D>::v);
+  __syncthreads();
+  if (!active) return;
+  unsigned char* rec = a.out + row * MfmaGeom<D>::PREP_BYTES;
+  // operand-ordered fp16 values: lane -> (ks, g) = (lane / 4, lane % 4) for lane < 4 NG
+  if (lane < 4 * NG) {
+    const int ks = lane >> 2, g = lane & 3;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2_t h = {(_Float16)buf[wave][rs_coord(ks, g, 2 * i)], (_Float16)buf[wave][rs_coord(ks, g, 2 * i + 1)]};
+      w[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    *reinterpret_cast<uint4*>(rec + 16 * (4 * ks + g)) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (lane < NG) {
+    float s = 0.0f;
+    for (int d = 0; d < 32; ++d) s += buf[wave][32 * lane + d];
+    const float off = bits == 4 ? 23.5f : 5.5f;
+    reinterpret_cast<float*>(rec + 2 * D)[lane] = -off * s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// partial kernel
+// ---------------------------------------------------------------------------
+
+// Issue the DMA of one residual loop's tile data (codes and scales of K and V).
+template <int D, int BITS>
+__device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned char* base, int64_t row_base,
+                                           int t0, int tlast, int lane) {
+  constexpr int NG = D / 32;
+  constexpr int W = D * BITS / 32;  // code words per vector
+  unsigned char* kc_l = base;
+  unsigned char* ks_l = kc_l + 128 * W;
+  unsigned char* vc_l = ks_l + 64 * NG;
+  unsigned char* vs_l = vc_l + 128 * W;
+  // K code words in 16-byte chunks: chunk c -> token c / (W/4), words 4 (c % (W/4))
+#pragma unroll
+  for (int i = 0; i * 64 < 8 * W; ++i) {
+    const int c = 64 * i + lane;
+    if (8 * W >= 64 * (i + 1) || c < 8 * W) {
+      const int tok = c / (W / 4), q4 = c % (W / 4);
+      dma16(a.kc[li] + (row_base + min(t0 + tok, tlast)) * W + 4 * q4, kc_l + 1024 * i);
+    }
+  }
+  // scales, 4 bytes per lane: lane -> token lane / (NG/2), pair lane % (NG/2)
+  if (16 * NG >= 64 || lane < 16 * NG) {
+    const int tok = lane / (NG / 2), pr = lane % (NG / 2);
+    const int64_t vec = row_base + min(t0 + tok, tlast);
+    dma4(a.ks[li] + vec * NG + 2 * pr, ks_l);
+    dma4(a.vs[li] + vec * NG + 2 * pr, vs_l);
+  }
+  // V code words transposed: slot idx -> word idx / 32 of token idx % 32
+#pragma unroll
+  for (int i = 0; i < W / 2; ++i) {
+    const int idx = 64 * i + lane;
+    dma4(a.vc[li] + (row_base + min(t0 + (idx & 31), tlast)) * W + (idx >> 5), vc_l + 256 * i);
+  }
+}
+
+// Residual scores of loop li added to this lane's score fragment.
+template <int D, int NB, int BITS>
+__device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, const unsigned char* base,
+                                                const uint4 (&qtB)[NB][D / 32], const float (&qoff)[NB][D / 32],
+                                                const float (&qmul)[NB], const int (&my_loop)[NB],
+                                                f32x4_t (&sc)[2][NB], int m, int g) {
+  constexpr int NG = D / 32;
+  constexpr int W = D * BITS / 32;
+  const unsigned char* kc_l = base;
+  const unsigned char* ks_l = kc_l + 128 * W;
+  const int G = a.group;
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+    // code words of token 16bk + m (this lane's A-operand row)
+    const unsigned char* cw = kc_l + (16 * bk + m) * W * 4;
+    uint4 kx[NG];
+    if constexpr (BITS == 2) {
+      uint32_t wsel[NG];
+      const bool hi = (g >> 1) != 0;
+      const uint4 w0 = *reinterpret_cast<const uint4*>(cw);
+      wsel[0] = hi ? w0.y : w0.x;
+      wsel[1] = hi ? w0.w : w0.z;
+      if constexpr (NG == 4) {
+        const uint4 w1 = *reinterpret_cast<const uint4*>(cw + 16);
+        wsel[2] = hi ? w1.y : w1.x;
+        wsel[3] = hi ? w1.w : w1.z;
+      }
+      const uint32_t pre = (g & 1) ? 0u : 8u;
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) {
+        const uint32_t w = wsel[ks] << pre;
+        kx[ks].x = (w & 0x03000300u) | 0x3C003C00u;
+        kx[ks].y = ((w >> 2) & 0x03000300u) | 0x3C003C00u;
+        kx[ks].z = ((w >> 4) & 0x03000300u) | 0x3C003C00u;
+        kx[ks].w = ((w >> 6) & 0x03000300u) | 0x3C003C00u;
+      }
+    } else {
+      const uint32_t f4 = 16u * (uint32_t)(g & 1);
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) {
+        const uint2 w = *reinterpret_cast<const uint2*>(cw + (4 * ks + 2 * (g >> 1)) * 4);
+        uint32_t e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t c0 = __builtin_amdgcn_ubfe(w.x, f4 + 4 * i, 4);
+          const uint32_t c1 = __builtin_amdgcn_ubfe(w.y, f4 + 4 * i, 4);
+          e[i] = (c1 << 22) | (c0 << 6) | 0x3C003C00u;
+        }
+        kx[ks] = make_uint4(e[0], e[1], e[2], e[3]);
+      }
+    }
+    // k scales of this lane's four C-layout tokens 16bk + 4g + i
+    uint32_t sw[4][(NG + 1) / 2];
+    const unsigned char* sp = ks_l + (16 * bk + 4 * g) * NG * 2;
+    if constexpr (NG == 4) {
+      const uint4 u0 = *reinterpret_cast<const uint4*>(sp);
+      const uint4 u1 = *reinterpret_cast<const uint4*>(sp + 16);
+      sw[0][0] = u0.x; sw[0][1] = u0.y; sw[1][0] = u0.z; sw[1][1] = u0.w;
+      sw[2][0] = u1.x; sw[2][1] = u1.y; sw[3][0] = u1.z; sw[3][1] = u1.w;
+    } else {
+      const uint4 u0 = *reinterpret_cast<const uint4*>(sp);
+      sw[0][0] = u0.x; sw[1][0] = u0.y; sw[2][0] = u0.z; sw[3][0] = u0.w;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if (li * G >= 16 * nb + 16 || li * G + G <= 16 * nb) continue;  // no row of loop li here
+      f32x4_t r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) {
+        const f32x4_t c = mma_f16(kx[ks], qtB[nb][ks], f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float s = (ks & 1) ? half_hi(sw[i][ks >> 1]) : half_lo(sw[i][ks >> 1]);
+          r[i] = fmaf(s, fmaf(c[i], qmul[nb], qoff[nb][ks]), r[i]);
+        }
+      }
+      if (my_loop[nb] == li) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[bk][nb][i] += r[i];
+      }
+    }
+  }
+}
+
+// Residual PV of loop li into the shared residual accumulator.
+template <int D, int NB, int BITS>
+__device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const unsigned char* base,
+                                            const float (&p)[NB][8], const int (&my_loop)[NB],
+                                            f32x4_t (&o_res)[NB][2 * (D / 32)], int m, int g) {
+  constexpr int NG = D / 32;
+  constexpr int W = D * BITS / 32;
+  const unsigned char* vc_l = base + 128 * W + 64 * NG;
+  const unsigned char* vs_l = vc_l + 128 * W;
+  const int G = a.group;
+  // v scales of this lane's eight B-operand tokens (two runs of four)
+  uint32_t vsw[8][(NG + 1) / 2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const unsigned char* sp = vs_l + (16 * h2 + 4 * g) * NG * 2;
+    if constexpr (NG == 4) {
+      const uint4 u0 = *reinterpret_cast<const uint4*>(sp);
+      const uint4 u1 = *reinterpret_cast<const uint4*>(sp + 16);
+      vsw[4 * h2 + 0][0] = u0.x; vsw[4 * h2 + 0][1] = u0.y;
+      vsw[4 * h2 + 1][0] = u0.z; vsw[4 * h2 + 1][1] = u0.w;
+      vsw[4 * h2 + 2][0] = u1.x; vsw[4 * h2 + 2][1] = u1.y;
+      vsw[4 * h2 + 3][0] = u1.z; vsw[4 * h2 + 3][1] = u1.w;
+    } else {
+      const uint4 u0 = *reinterpret_cast<const uint4*>(sp);
+      vsw[4 * h2 + 0][0] = u0.x; vsw[4 * h2 + 1][0] = u0.y;
+      vsw[4 * h2 + 2][0] = u0.z; vsw[4 * h2 + 3][0] = u0.w;
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if (li * G >= 16 * nb + 16 || li * G + G <= 16 * nb) continue;
+    const float mem = my_loop[nb] == li ? 1.0f : 0.0f;
+    uint32_t p16[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p16[i] = pack_rtz(p[nb][2 * i] * mem, p[nb][2 * i + 1] * mem);
+#pragma unroll
+    for (int grp = 0; grp < NG; ++grp) {
+      const uint32_t hsel = (grp & 1) ? 0x07060302u : 0x05040100u;
+      uint4 bop;
+      bop.x = mul_f16x2(p16[0], vperm(vsw[1][grp >> 1], vsw[0][grp >> 1], hsel));
+      bop.y = mul_f16x2(p16[1], vperm(vsw[3][grp >> 1], vsw[2][grp >> 1], hsel));
+      bop.z = mul_f16x2(p16[2], vperm(vsw[5][grp >> 1], vsw[4][grp >> 1], hsel));
+      bop.w = mul_f16x2(p16[3], vperm(vsw[7][grp >> 1], vsw[6][grp >> 1], hsel));
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        // A rows: coordinate 32grp + 16hf + m; its code sits in word wv, field f
+        int wv, sh;
+        uint32_t selx;
+        if constexpr (BITS == 2) {
+          wv = 2 * grp + hf;
+          selx = ((uint32_t)(m >> 2) << 8) | ((uint32_t)(4 + (m >> 2)) << 24);
+          sh = 2 * (m & 3);
+        } else {
+          wv = 4 * grp + 2 * hf + (m >> 3);
+          const int f = m & 7;
+          selx = ((uint32_t)(f >> 1) << 8) | ((uint32_t)(4 + (f >> 1)) << 24);
+          sh = 4 * (f & 1);
+        }
+        const uint4 wa = *reinterpret_cast<const uint4*>(vc_l + (wv * 32 + 4 * g) * 4);
+        const uint4 wb = *reinterpret_cast<const uint4*>(vc_l + (wv * 32 + 16 + 4 * g) * 4);
+        const uint32_t y0 = vperm(wa.y, wa.x, selx) >> sh;
+        const uint32_t y1 = vperm(wa.w, wa.z, selx) >> sh;
+        const uint32_t y2 = vperm(wb.y, wb.x, selx) >> sh;
+        const uint32_t y3 = vperm(wb.w, wb.z, selx) >> sh;
+        uint4 alo;
+        alo.x = vperm(0u, kLutInt2, (y0 & 0x03000300u) | 0x000C000Cu);
+        alo.y = vperm(0u, kLutInt2, (y1 & 0x03000300u) | 0x000C000Cu);
+        alo.z = vperm(0u, kLutInt2, (y2 & 0x03000300u) | 0x000C000Cu);
+        alo.w = vperm(0u, kLutInt2, (y3 & 0x03000300u) | 0x000C000Cu);
+        o_res[nb][2 * grp + hf] = mma_f16(alo, bop, o_res[nb][2 * grp + hf]);
+        if constexpr (BITS == 4) {
+          uint4 ahi;
+          ahi.x = vperm(0u, kLutInt4Hi, ((y0 >> 2) & 0x03000300u) | 0x000C000Cu);
+          ahi.y = vperm(0u, kLutInt4Hi, ((y1 >> 2) & 0x03000300u) | 0x000C000Cu);
+          ahi.z = vperm(0u, kLutInt4Hi, ((y2 >> 2) & 0x03000300u) | 0x000C000Cu);
+          ahi.w = vperm(0u, kLutInt4Hi, ((y3 >> 2) & 0x03000300u) | 0x000C000Cu);
+          o_res[nb][2 * grp + hf] = mma_f16(ahi, bop, o_res[nb][2 * grp + hf]);
+        }
+      }
+    }
+  }
 }
 
 template <int D, int NB, bool RESID>
-__global__ __launch_bounds__(256) void rq_decode_partial_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RESID && NB == 2 ? 1 : 2,
+                                                                     RESID && NB == 1 ? 2 : 4)))
+void rq_decode_partial_mfma(DecodeArgs a) {
   using Gm = MfmaGeom<D>;
-  constexpr int NG = Gm::NG, NH = Gm::NH, VTS = Gm::VTS;
+  constexpr int NG = Gm::NG, NH = Gm::NH;
   constexpr int NR = 16 * NB;
+  constexpr int REC = 2 * D + 2;  // partial record: m, l, o_ref[D], o_res[D]
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -102,84 +409,41 @@ __global__ __launch_bounds__(256) void rq_decode_partial_mfma(DecodeArgs a) {
   const int64_t row_base = (int64_t)bh * S;  // first cached vector of this (b, kv head)
 
   // ------------------------------------------------------------------ setup
-  // Reference-score B operand (bf16 Q^T): lane (m, g) holds q[row 16nb+m][32ks + 8g .. +8].
+  // B operands: bf16 Q^T for the reference scores (lane (m, g) holds
+  // q[row 16nb+m][32ks + 8g .. +8]); fp16 rotated query + offsets (prepared).
   uint4 qB[NB][NG];
+  uint4 qtB[NB][NG];
+  float qoff[NB][NG];
+  float qmul[NB];
   int my_loop[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int row = 16 * nb + m;
     my_loop[nb] = row < R ? row / G : -1;
-    const uint16_t* qp = nullptr;
-    if (row < R) {
-      const int loop = a.loop_base + row / G + z;
-      qp = a.q + (((int64_t)loop * a.batch + b) * a.n_q_heads + kvh * G + row % G) * D;
+    const int lb = my_loop[nb] >= 0 ? a.bits[my_loop[nb]] : 0;
+    qmul[nb] = lb == 4 ? 16.0f : 4.0f;
+    int64_t qrow = -1;
+    if (row < R) qrow = ((int64_t)(a.loop_base + row / G + z) * a.batch + b) * a.n_q_heads + kvh * G + row % G;
+#pragma unroll
+    for (int ks = 0; ks < NG; ++ks) {
+      qB[nb][ks] = qrow >= 0 ? *reinterpret_cast<const uint4*>(a.q + qrow * D + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
+      qtB[nb][ks] = make_uint4(0, 0, 0, 0);
+      qoff[nb][ks] = 0.0f;
     }
+    if constexpr (RESID) {
+      if (qrow >= 0 && lb != 0) {
+        const unsigned char* rec = a.qprep + qrow * Gm::PREP_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < NG; ++ks)
-      qB[nb][ks] = qp ? *reinterpret_cast<const uint4*>(qp + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
-  }
-
-  // Residual-score B operand (fp16 rotated query). Lane (m, g), k-step ks,
-  // element 2i <-> coordinate 32ks + 16(g>>1) + 4(g&1) + i, element 2i+1 <-> +8;
-  // this matches how the code words are unpacked below.
-  uint4 qtB[NB][NG];
-  float qoff[NB][NG];   // -(2^b + offset) * sum of the group's rotated query coordinates
-  float qmul[NB];       // 2^b of the row's own loop
-  (void)qtB; (void)qoff; (void)qmul;
-  if constexpr (RESID) {
-    float* qs = reinterpret_cast<float*>(smem);  // [NR][D]
-    for (int i = threadIdx.x; i < NR * D; i += 256) {
-      const int r = i / D, d = i % D;
-      float v = 0.0f;
-      if (r < R) {
-        const int loop = a.loop_base + r / G + z;
-        const uint16_t qb = a.q[(((int64_t)loop * a.batch + b) * a.n_q_heads + kvh * G + r % G) * D + d];
-        v = __uint_as_float((uint32_t)qb << 16);
-      }
-      qs[i] = v;
-    }
-    __syncthreads();
-    for (int h = 1; h < D; h <<= 1) {
-      for (int i = threadIdx.x; i < NR * D / 2; i += 256) {
-        const int r = i / (D / 2), k = i % (D / 2);
-        const int lo = r * D + (k / h) * 2 * h + (k % h);
-        const float x = qs[lo], y = qs[lo + h];
-        qs[lo] = x + y;
-        qs[lo + h] = x - y;
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const float* qr = qs + (16 * nb + m) * D;
-      const int lb = my_loop[nb] >= 0 ? a.bits[my_loop[nb]] : 0;
-      qmul[nb] = lb == 4 ? 16.0f : 4.0f;
-      const float off = lb == 4 ? 23.5f : 5.5f;  // 2^b + (2^(b-1) - 1/2)
-#pragma unroll
-      for (int ks = 0; ks < NG; ++ks) {
-        uint32_t w[4];
-        float part = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d0 = 32 * ks + 16 * (g >> 1) + 4 * (g & 1) + i;
-          const f16x2_t h2 = {(_Float16)(qr[d0] * RsqrtD<D>::v), (_Float16)(qr[d0 + 8] * RsqrtD<D>::v)};
-          w[i] = __builtin_bit_cast(uint32_t, h2);
-          part += (float)h2[0] + (float)h2[1];
+        for (int ks = 0; ks < NG; ++ks) {
+          qtB[nb][ks] = *reinterpret_cast<const uint4*>(rec + 16 * (4 * ks + g));
+          qoff[nb][ks] = reinterpret_cast<const float*>(rec + 2 * D)[ks];
         }
-        qtB[nb][ks] = make_uint4(w[0], w[1], w[2], w[3]);
-        part += __shfl_xor(part, 16);
-        part += __shfl_xor(part, 32);
-        qoff[nb][ks] = -off * part;
       }
     }
-    __syncthreads();  // the per-wave tile buffers below reuse this LDS
   }
 
   // ------------------------------------------------------------ token loop
   unsigned char* wbase = smem + wave * a.lds_wave_bytes;
-  uint16_t* vt = reinterpret_cast<uint16_t*>(wbase);                        // [32][VTS] bf16
-  uint32_t* ct = reinterpret_cast<uint32_t*>(wbase + Gm::VTILE_BYTES);     // [words][kCodeStride]
-
   f32x4_t o_ref[NB][NH][4];
   f32x4_t o_res[NB][2 * NG];
   float m_run[NB], l_run[NB];
@@ -194,124 +458,57 @@ __global__ __launch_bounds__(256) void rq_decode_partial_mfma(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < 2 * NG; ++k) o_res[nb][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  (void)o_res;
 
   const int t_begin = split * a.tokens_per_split;
   const int t_end = min(S, t_begin + a.tokens_per_split);
+  const int tlast = t_end - 1;
   const uint16_t* kbase = a.k[z] + row_base * D;
   const uint16_t* vbase = a.v[z] + row_base * D;
 
   for (int t0 = t_begin + wave * kTile; t0 < t_end; t0 += 4 * kTile) {
-    // stage the V tile: 16-byte chunk c -> token c / (D/8), column 8 (c % (D/8))
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {
-      const int c = lane + 64 * i;
-      const int tok = c / (D / 8), col = c % (D / 8);
-      const int t = min(t0 + tok, t_end - 1);
-      const uint4 v = *reinterpret_cast<const uint4*>(vbase + (int64_t)t * D + 8 * col);
-      *reinterpret_cast<uint4*>(vt + tok * VTS + 8 * col) = v;
+    // ---- issue every load of the tile
+    if constexpr (RESID) {
+      int off = Gm::VT_BYTES;
+      for (int li = 0; li < a.n_loops_launch; ++li) {
+        const int bits = a.bits[li];
+        if (bits == 2) stage_loop<D, 2>(a, li, wbase + off, row_base, t0, tlast, lane);
+        else if (bits == 4) stage_loop<D, 4>(a, li, wbase + off, row_base, t0, tlast, lane);
+        off += loop_lds_bytes(D, bits);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < Gm::VT_INSTR; ++i) {
+      const int tok = i * Gm::VT_TOK + lane / (D / 8);
+      dma16(vbase + (int64_t)min(t0 + tok, tlast) * D + 8 * (lane % (D / 8)), wbase + i * Gm::VT_STRIDE);
+    }
+    uint4 ka[2][NG];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+      const uint16_t* kp = kbase + (int64_t)min(t0 + 16 * bk + m, tlast) * D + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) ka[bk][ks] = *reinterpret_cast<const uint4*>(kp + 32 * ks);
+    }
+    wait_vmem();
+    wave_sync_lds();
 
     // ---- scores S^T[token][row]: lane holds tokens t0 + 16bk + 4g + i of row 16nb + m
     f32x4_t sc[2][NB];
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-      const int t = min(t0 + 16 * bk + m, t_end - 1);
-      const uint16_t* kp = kbase + (int64_t)t * D + 8 * g;
-      uint4 ka[NG];
-#pragma unroll
-      for (int ks = 0; ks < NG; ++ks) ka[ks] = *reinterpret_cast<const uint4*>(kp + 32 * ks);
+    for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NG; ++ks) acc = mma_bf16(ka[ks], qB[nb][ks], acc);
+        for (int ks = 0; ks < NG; ++ks) acc = mma_bf16(ka[bk][ks], qB[nb][ks], acc);
         sc[bk][nb] = acc;
       }
-    }
-
     if constexpr (RESID) {
+      int off = Gm::VT_BYTES;
       for (int li = 0; li < a.n_loops_launch; ++li) {
         const int bits = a.bits[li];
-        if (bits == 0) continue;
-        const int words = D * bits / 32;
-#pragma unroll
-        for (int bk = 0; bk < 2; ++bk) {
-          // code words of token t0 + 16bk + m (this lane's A-operand row)
-          const int ta = min(t0 + 16 * bk + m, t_end - 1);
-          const uint32_t* cw = a.kc[li] + (row_base + ta) * words;
-          uint4 kx[NG];
-          if (bits == 2) {
-            uint32_t wsel[NG];
-            if constexpr (D == 128) {
-              const uint4 w0 = *reinterpret_cast<const uint4*>(cw);
-              const uint4 w1 = *reinterpret_cast<const uint4*>(cw + 4);
-              const bool hi = (g >> 1) != 0;
-              wsel[0] = hi ? w0.y : w0.x;
-              wsel[1] = hi ? w0.w : w0.z;
-              wsel[2] = hi ? w1.y : w1.x;
-              wsel[3] = hi ? w1.w : w1.z;
-            } else {
-              const uint4 w0 = *reinterpret_cast<const uint4*>(cw);
-              const bool hi = (g >> 1) != 0;
-              wsel[0] = hi ? w0.y : w0.x;
-              wsel[1] = hi ? w0.w : w0.z;
-            }
-            const uint32_t pre = (g & 1) ? 0u : 8u;
-#pragma unroll
-            for (int ks = 0; ks < NG; ++ks) {
-              const uint32_t w = wsel[ks] << pre;
-              kx[ks].x = (w & 0x03000300u) | 0x3C003C00u;
-              kx[ks].y = ((w >> 2) & 0x03000300u) | 0x3C003C00u;
-              kx[ks].z = ((w >> 4) & 0x03000300u) | 0x3C003C00u;
-              kx[ks].w = ((w >> 6) & 0x03000300u) | 0x3C003C00u;
-            }
-          } else {
-            const uint32_t f4 = 4u * (uint32_t)(4 * (g & 1));
-#pragma unroll
-            for (int ks = 0; ks < NG; ++ks) {
-              const uint2 w = *reinterpret_cast<const uint2*>(cw + 4 * ks + 2 * (g >> 1));
-              uint32_t e[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const uint32_t c0 = __builtin_amdgcn_ubfe(w.x, f4 + 4 * i, 4);
-                const uint32_t c1 = __builtin_amdgcn_ubfe(w.y, f4 + 4 * i, 4);
-                e[i] = (c1 << 22) | (c0 << 6) | 0x3C003C00u;
-              }
-              kx[ks] = make_uint4(e[0], e[1], e[2], e[3]);
-            }
-          }
-          // k scales of this lane's four C-layout tokens
-          float ksc[4][NG];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tt = min(t0 + 16 * bk + 4 * g + i, t_end - 1);
-            const uint16_t* sp = a.ks[li] + (row_base + tt) * NG;
-            if constexpr (NG == 4) {
-              const uint2 u = *reinterpret_cast<const uint2*>(sp);
-              ksc[i][0] = half_lo(u.x); ksc[i][1] = half_hi(u.x);
-              ksc[i][2] = half_lo(u.y); ksc[i][3] = half_hi(u.y);
-            } else {
-              const uint32_t u = *reinterpret_cast<const uint32_t*>(sp);
-              ksc[i][0] = half_lo(u); ksc[i][1] = half_hi(u);
-            }
-          }
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            if (li * G >= 16 * nb + 16 || li * G + G <= 16 * nb) continue;  // no row of loop li here
-            f32x4_t r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NG; ++ks) {
-              const f32x4_t c = mma_f16(kx[ks], qtB[nb][ks], f32x4_t{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-              for (int i = 0; i < 4; ++i) r[i] = fmaf(ksc[i][ks], fmaf(c[i], qmul[nb], qoff[nb][ks]), r[i]);
-            }
-            if (my_loop[nb] == li) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) sc[bk][nb][i] += r[i];
-            }
-          }
-        }
+        if (bits == 2) residual_scores<D, NB, 2>(a, li, wbase + off, qtB, qoff, qmul, my_loop, sc, m, g);
+        else if (bits == 4) residual_scores<D, NB, 4>(a, li, wbase + off, qtB, qoff, qmul, my_loop, sc, m, g);
+        off += loop_lds_bytes(D, bits);
       }
     }
 
@@ -339,17 +536,17 @@ __global__ __launch_bounds__(256) void rq_decode_partial_mfma(DecodeArgs a) {
         ls += p[nb][j];
       }
       l_run[nb] = fmaf(l_run[nb], alpha, ls);
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {  // running max moved for some row
 #pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
+        for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o_ref[nb][hh][r] *= alpha;
-      if constexpr (RESID) {
+          for (int r = 0; r < 4; ++r) o_ref[nb][hh][r] *= alpha;
+        if constexpr (RESID) {
 #pragma unroll
-        for (int k = 0; k < 2 * NG; ++k) o_res[nb][k] *= alpha;
+          for (int k = 0; k < 2 * NG; ++k) o_res[nb][k] *= alpha;
+        }
       }
     }
-
-    wave_sync_lds();  // V tile visible to the whole wave
 
     // ---- reference PV: O_ref^T[d][row] += V^T P^T, P = hi + lo in bf16
     uint4 pbh[NB], pbl[NB];
@@ -373,7 +570,7 @@ __global__ __launch_bounds__(256) void rq_decode_partial_mfma(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int tok = 16 * (j >> 2) + 4 * g + (j & 3);
-        vv[j] = *reinterpret_cast<const uint2*>(vt + tok * VTS + 64 * hh + 4 * m);
+        vv[j] = *reinterpret_cast<const uint2*>(wbase + Gm::vt_offset(tok) + 2 * (64 * hh + 4 * m));
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -391,218 +588,142 @@ __global__ __launch_bounds__(256) void rq_decode_partial_mfma(DecodeArgs a) {
       }
     }
 
-    // ---- residual PV: O_res^T[d][row] += lev^T (P s)^T, per loop
+    // ---- residual PV
     if constexpr (RESID) {
+      int off = Gm::VT_BYTES;
       for (int li = 0; li < a.n_loops_launch; ++li) {
         const int bits = a.bits[li];
-        if (bits == 0) continue;
-        const int words = D * bits / 32;
-        // stage this tile's V code words transposed: ct[word][token]
-        const int chunks = kTile * words / 4;
-        for (int c = lane; c < chunks; c += 64) {
-          const int tok = c / (words / 4), q4 = c % (words / 4);
-          const int t = min(t0 + tok, t_end - 1);
-          const uint4 w = *reinterpret_cast<const uint4*>(a.vc[li] + (row_base + t) * words + 4 * q4);
-          ct[(4 * q4 + 0) * kCodeStride + tok] = w.x;
-          ct[(4 * q4 + 1) * kCodeStride + tok] = w.y;
-          ct[(4 * q4 + 2) * kCodeStride + tok] = w.z;
-          ct[(4 * q4 + 3) * kCodeStride + tok] = w.w;
-        }
-        // v scales of this lane's eight B-operand tokens
-        uint32_t vsw[8][(NG + 1) / 2];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int tt = min(t0 + 16 * (j >> 2) + 4 * g + (j & 3), t_end - 1);
-          const uint16_t* sp = a.vs[li] + (row_base + tt) * NG;
-          if constexpr (NG == 4) {
-            const uint2 u = *reinterpret_cast<const uint2*>(sp);
-            vsw[j][0] = u.x;
-            vsw[j][1] = u.y;
-          } else {
-            vsw[j][0] = *reinterpret_cast<const uint32_t*>(sp);
-          }
-        }
-        wave_sync_lds();
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          if (li * G >= 16 * nb + 16 || li * G + G <= 16 * nb) continue;
-          const float mem = my_loop[nb] == li ? 1.0f : 0.0f;
-          float pm[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pm[j] = p[nb][j] * mem;
-#pragma unroll
-          for (int grp = 0; grp < NG; ++grp) {
-            uint32_t bw[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint32_t s0 = vsw[2 * i][grp >> 1], s1 = vsw[2 * i + 1][grp >> 1];
-              const float f0 = (grp & 1) ? half_hi(s0) : half_lo(s0);
-              const float f1 = (grp & 1) ? half_hi(s1) : half_lo(s1);
-              bw[i] = pack_rtz(pm[2 * i] * f0, pm[2 * i + 1] * f1);
-            }
-            const uint4 bop = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              // A rows: coordinate 32grp + 16hf + m; its code sits in word wv, field f
-              int wv, sh;
-              uint32_t selx;
-              if (bits == 2) {
-                wv = 2 * grp + hf;
-                selx = ((uint32_t)(m >> 2) << 8) | ((uint32_t)(4 + (m >> 2)) << 24);
-                sh = 2 * (m & 3);
-              } else {
-                wv = 4 * grp + 2 * hf + (m >> 3);
-                const int f = m & 7;
-                selx = ((uint32_t)(f >> 1) << 8) | ((uint32_t)(4 + (f >> 1)) << 24);
-                sh = 4 * (f & 1);
-              }
-              const uint4 wa = *reinterpret_cast<const uint4*>(ct + wv * kCodeStride + 4 * g);
-              const uint4 wb = *reinterpret_cast<const uint4*>(ct + wv * kCodeStride + 16 + 4 * g);
-              const uint32_t cw[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-              uint32_t y[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) y[i] = vperm(cw[2 * i + 1], cw[2 * i], selx) >> sh;
-              uint4 alo;
-              alo.x = vperm(0u, kLutInt2, (y[0] & 0x03000300u) | 0x000C000Cu);
-              alo.y = vperm(0u, kLutInt2, (y[1] & 0x03000300u) | 0x000C000Cu);
-              alo.z = vperm(0u, kLutInt2, (y[2] & 0x03000300u) | 0x000C000Cu);
-              alo.w = vperm(0u, kLutInt2, (y[3] & 0x03000300u) | 0x000C000Cu);
-              o_res[nb][2 * grp + hf] = mma_f16(alo, bop, o_res[nb][2 * grp + hf]);
-              if (bits == 4) {
-                uint4 ahi;
-                ahi.x = vperm(0u, kLutInt4Hi, ((y[0] >> 2) & 0x03000300u) | 0x000C000Cu);
-                ahi.y = vperm(0u, kLutInt4Hi, ((y[1] >> 2) & 0x03000300u) | 0x000C000Cu);
-                ahi.z = vperm(0u, kLutInt4Hi, ((y[2] >> 2) & 0x03000300u) | 0x000C000Cu);
-                ahi.w = vperm(0u, kLutInt4Hi, ((y[3] >> 2) & 0x03000300u) | 0x000C000Cu);
-                o_res[nb][2 * grp + hf] = mma_f16(ahi, bop, o_res[nb][2 * grp + hf]);
-              }
-            }
-          }
-        }
-        wave_sync_lds();  // code tile free for the next loop
+        if (bits == 2) residual_pv<D, NB, 2>(a, li, wbase + off, p, my_loop, o_res, m, g);
+        else if (bits == 4) residual_pv<D, NB, 4>(a, li, wbase + off, p, my_loop, o_res, m, g);
+        off += loop_lds_bytes(D, bits);
       }
     }
-    wave_sync_lds();  // V tile free for the next tile
+    wait_lds();
+    wave_sync_lds();  // this tile's LDS is free for the next tile's DMA
   }
 
   // ------------------------------------------------ merge the four waves
+  // Each wave leaves (m, l, o_ref, o_res) per row in its LDS slot; the block
+  // then sums the slots in wave order (reproducible) into one partial record.
   __syncthreads();
-  float* mw = reinterpret_cast<float*>(smem);  // [4][NR]
-  float* lw = mw + 4 * NR;                     // [4][NR]
-  float* acc_ref = lw + 4 * NR;                // [NR][D]
-  float* acc_res = acc_ref + NR * D;           // [NR][D]
+  float* slot = reinterpret_cast<float*>(smem) + wave * NR * REC;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
+    float* rs = slot + (16 * nb + m) * REC;
     float ls = l_run[nb];
     ls += __shfl_xor(ls, 16);
     ls += __shfl_xor(ls, 32);
     if (g == 0) {
-      mw[wave * NR + 16 * nb + m] = m_run[nb];
-      lw[wave * NR + 16 * nb + m] = ls;
+      rs[0] = m_run[nb];
+      rs[1] = ls;
+    }
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rs[2 + 64 * hh + 4 * (4 * g + i) + r] = o_ref[nb][hh][r][i];
+    if constexpr (RESID) {
+#pragma unroll
+      for (int k = 0; k < 2 * NG; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rs[2 + D + 16 * k + 4 * g + i] = o_res[nb][k][i];
     }
   }
   __syncthreads();
-  float fw[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int row = 16 * nb + m;
+  float* fac = reinterpret_cast<float*>(smem) + 4 * NR * REC;  // [NR][5]: max, 4 wave factors
+  if (threadIdx.x < NR) {
+    const float* s0 = reinterpret_cast<const float*>(smem) + threadIdx.x * REC;
     float mm = -INFINITY;
-    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, mw[w * NR + row]);
-    fw[nb] = m_run[nb] == -INFINITY ? 0.0f : exp2f(m_run[nb] - mm);
-  }
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float* ar = acc_ref + (16 * nb + m) * D;
-        float* as = acc_res + (16 * nb + m) * D;
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int d = 64 * hh + 4 * (4 * g + i) + r;
-              const float v = fw[nb] * o_ref[nb][hh][r][i];
-              ar[d] = (w == 0) ? v : ar[d] + v;
-            }
-        if constexpr (RESID) {
-#pragma unroll
-          for (int k = 0; k < 2 * NG; ++k)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int d = 16 * k + 4 * g + i;  // k = 2 grp + hf -> 32 grp + 16 hf
-              const float v = fw[nb] * o_res[nb][k][i];
-              as[d] = (w == 0) ? v : as[d] + v;
-            }
-        }
-      }
-    }
-    __syncthreads();
-  }
-  if constexpr (RESID) {
-    for (int h = 1; h < D; h <<= 1) {
-      for (int i = threadIdx.x; i < NR * D / 2; i += 256) {
-        const int r = i / (D / 2), k = i % (D / 2);
-        const int lo = r * D + (k / h) * 2 * h + (k % h);
-        const float x = acc_res[lo], y = acc_res[lo + h];
-        acc_res[lo] = x + y;
-        acc_res[lo + h] = x - y;
-      }
-      __syncthreads();
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, s0[w * NR * REC]);
+    fac[threadIdx.x * 5] = mm;
+    for (int w = 0; w < 4; ++w) {
+      const float mw = s0[w * NR * REC];
+      fac[threadIdx.x * 5 + 1 + w] = mw == -INFINITY ? 0.0f : exp2f(mw - mm);
     }
   }
-  for (int i = threadIdx.x; i < R * (D + 2); i += 256) {
-    const int r = i / (D + 2), e = i % (D + 2);
+  __syncthreads();
+  // Without residual loops the record ends after o_ref, unless the call's
+  // combine reads residual accumulators (other launches of the call carry
+  // residual loops): then this launch's rows get a zero one.
+  const int rec_len = (RESID || a.zero_residual) ? REC : D + 2;
+  for (int i = threadIdx.x; i < R * rec_len; i += 256) {
+    const int r = i / rec_len, e = i % rec_len;
     const int loop = a.loop_base + r / G + z;
     const int hq = kvh * G + r % G;
-    float* dst = a.ws + ((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.n_splits + split) * (D + 2);
-    float mm = -INFINITY;
-    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, mw[w * NR + r]);
+    float* dst = a.ws + ((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.n_splits + split) * REC;
+    const float* s0 = reinterpret_cast<const float*>(smem) + r * REC + e;
     float val;
     if (e == 0) {
-      val = mm;
-    } else if (e == 1) {
-      float ls = 0.0f;
-      for (int w = 0; w < 4; ++w) ls += mw[w * NR + r] == -INFINITY ? 0.0f : exp2f(mw[w * NR + r] - mm) * lw[w * NR + r];
-      val = ls;
+      val = fac[r * 5];
+    } else if (!RESID && e >= D + 2) {
+      val = 0.0f;
     } else {
-      const int d = e - 2;
-      val = acc_ref[r * D + d] + (RESID ? acc_res[r * D + d] * RsqrtD<D>::v : 0.0f);
+      val = 0.0f;
+      for (int w = 0; w < 4; ++w) val = fmaf(fac[r * 5 + 1 + w], s0[w * NR * REC], val);
     }
     dst[e] = val;
   }
 }
 
-// LDS bytes of one block: the larger of the setup / merge area and 4 wave tiles
-static int mfma_block_lds_bytes(int d, int nb, int max_bits) {
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+int decode_wave_lds_bytes(int head_dim, const int32_t* bits, int n_loops) {
+  int bytes = head_dim == 128 ? MfmaGeom<128>::VT_BYTES : MfmaGeom<64>::VT_BYTES;
+  for (int i = 0; i < n_loops; ++i) bytes += loop_lds_bytes(head_dim, bits[i]);
+  return bytes;
+}
+
+int query_prep_bytes(int head_dim) {
+  return head_dim == 128 ? MfmaGeom<128>::PREP_BYTES : MfmaGeom<64>::PREP_BYTES;
+}
+
+// LDS bytes of one block: the larger of the merge slots and 4 wave tiles
+static int block_lds_bytes(int d, int nb, int wave_bytes) {
   const int nr = 16 * nb;
-  const int merge = (8 * nr + 2 * nr * d) * 4;
-  const int tiles = 4 * mfma_wave_lds_bytes(d, max_bits);
+  const int merge = (4 * nr * (2 * d + 2) + 5 * nr) * 4;
+  const int tiles = 4 * wave_bytes;
   return merge > tiles ? merge : tiles;
 }
 
+template <int D, int NB, bool RESID>
+static void launch_mfma_kernel(const DecodeArgs& a, dim3 grid, int lds, hipStream_t stream) {
+  static bool attr_set = false;  // lift the default dynamic-LDS cap once per instantiation
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rq_decode_partial_mfma<D, NB, RESID>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kMaxBlockLds);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID>), grid, dim3(256), lds, stream, a);
+}
+
 template <int D, int NB>
-static void launch_mfma_d(DecodeArgs a, dim3 grid, bool residual, int max_bits, hipStream_t stream) {
-  a.lds_wave_bytes = mfma_wave_lds_bytes(D, max_bits);
-  const int lds = mfma_block_lds_bytes(D, NB, max_bits);
-  if (residual) hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, true>), grid, dim3(256), lds, stream, a);
-  else hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, false>), grid, dim3(256), lds, stream, a);
+static void launch_mfma_d(DecodeArgs a, dim3 grid, bool residual, hipStream_t stream) {
+  a.lds_wave_bytes = decode_wave_lds_bytes(D, a.bits, residual ? a.n_loops_launch : 0);
+  const int lds = block_lds_bytes(D, NB, a.lds_wave_bytes);
+  if (residual) launch_mfma_kernel<D, NB, true>(a, grid, lds, stream);
+  else launch_mfma_kernel<D, NB, false>(a, grid, lds, stream);
 }
 
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, int n_z, bool residual, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)a.n_splits * a.batch * a.n_kv_heads), n_z);
-  int max_bits = 0;
-  for (int li = 0; li < a.n_loops_launch; ++li) max_bits = a.bits[li] > max_bits ? a.bits[li] : max_bits;
-  if (!residual) max_bits = 0;
   const bool two = a.n_rows > 16;
   if (head_dim == 128) {
-    if (two) launch_mfma_d<128, 2>(a, grid, residual, max_bits, stream);
-    else launch_mfma_d<128, 1>(a, grid, residual, max_bits, stream);
+    if (two) launch_mfma_d<128, 2>(a, grid, residual, stream);
+    else launch_mfma_d<128, 1>(a, grid, residual, stream);
   } else {
-    if (two) launch_mfma_d<64, 2>(a, grid, residual, max_bits, stream);
-    else launch_mfma_d<64, 1>(a, grid, residual, max_bits, stream);
+    if (two) launch_mfma_d<64, 2>(a, grid, residual, stream);
+    else launch_mfma_d<64, 1>(a, grid, residual, stream);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_query_prep(const QueryPrepArgs& a, int head_dim, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.n_rows + 3) / 4));
+  if (head_dim == 128) hipLaunchKernelGGL(rq_query_prep<128>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(rq_query_prep<64>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -46,7 +46,8 @@ struct DecodeArgs {
   const uint16_t* ks[kMaxLoops];
   const uint32_t* vc[kMaxLoops];
   const uint16_t* vs[kMaxLoops];
-  float* ws;                            // partials [n_loops_total][B][Hq][n_splits][D + 2]
+  float* ws;                            // partials [n_loops_total][B][Hq][n_splits][2D + 2]
+  const unsigned char* qprep;           // rotated-query records [n_loops_total][B][Hq] (residual launches)
   int32_t loop_base;
   int32_t n_loops_launch;               // loops whose rows this launch holds
   int32_t n_rows;                       // n_loops_launch * G
@@ -55,6 +56,7 @@ struct DecodeArgs {
   int32_t n_splits, tokens_per_split;
   float scale_log2;                     // softmax scale * log2(e)
   int32_t lds_wave_bytes;               // per-wave LDS stride (set by the launcher)
+  int32_t zero_residual;                // write a zero residual accumulator (reference-only launch)
 };
 
 struct CombineArgs {
@@ -62,6 +64,15 @@ struct CombineArgs {
   float* out;
   int64_t n_out;       // n_loops * B * Hq
   int32_t n_splits;
+  int32_t residual;    // records carry a rotated-domain residual accumulator
+};
+
+struct QueryPrepArgs {
+  const uint16_t* q;            // [n_loops][B][Hq][D] bf16
+  unsigned char* out;           // one record per query row
+  int32_t bits[kMaxLoops];      // residual width of each loop (selects the offset constant)
+  int64_t n_rows;               // n_loops * B * Hq
+  int32_t batch, n_q_heads;
 };
 
 // ---------------------------------------------------------------------------
@@ -72,8 +83,18 @@ hipError_t launch_encode(const EncodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_reconstruct(const ReconstructArgs& a, int head_dim, int bits, int out_bf16, hipStream_t stream);
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, int n_z, bool residual, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_query_prep(const QueryPrepArgs& a, int head_dim, hipStream_t stream);
+
+// bytes of one rotated-query record
+int query_prep_bytes(int head_dim);
 
 // tile of tokens one decode block iteration covers; split boundaries are multiples of it
 constexpr int kDecodeTile = 64;
+
+// LDS one decode block may use (gfx950: 160 KB per workgroup)
+constexpr int kMaxBlockLds = 160 * 1024;
+
+// LDS bytes one decode wave stages per token tile for the given residual loops
+int decode_wave_lds_bytes(int head_dim, const int32_t* bits, int n_loops);
 
 }  // namespace rq
