@@ -9,7 +9,9 @@ K steps are timed between two device synchronisations. `value` is KV tokens
 through the hot path per second: batch * seq_len * n_loops / step time.
 
 Timed in the same run, each alone and outside the timed steps, with the
-256 MB last-level cache flushed before every repetition:
+256 MB last-level cache flushed before every repetition by reading a 1 GiB
+buffer (a read leaves no dirty lines whose write-back would compete with the
+measured kernel):
 * rq_decode_attn alone: KV tokens/s, algorithmic GB/s and the fraction of the
   8 TB/s HBM peak;
 * the bf16-KV baseline decode (rq_decode_attn_bf16) over the same loops;
@@ -282,12 +284,12 @@ def main():
     result["wall_s_timed"] = wall_s
 
     if not args.only_step:
-        flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+        flush = torch.ones(2 ** 28, dtype=torch.float32, device=dev)  # 1 GiB, read to evict the caches
 
         def timed(fn, reps):
             ts = []
             for _ in range(reps):
-                flush.zero_()
+                flush.amax()
                 a, b = Ev(enable_timing=True), Ev(enable_timing=True)
                 a.record(stream); fn(); b.record(stream)
                 torch.cuda.synchronize()

@@ -32,9 +32,10 @@ int check_heads(const rq_shape* s, int32_t n_q_heads, int32_t n_loops) {
   return RQ_OK;
 }
 
-// Target number of partial blocks per launch; a split never holds fewer
-// tokens than one tile.
-constexpr int64_t kTargetBlocks = 1024;
+// Target number of partial blocks per launch (two resident blocks per CU on
+// 256 CUs, the best point of a split sweep on l4_b16_s4k and mixed_s32k); a
+// split never holds fewer tokens than one tile.
+constexpr int64_t kTargetBlocks = 512;
 
 struct SplitPlan {
   int32_t n_splits;

@@ -389,6 +389,155 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
   }
 }
 
+// Issue every load of one tile: the residual loops' codes and scales and the
+// V reference tile by LDS DMA into `buf`, the K reference into registers.
+template <int D, bool RESID>
+__device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* buf, const uint16_t* kbase,
+                                           const uint16_t* vbase, int64_t row_base, int t0, int tlast, int lane,
+                                           int m, int g, uint4 (&ka)[2][D / 32]) {
+  using Gm = MfmaGeom<D>;
+  constexpr int NG = Gm::NG;
+  if constexpr (RESID) {
+    int off = Gm::VT_BYTES;
+    for (int li = 0; li < a.n_loops_launch; ++li) {
+      const int bits = a.bits[li];
+      if (bits == 2) stage_loop<D, 2>(a, li, buf + off, row_base, t0, tlast, lane);
+      else if (bits == 4) stage_loop<D, 4>(a, li, buf + off, row_base, t0, tlast, lane);
+      off += loop_lds_bytes(D, bits);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < Gm::VT_INSTR; ++i) {
+    const int tok = i * Gm::VT_TOK + lane / (D / 8);
+    dma16(vbase + (int64_t)min(t0 + tok, tlast) * D + 8 * (lane % (D / 8)), buf + i * Gm::VT_STRIDE);
+  }
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+    const uint16_t* kp = kbase + (int64_t)min(t0 + 16 * bk + m, tlast) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < NG; ++ks) ka[bk][ks] = *reinterpret_cast<const uint4*>(kp + 32 * ks);
+  }
+}
+
+// Scores, online softmax and PV of one staged tile.
+template <int D, int NB, bool RESID>
+__device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned char* buf, int t0, int t_end,
+                                             int m, int g, const uint4 (&ka)[2][D / 32], const uint4 (&qB)[NB][D / 32],
+                                             const uint4 (&qtB)[NB][D / 32], const float (&qoff)[NB][D / 32],
+                                             const float (&qmul)[NB], const int (&my_loop)[NB],
+                                             f32x4_t (&o_ref)[NB][D / 64][4], f32x4_t (&o_res)[NB][2 * (D / 32)],
+                                             float (&m_run)[NB], float (&l_run)[NB]) {
+  using Gm = MfmaGeom<D>;
+  constexpr int NG = Gm::NG, NH = Gm::NH;
+  // ---- scores S^T[token][row]: lane holds tokens t0 + 16bk + 4g + i of row 16nb + m
+  f32x4_t sc[2][NB];
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) acc = mma_bf16(ka[bk][ks], qB[nb][ks], acc);
+      sc[bk][nb] = acc;
+    }
+  if constexpr (RESID) {
+    int off = Gm::VT_BYTES;
+    for (int li = 0; li < a.n_loops_launch; ++li) {
+      const int bits = a.bits[li];
+      if (bits == 2) residual_scores<D, NB, 2>(a, li, buf + off, qtB, qoff, qmul, my_loop, sc, m, g);
+      else if (bits == 4) residual_scores<D, NB, 4>(a, li, buf + off, qtB, qoff, qmul, my_loop, sc, m, g);
+      off += loop_lds_bytes(D, bits);
+    }
+  }
+
+  // ---- online softmax (log2 domain); row statistics live in the row's 4 lanes
+  float p[NB][8];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float zz[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
+      zz[j] = t < t_end ? sc[j >> 2][nb][j & 3] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, zz[j]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run[nb], mx);
+    const float alpha = exp2f(m_run[nb] - m_new);
+    m_run[nb] = m_new;
+    float ls = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[nb][j] = exp2f(zz[j] - m_new);
+      ls += p[nb][j];
+    }
+    l_run[nb] = fmaf(l_run[nb], alpha, ls);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {  // running max moved for some row
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o_ref[nb][hh][r] *= alpha;
+      if constexpr (RESID) {
+#pragma unroll
+        for (int k = 0; k < 2 * NG; ++k) o_res[nb][k] *= alpha;
+      }
+    }
+  }
+
+  // ---- reference PV: O_ref^T[d][row] += V^T P^T, P = hi + lo in bf16
+  uint4 pbh[NB], pbl[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u0 = __float_as_uint(p[nb][2 * i]), u1 = __float_as_uint(p[nb][2 * i + 1]);
+      hi[i] = vperm(u1, u0, 0x07060302u);
+      const float r0 = p[nb][2 * i] - __uint_as_float(u0 & 0xFFFF0000u);
+      const float r1 = p[nb][2 * i + 1] - __uint_as_float(u1 & 0xFFFF0000u);
+      lo[i] = vperm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+    }
+    pbh[nb] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    pbl[nb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    uint2 vv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tok = 16 * (j >> 2) + 4 * g + (j & 3);
+      vv[j] = *reinterpret_cast<const uint2*>(buf + Gm::vt_offset(tok) + 2 * (64 * hh + 4 * m));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
+      uint4 av;
+      av.x = vperm(r < 2 ? vv[1].x : vv[1].y, r < 2 ? vv[0].x : vv[0].y, sel);
+      av.y = vperm(r < 2 ? vv[3].x : vv[3].y, r < 2 ? vv[2].x : vv[2].y, sel);
+      av.z = vperm(r < 2 ? vv[5].x : vv[5].y, r < 2 ? vv[4].x : vv[4].y, sel);
+      av.w = vperm(r < 2 ? vv[7].x : vv[7].y, r < 2 ? vv[6].x : vv[6].y, sel);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        o_ref[nb][hh][r] = mma_bf16(av, pbh[nb], o_ref[nb][hh][r]);
+        o_ref[nb][hh][r] = mma_bf16(av, pbl[nb], o_ref[nb][hh][r]);
+      }
+    }
+  }
+
+  // ---- residual PV
+  if constexpr (RESID) {
+    int off = Gm::VT_BYTES;
+    for (int li = 0; li < a.n_loops_launch; ++li) {
+      const int bits = a.bits[li];
+      if (bits == 2) residual_pv<D, NB, 2>(a, li, buf + off, p, my_loop, o_res, m, g);
+      else if (bits == 4) residual_pv<D, NB, 4>(a, li, buf + off, p, my_loop, o_res, m, g);
+      off += loop_lds_bytes(D, bits);
+    }
+  }
+}
+
 template <int D, int NB, bool RESID>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RESID && NB == 2 ? 1 : 2,
                                                                      RESID && NB == 1 ? 2 : 4)))
@@ -443,7 +592,10 @@ void rq_decode_partial_mfma(DecodeArgs a) {
   }
 
   // ------------------------------------------------------------ token loop
-  unsigned char* wbase = smem + wave * a.lds_wave_bytes;
+  // One tile buffer per wave: with two waves per SIMD, one wave's compute
+  // covers the other's load latency. Measured on MI355X, a second buffer per
+  // wave (prefetching the next tile) costs more occupancy than it hides.
+  unsigned char* buf = smem + wave * a.lds_wave_bytes;
   f32x4_t o_ref[NB][NH][4];
   f32x4_t o_res[NB][2 * NG];
   float m_run[NB], l_run[NB];
@@ -464,142 +616,16 @@ void rq_decode_partial_mfma(DecodeArgs a) {
   const int tlast = t_end - 1;
   const uint16_t* kbase = a.k[z] + row_base * D;
   const uint16_t* vbase = a.v[z] + row_base * D;
+  constexpr int kStep = 4 * kTile;  // tokens between a wave's consecutive tiles
 
-  for (int t0 = t_begin + wave * kTile; t0 < t_end; t0 += 4 * kTile) {
-    // ---- issue every load of the tile
-    if constexpr (RESID) {
-      int off = Gm::VT_BYTES;
-      for (int li = 0; li < a.n_loops_launch; ++li) {
-        const int bits = a.bits[li];
-        if (bits == 2) stage_loop<D, 2>(a, li, wbase + off, row_base, t0, tlast, lane);
-        else if (bits == 4) stage_loop<D, 4>(a, li, wbase + off, row_base, t0, tlast, lane);
-        off += loop_lds_bytes(D, bits);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < Gm::VT_INSTR; ++i) {
-      const int tok = i * Gm::VT_TOK + lane / (D / 8);
-      dma16(vbase + (int64_t)min(t0 + tok, tlast) * D + 8 * (lane % (D / 8)), wbase + i * Gm::VT_STRIDE);
-    }
-    uint4 ka[2][NG];
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-      const uint16_t* kp = kbase + (int64_t)min(t0 + 16 * bk + m, tlast) * D + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < NG; ++ks) ka[bk][ks] = *reinterpret_cast<const uint4*>(kp + 32 * ks);
-    }
+  uint4 ka[2][NG];
+  for (int t0 = t_begin + wave * kTile; t0 < t_end; t0 += kStep) {
+    issue_tile<D, RESID>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
     wait_vmem();
     wave_sync_lds();
-
-    // ---- scores S^T[token][row]: lane holds tokens t0 + 16bk + 4g + i of row 16nb + m
-    f32x4_t sc[2][NB];
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NG; ++ks) acc = mma_bf16(ka[bk][ks], qB[nb][ks], acc);
-        sc[bk][nb] = acc;
-      }
-    if constexpr (RESID) {
-      int off = Gm::VT_BYTES;
-      for (int li = 0; li < a.n_loops_launch; ++li) {
-        const int bits = a.bits[li];
-        if (bits == 2) residual_scores<D, NB, 2>(a, li, wbase + off, qtB, qoff, qmul, my_loop, sc, m, g);
-        else if (bits == 4) residual_scores<D, NB, 4>(a, li, wbase + off, qtB, qoff, qmul, my_loop, sc, m, g);
-        off += loop_lds_bytes(D, bits);
-      }
-    }
-
-    // ---- online softmax (log2 domain); row statistics live in the row's 4 lanes
-    float p[NB][8];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float zz[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
-        zz[j] = t < t_end ? sc[j >> 2][nb][j & 3] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, zz[j]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[nb], mx);
-      const float alpha = exp2f(m_run[nb] - m_new);
-      m_run[nb] = m_new;
-      float ls = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[nb][j] = exp2f(zz[j] - m_new);
-        ls += p[nb][j];
-      }
-      l_run[nb] = fmaf(l_run[nb], alpha, ls);
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {  // running max moved for some row
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o_ref[nb][hh][r] *= alpha;
-        if constexpr (RESID) {
-#pragma unroll
-          for (int k = 0; k < 2 * NG; ++k) o_res[nb][k] *= alpha;
-        }
-      }
-    }
-
-    // ---- reference PV: O_ref^T[d][row] += V^T P^T, P = hi + lo in bf16
-    uint4 pbh[NB], pbl[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t u0 = __float_as_uint(p[nb][2 * i]), u1 = __float_as_uint(p[nb][2 * i + 1]);
-        hi[i] = vperm(u1, u0, 0x07060302u);
-        const float r0 = p[nb][2 * i] - __uint_as_float(u0 & 0xFFFF0000u);
-        const float r1 = p[nb][2 * i + 1] - __uint_as_float(u1 & 0xFFFF0000u);
-        lo[i] = vperm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
-      }
-      pbh[nb] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      pbl[nb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    }
-#pragma unroll
-    for (int hh = 0; hh < NH; ++hh) {
-      uint2 vv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int tok = 16 * (j >> 2) + 4 * g + (j & 3);
-        vv[j] = *reinterpret_cast<const uint2*>(wbase + Gm::vt_offset(tok) + 2 * (64 * hh + 4 * m));
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t sel = (r & 1) ? 0x07060302u : 0x05040100u;
-        uint4 av;
-        av.x = vperm(r < 2 ? vv[1].x : vv[1].y, r < 2 ? vv[0].x : vv[0].y, sel);
-        av.y = vperm(r < 2 ? vv[3].x : vv[3].y, r < 2 ? vv[2].x : vv[2].y, sel);
-        av.z = vperm(r < 2 ? vv[5].x : vv[5].y, r < 2 ? vv[4].x : vv[4].y, sel);
-        av.w = vperm(r < 2 ? vv[7].x : vv[7].y, r < 2 ? vv[6].x : vv[6].y, sel);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          o_ref[nb][hh][r] = mma_bf16(av, pbh[nb], o_ref[nb][hh][r]);
-          o_ref[nb][hh][r] = mma_bf16(av, pbl[nb], o_ref[nb][hh][r]);
-        }
-      }
-    }
-
-    // ---- residual PV
-    if constexpr (RESID) {
-      int off = Gm::VT_BYTES;
-      for (int li = 0; li < a.n_loops_launch; ++li) {
-        const int bits = a.bits[li];
-        if (bits == 2) residual_pv<D, NB, 2>(a, li, wbase + off, p, my_loop, o_res, m, g);
-        else if (bits == 4) residual_pv<D, NB, 4>(a, li, wbase + off, p, my_loop, o_res, m, g);
-        off += loop_lds_bytes(D, bits);
-      }
-    }
+    compute_tile<D, NB, RESID>(a, buf, t0, t_end, m, g, ka, qB, qtB, qoff, qmul, my_loop, o_ref, o_res, m_run, l_run);
     wait_lds();
-    wave_sync_lds();  // this tile's LDS is free for the next tile's DMA
+    wave_sync_lds();  // the buffer is free for the next tile's DMA
   }
 
   // ------------------------------------------------ merge the four waves
