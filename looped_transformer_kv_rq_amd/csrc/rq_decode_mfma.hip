@@ -629,66 +629,85 @@ void rq_decode_partial_mfma(DecodeArgs a) {
   }
 
   // ------------------------------------------------ merge the four waves
-  // Each wave leaves (m, l, o_ref, o_res) per row in its LDS slot; the block
-  // then sums the slots in wave order (reproducible) into one partial record.
+  // Each wave leaves (m, l) and one accumulator per row in its LDS slot; the
+  // block sums the slots in wave order (reproducible) into the partial record.
+  // The reference and residual accumulators go through the slots one after
+  // the other, so the merge needs 4 * NR * (D + 2) floats of LDS.
+  constexpr int SREC = D + 2;
   __syncthreads();
-  float* slot = reinterpret_cast<float*>(smem) + wave * NR * REC;
+  float* slots = reinterpret_cast<float*>(smem);
+  float* fac = slots + 4 * NR * SREC;  // [NR][5]: max, 4 wave factors
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float* rs = slot + (16 * nb + m) * REC;
-    float ls = l_run[nb];
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    if (g == 0) {
-      rs[0] = m_run[nb];
-      rs[1] = ls;
+  for (int pass = 0; pass < (RESID ? 2 : 1); ++pass) {
+    float* slot = slots + wave * NR * SREC;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float* rs = slot + (16 * nb + m) * SREC;
+      if (pass == 0) {
+        float ls = l_run[nb];
+        ls += __shfl_xor(ls, 16);
+        ls += __shfl_xor(ls, 32);
+        if (g == 0) {
+          rs[0] = m_run[nb];
+          rs[1] = ls;
+        }
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rs[2 + 64 * hh + 4 * (4 * g + i) + r] = o_ref[nb][hh][r][i];
+      } else {
+#pragma unroll
+        for (int k = 0; k < 2 * NG; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rs[2 + 16 * k + 4 * g + i] = o_res[nb][k][i];
+      }
     }
-#pragma unroll
-    for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rs[2 + 64 * hh + 4 * (4 * g + i) + r] = o_ref[nb][hh][r][i];
-    if constexpr (RESID) {
-#pragma unroll
-      for (int k = 0; k < 2 * NG; ++k)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rs[2 + D + 16 * k + 4 * g + i] = o_res[nb][k][i];
+    __syncthreads();
+    if (pass == 0 && threadIdx.x < NR) {
+      const float* s0 = slots + threadIdx.x * SREC;
+      float mm = -INFINITY;
+      for (int w = 0; w < 4; ++w) mm = fmaxf(mm, s0[w * NR * SREC]);
+      fac[threadIdx.x * 5] = mm;
+      for (int w = 0; w < 4; ++w) {
+        const float mw = s0[w * NR * SREC];
+        fac[threadIdx.x * 5 + 1 + w] = mw == -INFINITY ? 0.0f : exp2f(mw - mm);
+      }
     }
+    if (pass == 0) __syncthreads();
+    // record elements of this pass: [m, l, o_ref] or [o_res]
+    const int e0 = pass == 0 ? 0 : D + 2;
+    for (int i = threadIdx.x; i < R * SREC; i += 256) {
+      const int r = i / SREC, e = i % SREC;
+      if (pass == 1 && e >= D) continue;
+      const int loop = a.loop_base + r / G + z;
+      const int hq = kvh * G + r % G;
+      float* dst = a.ws + ((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.n_splits + split) * REC + e0;
+      const float* s0 = slots + r * SREC + (pass == 0 ? e : 2 + e);
+      float val;
+      if (pass == 0 && e == 0) {
+        val = fac[r * 5];
+      } else {
+        val = 0.0f;
+        for (int w = 0; w < 4; ++w) val = fmaf(fac[r * 5 + 1 + w], s0[w * NR * SREC], val);
+      }
+      dst[e] = val;
+    }
+    __syncthreads();  // slots are rewritten by the next pass
   }
-  __syncthreads();
-  float* fac = reinterpret_cast<float*>(smem) + 4 * NR * REC;  // [NR][5]: max, 4 wave factors
-  if (threadIdx.x < NR) {
-    const float* s0 = reinterpret_cast<const float*>(smem) + threadIdx.x * REC;
-    float mm = -INFINITY;
-    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, s0[w * NR * REC]);
-    fac[threadIdx.x * 5] = mm;
-    for (int w = 0; w < 4; ++w) {
-      const float mw = s0[w * NR * REC];
-      fac[threadIdx.x * 5 + 1 + w] = mw == -INFINITY ? 0.0f : exp2f(mw - mm);
-    }
-  }
-  __syncthreads();
   // Without residual loops the record ends after o_ref, unless the call's
   // combine reads residual accumulators (other launches of the call carry
   // residual loops): then this launch's rows get a zero one.
-  const int rec_len = (RESID || a.zero_residual) ? REC : D + 2;
-  for (int i = threadIdx.x; i < R * rec_len; i += 256) {
-    const int r = i / rec_len, e = i % rec_len;
-    const int loop = a.loop_base + r / G + z;
-    const int hq = kvh * G + r % G;
-    float* dst = a.ws + ((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.n_splits + split) * REC;
-    const float* s0 = reinterpret_cast<const float*>(smem) + r * REC + e;
-    float val;
-    if (e == 0) {
-      val = fac[r * 5];
-    } else if (!RESID && e >= D + 2) {
-      val = 0.0f;
-    } else {
-      val = 0.0f;
-      for (int w = 0; w < 4; ++w) val = fmaf(fac[r * 5 + 1 + w], s0[w * NR * REC], val);
+  if constexpr (!RESID) {
+    if (a.zero_residual) {
+      for (int i = threadIdx.x; i < R * D; i += 256) {
+        const int r = i / D, e = i % D;
+        const int loop = a.loop_base + r / G + z;
+        const int hq = kvh * G + r % G;
+        a.ws[((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.n_splits + split) * REC + D + 2 + e] = 0.0f;
+      }
     }
-    dst[e] = val;
   }
 }
 
@@ -709,7 +728,7 @@ int query_prep_bytes(int head_dim) {
 // LDS bytes of one block: the larger of the merge slots and 4 wave tiles
 static int block_lds_bytes(int d, int nb, int wave_bytes) {
   const int nr = 16 * nb;
-  const int merge = (4 * nr * (2 * d + 2) + 5 * nr) * 4;
+  const int merge = (4 * nr * (d + 2) + 5 * nr) * 4;
   const int tiles = 4 * wave_bytes;
   return merge > tiles ? merge : tiles;
 }
