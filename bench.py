@@ -52,8 +52,12 @@ import workloads  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decode-attn KV tokens/s & achieved HBM GB/s (% of peak); encode GB/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+_CSRC = os.path.join(ROOT, "looped_transformer_kv_rq_amd", "csrc")
+# sources each counted kernel is built from (a change to any of them voids its traffic figure)
 KERNEL_SOURCES = {
-    "encode": os.path.join(ROOT, "looped_transformer_kv_rq_amd", "csrc", "rq_codec.hip"),
+    "encode": [os.path.join(_CSRC, f) for f in ("rq_codec.hip", "rq_device.h", "rq_internal.h")],
+    "decode_attn": [os.path.join(_CSRC, f) for f in ("rq_decode_mfma.hip", "rq_combine.hip", "rq_api.hip",
+                                                      "rq_device.h", "rq_internal.h")],
 }
 
 
@@ -145,13 +149,17 @@ def cpu_baseline(w, rows_per_worker=4):
 # GPU measurement
 # ---------------------------------------------------------------------------
 
-def _sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def _sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(kernel_key, workload_name):
-    """HBM bytes per launch from the committed PMC summary, if the kernel is unchanged."""
+    """HBM bytes per launch (per call for decode_attn) from the committed PMC summary, if the
+    kernel sources are unchanged since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)[kernel_key]
@@ -160,6 +168,24 @@ def _traffic(kernel_key, workload_name):
     if rec.get("workload") != workload_name or rec.get("source_sha") != _sha(KERNEL_SOURCES[kernel_key]):
         return None
     return rec.get("bytes_per_launch")
+
+
+COPY_PROBE_BYTES = 256 * 2 ** 20
+
+
+def copy_probe():
+    """Five copies of COPY_PROBE_BYTES between two device buffers: each reads and
+    writes exactly that many bytes, so a counter's reading per copy gives its
+    scale factor (bytes per reported unit)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 5}))
 
 
 def main():
@@ -171,12 +197,19 @@ def main():
     ap.add_argument("--reps", type=int, default=20, help="repetitions of each side measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-step", action="store_true", help="time the step only (for profiling runs)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain 256 MiB device-to-device copy, five times: the reference kernel "
+                         "whose FETCH_SIZE / WRITE_SIZE readings calibrate the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X: the ResidualQuant hot path has no cross-GPU step; "
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     w = workloads.WORKLOADS[args.workload]
     if w.name == "peak_batch":
@@ -301,7 +334,8 @@ def main():
         result["roofline_decode"] = {
             "kernel": "rq_decode_attn (split-S partial + combine), all loops, cache flushed",
             "bound": "hbm", "achieved": dec_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": None, "algorithmic_bytes_per_call": dec_b,
+            "frac": dec_gbps / HBM_PEAK_GBPS, "traffic": _traffic("decode_attn", w.name),
+            "algorithmic_bytes_per_call": dec_b,
         }
         out_b = torch.empty_like(out)
         ws_b = torch.empty_like(ws)

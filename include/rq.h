@@ -100,7 +100,8 @@ typedef struct rq_loop_view {
  *   ref       bf16 [B][Hkv][S][D], the final loop
  *   codes[i]  out: uint32 [B][Hkv][S][D*bits[i]/32]
  *   scales[i] out: fp16  [B][Hkv][S][D/32]
- * The output is deterministic: it depends only on the inputs. */
+ * The inputs must be finite. The output is deterministic: it depends only on
+ * the inputs. */
 int rq_encode(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
               const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, void* stream);
 

@@ -29,67 +29,156 @@ struct Grid {
   static constexpr int kPerWord = 32 / BITS;          // codes per uint32
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// x_lo * c_lo + x_hi * c_hi + acc over one pair of bf16 (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t c, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), __builtin_bit_cast(bf16x2_t, c), acc,
+                                         false);
+}
+constexpr uint32_t kPairSum = 0x3F803F80u;   // bf16 (+1, +1)
+constexpr uint32_t kPairDiff = 0xBF803F80u;  // bf16 (+1, -1), low half first
+
 // Quantize one rotated group (unnormalised transform values y' = sqrt(D) y)
-// and store its packed codes and fp16 scale. Codes are invariant to the
+// and return its packed code words and the scale. Codes are invariant to the
 // common sqrt(D) factor; the scale is divided by it at the end.
+//  * c = floor(y / s0) + 2^(b-1) with 1 / s0 = (2^(b-1) - 1/2) / max|y|. For
+//    finite inputs |y / s0| <= 2^(b-1) - 1/2, so c already lies in
+//    [0, 2^b - 1] and needs no clamp. An all-zero group takes 1 / s0 = 0,
+//    which gives every code 2^(b-1) and num = 0, so s = 0.
+//  * Packing sums c * 2^(b i) in fp32 over 16-bit halves of a word (exact:
+//    every partial sum is an integer below 2^16).
+//  * INT2: q^2 is 1/4 for the inner codes 1, 2 and 9/4 for 0, 3, so
+//    <q, q> = 72 - 2 * (number of inner codes), counted on the packed words.
 template <int BITS, int D>
-__device__ __forceinline__ void quantize_group_store(const float (&y)[32], uint32_t* __restrict__ codes,
-                                                     uint16_t* __restrict__ scales, int64_t v, int g) {
+__device__ __forceinline__ float quantize_group(const float* y, uint32_t (&words)[BITS]) {
   using G = Grid<BITS>;
+  constexpr int kPerHalf = G::kPerWord / 2;  // codes per 16-bit half word
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(y[i]));
-
-  uint32_t words[BITS];
+  const float inv = m > 0.0f ? G::kOff / m : 0.0f;
+  float num = 0.0f, den = 0.0f;
+  float half[2 * BITS];
 #pragma unroll
-  for (int k = 0; k < BITS; ++k) words[k] = 0u;
-  float s = 0.0f;
-  if (m > 0.0f) {
-    const float inv = G::kOff / m;  // 1 / s0
-    float num = 0.0f, den = 0.0f;
+  for (int k = 0; k < 2 * BITS; ++k) half[k] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float c = fminf(fmaxf(floorf(y[i] * inv) + (float)G::kHalf, 0.0f), (float)G::kTop);
-      const float q = c - G::kOff;
-      num = fmaf(y[i], q, num);
-      den = fmaf(q, q, den);
-      words[i / G::kPerWord] |= (uint32_t)c << (BITS * (i % G::kPerWord));
-    }
-    s = num / den * RsqrtD<D>::v;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) words[i / G::kPerWord] |= (uint32_t)G::kHalf << (BITS * (i % G::kPerWord));
+  for (int i = 0; i < 32; ++i) {
+    const float c = floorf(fmaf(y[i], inv, (float)G::kHalf));
+    const float q = c - G::kOff;
+    num = fmaf(y[i], q, num);
+    if constexpr (BITS == 4) den = fmaf(q, q, den);
+    half[i / kPerHalf] = fmaf(c, (float)(1u << (BITS * (i % kPerHalf))), half[i / kPerHalf]);
   }
-  uint32_t* dst = codes + v * (D * BITS / 32) + g * BITS;
+#pragma unroll
+  for (int k = 0; k < BITS; ++k)
+    words[k] = (uint32_t)half[2 * k] | ((uint32_t)half[2 * k + 1] << 16);
   if constexpr (BITS == 2) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
-  } else {
-    *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
+    int inner = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) inner += __builtin_popcount((words[k] ^ (words[k] >> 1)) & 0x55555555u);
+    den = (float)(72 - 2 * inner);
   }
-  scales[v * (D / 32) + g] = f32_to_f16_sat(s);
+  return num / den * RsqrtD<D>::v;
 }
 
-template <int D>
+// Encode kernel: PER coordinates of a vector per lane (PER / 32 scale
+// groups), D / PER consecutive lanes per vector.
+//  * The first butterfly (index bit 0) is folded into the bf16 unpacking:
+//    for the pair (x0, x1) with reference (r0, r1), one dot2 instruction
+//    gives (x0 - r0) + (x1 - r1) = x0 + x1 - (r0 + r1), and another the
+//    difference; the reference pair sums are formed once for all loops.
+//  * Butterflies on the remaining in-lane index bits stay in registers; those
+//    on the lane bits go across lanes inside a quad (DPP).
+template <int D, int PER>
 __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
-  constexpr int kLanes = D / 32;      // lanes per vector
+  constexpr int kLanes = D / PER;  // lanes per vector
   constexpr int kVecPerBlock = 256 / kLanes;
-  const int g = threadIdx.x % kLanes;
+  constexpr int NGL = PER / 32;    // scale groups per lane
+  const int sub = threadIdx.x % kLanes;
   const int64_t stride = (int64_t)gridDim.x * kVecPerBlock;
   for (int64_t v = (int64_t)blockIdx.x * kVecPerBlock + threadIdx.x / kLanes; v < a.n_vec; v += stride) {
-    const int64_t base = v * D + g * 32;
-    float ref[32];
-    load_bf16x32(a.ref + base, ref);
-    for (int l = 0; l < a.n_loops; ++l) {
-      float y[32];
-      load_bf16x32(a.x[l] + base, y);
+    const int64_t base = v * D + sub * PER;
+    // negated reference pair sums and differences
+    float nrs[PER / 2], nrd[PER / 2];
+    {
+      const uint4* rp = reinterpret_cast<const uint4*>(a.ref + base);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) y[i] -= ref[i];
-      fwht_groups<D>(y, g);
-      if (a.bits[l] == 2) {
-        quantize_group_store<2, D>(y, a.codes[l], a.scales[l], v, g);
-      } else {
-        quantize_group_store<4, D>(y, a.codes[l], a.scales[l], v, g);
+      for (int i = 0; i < PER / 8; ++i) {
+        const uint4 u = rp[i];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float r0 = bf16_lo(w[j]), r1 = bf16_hi(w[j]);
+          nrs[4 * i + j] = -(r0 + r1);
+          nrd[4 * i + j] = r1 - r0;
+        }
       }
+    }
+    for (int l = 0; l < a.n_loops; ++l) {
+      float y[PER];
+      const uint4* xp = reinterpret_cast<const uint4*>(a.x[l] + base);
+#pragma unroll
+      for (int i = 0; i < PER / 8; ++i) {
+        const uint4 u = xp[i];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y[8 * i + 2 * j] = dot2_bf16(w[j], kPairSum, nrs[4 * i + j]);
+          y[8 * i + 2 * j + 1] = dot2_bf16(w[j], kPairDiff, nrd[4 * i + j]);
+        }
+      }
+#pragma unroll
+      for (int h = 2; h < PER; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          if ((i & h) == 0) {
+            const float p = y[i], q = y[i + h];
+            y[i] = p + q;
+            y[i + h] = p - q;
+          }
+        }
+      }
+      if constexpr (kLanes >= 2) {
+        const float sgn = (sub & 1) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) y[i] = fmaf(sgn, y[i], quad_xor<1>(y[i]));
+      }
+      if constexpr (kLanes >= 4) {
+        const float sgn = (sub & 2) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) y[i] = fmaf(sgn, y[i], quad_xor<2>(y[i]));
+      }
+      const int bits = a.bits[l];
+      uint16_t sc[NGL];
+      if (bits == 2) {
+        uint32_t wd[2 * NGL];
+#pragma unroll
+        for (int gi = 0; gi < NGL; ++gi) {
+          uint32_t w2[2];
+          sc[gi] = f32_to_f16_sat(quantize_group<2, D>(y + 32 * gi, w2));
+          wd[2 * gi] = w2[0];
+          wd[2 * gi + 1] = w2[1];
+        }
+        uint32_t* dst = a.codes[l] + v * (D / 16) + sub * 2 * NGL;
+        if constexpr (NGL == 2) *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        else *reinterpret_cast<uint2*>(dst) = make_uint2(wd[0], wd[1]);
+      } else {
+        uint32_t wd[4 * NGL];
+#pragma unroll
+        for (int gi = 0; gi < NGL; ++gi) {
+          uint32_t w4[4];
+          sc[gi] = f32_to_f16_sat(quantize_group<4, D>(y + 32 * gi, w4));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) wd[4 * gi + k] = w4[k];
+        }
+        uint4* dst = reinterpret_cast<uint4*>(a.codes[l] + v * (D / 8) + sub * 4 * NGL);
+#pragma unroll
+        for (int gi = 0; gi < NGL; ++gi) dst[gi] = make_uint4(wd[4 * gi], wd[4 * gi + 1], wd[4 * gi + 2], wd[4 * gi + 3]);
+      }
+      uint16_t* sdst = a.scales[l] + v * (D / 32) + sub * NGL;
+      if constexpr (NGL == 2) *reinterpret_cast<uint32_t*>(sdst) = (uint32_t)sc[0] | ((uint32_t)sc[1] << 16);
+      else *sdst = sc[0];
     }
   }
 }
@@ -154,11 +243,19 @@ static unsigned grid_for(int64_t n_vec, int vec_per_block) {
   return (unsigned)(blocks < 1 ? 1 : blocks);
 }
 
+// 32 coordinates (one scale group) per lane: measured on MI355X, 64 per lane
+// saves the second cross-lane butterfly but halves the occupancy (about 200
+// registers) and runs slower.
+constexpr int kEncodePer = 32;
+
 hipError_t launch_encode(const EncodeArgs& a, int head_dim, hipStream_t stream) {
+  constexpr int per = kEncodePer;
   if (head_dim == 128) {
-    hipLaunchKernelGGL(rq_encode_kernel<128>, dim3(grid_for(a.n_vec, 64)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((rq_encode_kernel<128, per>), dim3(grid_for(a.n_vec, 256 / (128 / per))), dim3(256), 0,
+                       stream, a);
   } else {
-    hipLaunchKernelGGL(rq_encode_kernel<64>, dim3(grid_for(a.n_vec, 128)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((rq_encode_kernel<64, per>), dim3(grid_for(a.n_vec, 256 / (64 / per))), dim3(256), 0,
+                       stream, a);
   }
   return hipGetLastError();
 }

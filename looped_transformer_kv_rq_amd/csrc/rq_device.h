@@ -47,7 +47,7 @@ template <int MASK>
 __device__ __forceinline__ float quad_xor(float v) {
   static_assert(MASK == 1 || MASK == 2, "quad_xor covers lane bits 0 and 1");
   constexpr int ctrl = MASK == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, true));
 }
 
 // Unnormalised in-register Walsh-Hadamard transform of 32 values (natural
