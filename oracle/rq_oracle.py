@@ -16,8 +16,7 @@ It is plain NumPy in float64 and follows the method's steps in order:
 * ResidualQuant (paperaft JSON page), `summary`: a looped model's cache is
   stored in this custom residual format and decoded at attention time.
 
-The pages give no equations, so the details below are readings. Each is listed
-in the design doc with its reason:
+The pages give no equations, so the details below are readings of them:
 
 * The rotation is the normalised Sylvester Walsh-Hadamard matrix H over
   head_dim. It is built densely here, not with butterflies. It is symmetric and
