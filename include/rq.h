@@ -65,7 +65,8 @@ typedef enum rq_status {
   RQ_EINVAL = -1,        /* null pointer, non-positive size, n_q_heads % n_kv_heads != 0,
                             n_loops outside [1, RQ_MAX_LOOPS], non-finite softmax scale */
   RQ_EUNSUPPORTED = -2,  /* head_dim not in {64, 128}, bits not in {0, 2, 4} (not 0 for
-                            rq_encode), query heads per kv head above 32, bad out_dtype */
+                            rq_encode), query heads per kv head above 32, bad out_dtype,
+                            decode with seq_len * head_dim * 2 above 2^31 - 1 bytes */
   RQ_EALIGN = -3,        /* a pointer is not 16-byte aligned */
   RQ_EWORKSPACE = -4,    /* workspace NULL or smaller than the size query returned */
   RQ_EHIP = -5           /* the HIP runtime reported an error at launch */

@@ -29,6 +29,8 @@ int check_heads(const rq_shape* s, int32_t n_q_heads, int32_t n_loops) {
   if (n_q_heads <= 0 || n_q_heads % s->n_kv_heads != 0) return RQ_EINVAL;
   if (n_loops < 1 || n_loops > kMaxLoops) return RQ_EINVAL;
   if (n_q_heads / s->n_kv_heads > 32) return RQ_EUNSUPPORTED;
+  // the decode addresses one (batch, kv head) row of the cache with 32-bit byte offsets
+  if ((int64_t)s->seq_len * 2 * s->head_dim > INT32_MAX) return RQ_EUNSUPPORTED;
   return RQ_OK;
 }
 

@@ -80,6 +80,23 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
 __device__ __forceinline__ void dma4(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 4, 0, 0);
 }
+// Buffer-resource forms for tiles that lie inside the sequence: the resource
+// (base = start of the (batch, kv head) row, set up in scalar registers) and
+// the tile offset are wave-uniform, the per-lane offset is a constant, so
+// issuing a tile costs no vector instructions.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 4, voff, soff, 0, 0);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // s_waitcnt vmcnt(0) / lgkmcnt(0) (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8])
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
@@ -189,7 +206,7 @@ __global__ __launch_bounds__(256) void rq_query_prep(QueryPrepArgs a) {
 // ---------------------------------------------------------------------------
 
 // Issue the DMA of one residual loop's tile data (codes and scales of K and V).
-template <int D, int BITS>
+template <int D, int BITS, bool FULL>
 __device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned char* base, int64_t row_base,
                                            int t0, int tlast, int lane) {
   constexpr int NG = D / 32;
@@ -198,6 +215,29 @@ __device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned
   unsigned char* ks_l = kc_l + 128 * W;
   unsigned char* vc_l = ks_l + 64 * NG;
   unsigned char* vs_l = vc_l + 128 * W;
+  if constexpr (FULL) {
+    // All 32 tokens lie inside the sequence: buffer loads with the row as the
+    // resource, the tile start as the scalar offset and per-lane constants.
+    const uint32_t S = (uint32_t)a.seq_len;
+    const auto kc_r = row_rsrc(a.kc[li] + row_base * W, S * 4u * W);
+    const auto vc_r = row_rsrc(a.vc[li] + row_base * W, S * 4u * W);
+    const auto ks_r = row_rsrc(a.ks[li] + row_base * NG, S * 2u * NG);
+    const auto vs_r = row_rsrc(a.vs[li] + row_base * NG, S * 2u * NG);
+    const uint32_t tc = (uint32_t)t0 * 4u * W, ts = (uint32_t)t0 * 2u * NG;
+    const uint32_t lane16 = 16u * (uint32_t)lane;
+#pragma unroll
+    for (int i = 0; i * 64 < 8 * W; ++i) {
+      if (8 * W >= 64 * (i + 1) || 64 * i + lane < 8 * W) bdma16(kc_r, lane16, tc + 1024 * i, kc_l + 1024 * i);
+    }
+    if (16 * NG >= 64 || lane < 16 * NG) {
+      bdma4(ks_r, 4u * (uint32_t)lane, ts, ks_l);
+      bdma4(vs_r, 4u * (uint32_t)lane, ts, vs_l);
+    }
+    const uint32_t vc_lane = (uint32_t)(lane & 31) * (4u * W) + 4u * (uint32_t)(lane >> 5);
+#pragma unroll
+    for (int i = 0; i < W / 2; ++i) bdma4(vc_r, vc_lane, tc + 8 * i, vc_l + 256 * i);
+    return;
+  }
   // K code words in 16-byte chunks: chunk c -> token c / (W/4), words 4 (c % (W/4))
 #pragma unroll
   for (int i = 0; i * 64 < 8 * W; ++i) {
@@ -391,7 +431,7 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
 
 // Issue every load of one tile: the residual loops' codes and scales and the
 // V reference tile by LDS DMA into `buf`, the K reference into registers.
-template <int D, bool RESID>
+template <int D, bool RESID, bool FULL>
 __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* buf, const uint16_t* kbase,
                                            const uint16_t* vbase, int64_t row_base, int t0, int tlast, int lane,
                                            int m, int g, uint4 (&ka)[2][D / 32]) {
@@ -401,10 +441,26 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* b
     int off = Gm::VT_BYTES;
     for (int li = 0; li < a.n_loops_launch; ++li) {
       const int bits = a.bits[li];
-      if (bits == 2) stage_loop<D, 2>(a, li, buf + off, row_base, t0, tlast, lane);
-      else if (bits == 4) stage_loop<D, 4>(a, li, buf + off, row_base, t0, tlast, lane);
+      if (bits == 2) stage_loop<D, 2, FULL>(a, li, buf + off, row_base, t0, tlast, lane);
+      else if (bits == 4) stage_loop<D, 4, FULL>(a, li, buf + off, row_base, t0, tlast, lane);
       off += loop_lds_bytes(D, bits);
     }
+  }
+  if constexpr (FULL) {
+    // the tile's 32 vectors are contiguous: 2D bytes each, one 16-byte chunk per lane
+    const uint32_t rb = (uint32_t)a.seq_len * 2u * D;
+    const auto v_r = row_rsrc(vbase, rb);
+    const auto k_r = row_rsrc(kbase, rb);
+    const uint32_t tb = (uint32_t)t0 * 2u * D;
+    const uint32_t lane16 = 16u * (uint32_t)lane;
+#pragma unroll
+    for (int i = 0; i < Gm::VT_INSTR; ++i) bdma16(v_r, lane16, tb + 1024 * i, buf + i * Gm::VT_STRIDE);
+    const uint32_t koff = 2u * (uint32_t)(m * D + 8 * g);
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) ka[bk][ks] = bload16(k_r, koff, tb + 32 * D * bk + 64 * ks);
+    return;
   }
 #pragma unroll
   for (int i = 0; i < Gm::VT_INSTR; ++i) {
@@ -548,7 +604,8 @@ void rq_decode_partial_mfma(DecodeArgs a) {
   constexpr int REC = 2 * D + 2;  // partial record: m, l, o_ref[D], o_res[D]
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: tile bases stay scalar
   const int m = lane & 15, g = lane >> 4;
   const int split = blockIdx.x % a.n_splits;
   const int bh = blockIdx.x / a.n_splits;
@@ -620,7 +677,8 @@ void rq_decode_partial_mfma(DecodeArgs a) {
 
   uint4 ka[2][NG];
   for (int t0 = t_begin + wave * kTile; t0 < t_end; t0 += kStep) {
-    issue_tile<D, RESID>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
+    if (t0 + kTile <= S) issue_tile<D, RESID, true>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
+    else issue_tile<D, RESID, false>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
     wait_vmem();
     wave_sync_lds();
     compute_tile<D, NB, RESID>(a, buf, t0, t_end, m, g, ka, qB, qtB, qoff, qmul, my_loop, o_ref, o_res, m_run, l_run);

@@ -52,6 +52,10 @@ def test_workspace_and_split_queries():
     assert rq.decode_workspace_bytes(1, 1, 1, 96, 1, 1) == 0       # unsupported head_dim
     assert rq.decode_workspace_bytes(1, 2, 1, 64, 3, 1) == 0       # Hq % Hkv != 0
     assert rq.decode_workspace_bytes(1, 1, 1, 64, 1, 9) == 0       # too many loops
+    # one (batch, kv head) row of bf16 K must stay below 2^31 bytes
+    assert rq.decode_workspace_bytes(1, 1, 2 ** 24 - 1, 64, 1, 1) > 0
+    assert rq.decode_workspace_bytes(1, 1, 2 ** 24, 64, 1, 1) == 0
+    assert rq.decode_workspace_bytes(1, 1, 2 ** 23, 128, 1, 1) == 0
 
 
 def _shape(b=1, h=1, s=4, d=64):
