@@ -262,23 +262,48 @@ __device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned
   }
 }
 
-// Residual scores of loop li added to this lane's score fragment.
+// Constants kept in vector registers, so that mask-and-insert steps compile to
+// one v_and_or_b32 (a gfx9 VOP3 instruction takes no literal operand).
+struct Consts {
+  uint32_t m2;    // 0x03000300: INT2 field at bits 8-9 of each half
+  uint32_t m4;    // 0x03C003C0: INT4 field at bits 6-9 of each half
+  uint32_t one;   // 0x3C003C00: fp16 1.0 in both halves
+  uint32_t sel0;  // 0x000C000C: v_perm "zero byte" in bytes 0 and 2
+};
+__device__ __forceinline__ Consts make_consts() {
+  Consts c{0x03000300u, 0x03C003C0u, 0x3C003C00u, 0x000C000Cu};
+  asm volatile("" : "+v"(c.m2), "+v"(c.m4), "+v"(c.one), "+v"(c.sel0));
+  return c;
+}
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) { return (x & m) | o; }
+
+// Residual scores of loop li added to this lane's score fragment. Rows of
+// other loops get zero factors (qm = qo = 0), so every lane runs the same code.
 template <int D, int NB, int BITS>
 __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, const unsigned char* base,
                                                 const uint4 (&qtB)[NB][D / 32], const float (&qoff)[NB][D / 32],
                                                 const float (&qmul)[NB], const int (&my_loop)[NB],
-                                                f32x4_t (&sc)[2][NB], int m, int g) {
+                                                f32x4_t (&sc)[2][NB], int m, int g, const Consts& k) {
   constexpr int NG = D / 32;
   constexpr int W = D * BITS / 32;
   const unsigned char* kc_l = base;
   const unsigned char* ks_l = kc_l + 128 * W;
   const int G = a.group;
+  float qm[NB], qo[NB][NG];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const bool mine = my_loop[nb] == li;
+    qm[nb] = mine ? qmul[nb] : 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < NG; ++ks) qo[nb][ks] = mine ? qoff[nb][ks] : 0.0f;
+  }
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk) {
     // code words of token 16bk + m (this lane's A-operand row)
     const unsigned char* cw = kc_l + (16 * bk + m) * W * 4;
     uint4 kx[NG];
     if constexpr (BITS == 2) {
+      // element 2i <- field 4(g&1) + i of word 2ks + (g>>1), element 2i+1 <- the field 8 later
       uint32_t wsel[NG];
       const bool hi = (g >> 1) != 0;
       const uint4 w0 = *reinterpret_cast<const uint4*>(cw);
@@ -293,24 +318,26 @@ __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, con
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
         const uint32_t w = wsel[ks] << pre;
-        kx[ks].x = (w & 0x03000300u) | 0x3C003C00u;
-        kx[ks].y = ((w >> 2) & 0x03000300u) | 0x3C003C00u;
-        kx[ks].z = ((w >> 4) & 0x03000300u) | 0x3C003C00u;
-        kx[ks].w = ((w >> 6) & 0x03000300u) | 0x3C003C00u;
+        kx[ks].x = and_or(w, k.m2, k.one);
+        kx[ks].y = and_or(w >> 2, k.m2, k.one);
+        kx[ks].z = and_or(w >> 4, k.m2, k.one);
+        kx[ks].w = and_or(w >> 6, k.m2, k.one);
       }
     } else {
-      const uint32_t f4 = 16u * (uint32_t)(g & 1);
+      // element 2i <- nibble 4(g&1) + i of word 4ks + 2(g>>1), element 2i+1 <- same nibble of
+      // the next word. One v_perm puts the byte holding nibbles (i, i+1) of both words at
+      // bytes 1 and 3; a shift then aligns either nibble at bits 6-9 of each half.
+      const uint32_t b0 = 2u * (uint32_t)(g & 1);
+      const uint32_t selA = ((b0) << 8) | ((4u + b0) << 24);
+      const uint32_t selB = ((b0 + 1u) << 8) | ((5u + b0) << 24);
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
         const uint2 w = *reinterpret_cast<const uint2*>(cw + (4 * ks + 2 * (g >> 1)) * 4);
-        uint32_t e[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t c0 = __builtin_amdgcn_ubfe(w.x, f4 + 4 * i, 4);
-          const uint32_t c1 = __builtin_amdgcn_ubfe(w.y, f4 + 4 * i, 4);
-          e[i] = (c1 << 22) | (c0 << 6) | 0x3C003C00u;
-        }
-        kx[ks] = make_uint4(e[0], e[1], e[2], e[3]);
+        const uint32_t tA = vperm(w.y, w.x, selA), tB = vperm(w.y, w.x, selB);
+        kx[ks].x = and_or(tA >> 2, k.m4, k.one);
+        kx[ks].y = and_or(tA >> 6, k.m4, k.one);
+        kx[ks].z = and_or(tB >> 2, k.m4, k.one);
+        kx[ks].w = and_or(tB >> 6, k.m4, k.one);
       }
     }
     // k scales of this lane's four C-layout tokens 16bk + 4g + i
@@ -328,19 +355,14 @@ __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, con
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if (li * G >= 16 * nb + 16 || li * G + G <= 16 * nb) continue;  // no row of loop li here
-      f32x4_t r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
         const f32x4_t c = mma_f16(kx[ks], qtB[nb][ks], f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float s = (ks & 1) ? half_hi(sw[i][ks >> 1]) : half_lo(sw[i][ks >> 1]);
-          r[i] = fmaf(s, fmaf(c[i], qmul[nb], qoff[nb][ks]), r[i]);
+          sc[bk][nb][i] = fmaf(s, fmaf(c[i], qm[nb], qo[nb][ks]), sc[bk][nb][i]);
         }
-      }
-      if (my_loop[nb] == li) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[bk][nb][i] += r[i];
       }
     }
   }
@@ -350,7 +372,7 @@ __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, con
 template <int D, int NB, int BITS>
 __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const unsigned char* base,
                                             const float (&p)[NB][8], const int (&my_loop)[NB],
-                                            f32x4_t (&o_res)[NB][2 * (D / 32)], int m, int g) {
+                                            f32x4_t (&o_res)[NB][2 * (D / 32)], int m, int g, const Consts& k) {
   constexpr int NG = D / 32;
   constexpr int W = D * BITS / 32;
   const unsigned char* vc_l = base + 128 * W + 64 * NG;
@@ -374,6 +396,19 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
       vsw[4 * h2 + 2][0] = u0.z; vsw[4 * h2 + 3][0] = u0.w;
     }
   }
+  // A rows: coordinate 32grp + 16hf + m. Its code sits in byte `cb` of word
+  // wv (INT2: byte m/4 of word 2grp + hf; INT4: byte (m%8)/2 of word
+  // 4grp + 2hf + m/8), `sh` bits up.
+  uint32_t selx;
+  uint32_t sh;
+  if constexpr (BITS == 2) {
+    selx = ((uint32_t)(m >> 2) << 8) | ((uint32_t)(4 + (m >> 2)) << 24);
+    sh = 2u * (uint32_t)(m & 3);
+  } else {
+    const int f = m & 7;
+    selx = ((uint32_t)(f >> 1) << 8) | ((uint32_t)(4 + (f >> 1)) << 24);
+    sh = 4u * (uint32_t)(f & 1);
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     if (li * G >= 16 * nb + 16 || li * G + G <= 16 * nb) continue;
@@ -391,37 +426,26 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
       bop.w = mul_f16x2(p16[3], vperm(vsw[7][grp >> 1], vsw[6][grp >> 1], hsel));
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        // A rows: coordinate 32grp + 16hf + m; its code sits in word wv, field f
-        int wv, sh;
-        uint32_t selx;
-        if constexpr (BITS == 2) {
-          wv = 2 * grp + hf;
-          selx = ((uint32_t)(m >> 2) << 8) | ((uint32_t)(4 + (m >> 2)) << 24);
-          sh = 2 * (m & 3);
-        } else {
-          wv = 4 * grp + 2 * hf + (m >> 3);
-          const int f = m & 7;
-          selx = ((uint32_t)(f >> 1) << 8) | ((uint32_t)(4 + (f >> 1)) << 24);
-          sh = 4 * (f & 1);
-        }
+        const int wv = BITS == 2 ? 2 * grp + hf : 4 * grp + 2 * hf + (m >> 3);
         const uint4 wa = *reinterpret_cast<const uint4*>(vc_l + (wv * 32 + 4 * g) * 4);
         const uint4 wb = *reinterpret_cast<const uint4*>(vc_l + (wv * 32 + 16 + 4 * g) * 4);
+        // bytes 1 and 3 of y = the code bytes of two tokens, code at bits 8.. and 24..
         const uint32_t y0 = vperm(wa.y, wa.x, selx) >> sh;
         const uint32_t y1 = vperm(wa.w, wa.z, selx) >> sh;
         const uint32_t y2 = vperm(wb.y, wb.x, selx) >> sh;
         const uint32_t y3 = vperm(wb.w, wb.z, selx) >> sh;
         uint4 alo;
-        alo.x = vperm(0u, kLutInt2, (y0 & 0x03000300u) | 0x000C000Cu);
-        alo.y = vperm(0u, kLutInt2, (y1 & 0x03000300u) | 0x000C000Cu);
-        alo.z = vperm(0u, kLutInt2, (y2 & 0x03000300u) | 0x000C000Cu);
-        alo.w = vperm(0u, kLutInt2, (y3 & 0x03000300u) | 0x000C000Cu);
+        alo.x = vperm(0u, kLutInt2, and_or(y0, k.m2, k.sel0));
+        alo.y = vperm(0u, kLutInt2, and_or(y1, k.m2, k.sel0));
+        alo.z = vperm(0u, kLutInt2, and_or(y2, k.m2, k.sel0));
+        alo.w = vperm(0u, kLutInt2, and_or(y3, k.m2, k.sel0));
         o_res[nb][2 * grp + hf] = mma_f16(alo, bop, o_res[nb][2 * grp + hf]);
         if constexpr (BITS == 4) {
           uint4 ahi;
-          ahi.x = vperm(0u, kLutInt4Hi, ((y0 >> 2) & 0x03000300u) | 0x000C000Cu);
-          ahi.y = vperm(0u, kLutInt4Hi, ((y1 >> 2) & 0x03000300u) | 0x000C000Cu);
-          ahi.z = vperm(0u, kLutInt4Hi, ((y2 >> 2) & 0x03000300u) | 0x000C000Cu);
-          ahi.w = vperm(0u, kLutInt4Hi, ((y3 >> 2) & 0x03000300u) | 0x000C000Cu);
+          ahi.x = vperm(0u, kLutInt4Hi, and_or(y0 >> 2, k.m2, k.sel0));
+          ahi.y = vperm(0u, kLutInt4Hi, and_or(y1 >> 2, k.m2, k.sel0));
+          ahi.z = vperm(0u, kLutInt4Hi, and_or(y2 >> 2, k.m2, k.sel0));
+          ahi.w = vperm(0u, kLutInt4Hi, and_or(y3 >> 2, k.m2, k.sel0));
           o_res[nb][2 * grp + hf] = mma_f16(ahi, bop, o_res[nb][2 * grp + hf]);
         }
       }
@@ -482,7 +506,7 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
                                              const uint4 (&qtB)[NB][D / 32], const float (&qoff)[NB][D / 32],
                                              const float (&qmul)[NB], const int (&my_loop)[NB],
                                              f32x4_t (&o_ref)[NB][D / 64][4], f32x4_t (&o_res)[NB][2 * (D / 32)],
-                                             float (&m_run)[NB], float (&l_run)[NB]) {
+                                             float (&m_run)[NB], float (&l_run)[NB], const Consts& k) {
   using Gm = MfmaGeom<D>;
   constexpr int NG = Gm::NG, NH = Gm::NH;
   // ---- scores S^T[token][row]: lane holds tokens t0 + 16bk + 4g + i of row 16nb + m
@@ -500,8 +524,8 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
     int off = Gm::VT_BYTES;
     for (int li = 0; li < a.n_loops_launch; ++li) {
       const int bits = a.bits[li];
-      if (bits == 2) residual_scores<D, NB, 2>(a, li, buf + off, qtB, qoff, qmul, my_loop, sc, m, g);
-      else if (bits == 4) residual_scores<D, NB, 4>(a, li, buf + off, qtB, qoff, qmul, my_loop, sc, m, g);
+      if (bits == 2) residual_scores<D, NB, 2>(a, li, buf + off, qtB, qoff, qmul, my_loop, sc, m, g, k);
+      else if (bits == 4) residual_scores<D, NB, 4>(a, li, buf + off, qtB, qoff, qmul, my_loop, sc, m, g, k);
       off += loop_lds_bytes(D, bits);
     }
   }
@@ -587,8 +611,8 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
     int off = Gm::VT_BYTES;
     for (int li = 0; li < a.n_loops_launch; ++li) {
       const int bits = a.bits[li];
-      if (bits == 2) residual_pv<D, NB, 2>(a, li, buf + off, p, my_loop, o_res, m, g);
-      else if (bits == 4) residual_pv<D, NB, 4>(a, li, buf + off, p, my_loop, o_res, m, g);
+      if (bits == 2) residual_pv<D, NB, 2>(a, li, buf + off, p, my_loop, o_res, m, g, k);
+      else if (bits == 4) residual_pv<D, NB, 4>(a, li, buf + off, p, my_loop, o_res, m, g, k);
       off += loop_lds_bytes(D, bits);
     }
   }
@@ -675,13 +699,15 @@ void rq_decode_partial_mfma(DecodeArgs a) {
   const uint16_t* vbase = a.v[z] + row_base * D;
   constexpr int kStep = 4 * kTile;  // tokens between a wave's consecutive tiles
 
+  const Consts kc = make_consts();
   uint4 ka[2][NG];
   for (int t0 = t_begin + wave * kTile; t0 < t_end; t0 += kStep) {
     if (t0 + kTile <= S) issue_tile<D, RESID, true>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
     else issue_tile<D, RESID, false>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
     wait_vmem();
     wave_sync_lds();
-    compute_tile<D, NB, RESID>(a, buf, t0, t_end, m, g, ka, qB, qtB, qoff, qmul, my_loop, o_ref, o_res, m_run, l_run);
+    compute_tile<D, NB, RESID>(a, buf, t0, t_end, m, g, ka, qB, qtB, qoff, qmul, my_loop, o_ref, o_res, m_run, l_run,
+                               kc);
     wait_lds();
     wave_sync_lds();  // the buffer is free for the next tile's DMA
   }
