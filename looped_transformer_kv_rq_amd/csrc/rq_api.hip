@@ -219,18 +219,27 @@ int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, co
     a.qprep = prep;
     a.k[0] = k_ref;
     a.v[0] = v_ref;
-    a.loop_base = base;
     a.n_loops_launch = nl;
     a.n_rows = nl * G;
     bool residual = false;
-    for (int li = 0; li < nl; ++li) {
-      const rq_loop_view& lv = loops[base + li];
-      a.bits[li] = lv.bits;
-      a.kc[li] = lv.k_codes;
-      a.ks[li] = lv.k_scales;
-      a.vc[li] = lv.v_codes;
-      a.vs[li] = lv.v_scales;
-      residual = residual || lv.bits != 0;
+    // slots in the order INT4, INT2, reference-only: the kernel runs one
+    // branch-free loop per width
+    int li = 0;
+    for (const int want : {4, 2, 0}) {
+      for (int j = 0; j < nl; ++j) {
+        const rq_loop_view& lv = loops[base + j];
+        if (lv.bits != want) continue;
+        a.loop_id[li] = base + j;
+        a.bits[li] = lv.bits;
+        a.kc[li] = lv.k_codes;
+        a.ks[li] = lv.k_scales;
+        a.vc[li] = lv.v_codes;
+        a.vs[li] = lv.v_scales;
+        if (want == 4) ++a.n4;
+        if (want == 2) ++a.n2;
+        residual = residual || lv.bits != 0;
+        ++li;
+      }
     }
     a.zero_residual = any_residual && !residual;
     st = hip_status(launch_decode_partial(a, shape->head_dim, 1, residual, s));
@@ -269,7 +278,7 @@ int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loop
     a.k[i] = k[i];
     a.v[i] = v[i];
   }
-  a.loop_base = 0;
+  a.loop_id[0] = 0;  // blockIdx.y selects the loop
   a.n_loops_launch = 1;
   a.n_rows = G;
   st = hip_status(launch_decode_partial(a, shape->head_dim, n_loops, false, s));

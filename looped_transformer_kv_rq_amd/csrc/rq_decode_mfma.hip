@@ -132,6 +132,14 @@ __host__ __device__ constexpr int loop_lds_bytes(int d, int bits) {
   return bits == 0 ? 0 : 256 * (d * bits / 32) + 128 * (d / 32);
 }
 
+// LDS offset of residual slot li's tile data inside a wave's buffer: the V
+// tile, then the INT4 slots, then the INT2 slots.
+template <int D>
+__device__ __forceinline__ int slot_lds_offset(const DecodeArgs& a, int li) {
+  constexpr int L4 = loop_lds_bytes(D, 4), L2 = loop_lds_bytes(D, 2);
+  return MfmaGeom<D>::VT_BYTES + (li < a.n4 ? li * L4 : a.n4 * L4 + (li - a.n4) * L2);
+}
+
 // ---------------------------------------------------------------------------
 // query prep: rotated query in residual-score B-operand order + offsets
 // ---------------------------------------------------------------------------
@@ -462,13 +470,11 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* b
   using Gm = MfmaGeom<D>;
   constexpr int NG = Gm::NG;
   if constexpr (RESID) {
-    int off = Gm::VT_BYTES;
-    for (int li = 0; li < a.n_loops_launch; ++li) {
-      const int bits = a.bits[li];
-      if (bits == 2) stage_loop<D, 2, FULL>(a, li, buf + off, row_base, t0, tlast, lane);
-      else if (bits == 4) stage_loop<D, 4, FULL>(a, li, buf + off, row_base, t0, tlast, lane);
-      off += loop_lds_bytes(D, bits);
-    }
+    // INT4 slots first, then INT2 (the launcher orders them): no branch per loop
+    for (int li = 0; li < a.n4; ++li)
+      stage_loop<D, 4, FULL>(a, li, buf + slot_lds_offset<D>(a, li), row_base, t0, tlast, lane);
+    for (int li = a.n4; li < a.n4 + a.n2; ++li)
+      stage_loop<D, 2, FULL>(a, li, buf + slot_lds_offset<D>(a, li), row_base, t0, tlast, lane);
   }
   if constexpr (FULL) {
     // the tile's 32 vectors are contiguous: 2D bytes each, one 16-byte chunk per lane
@@ -521,13 +527,10 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
       sc[bk][nb] = acc;
     }
   if constexpr (RESID) {
-    int off = Gm::VT_BYTES;
-    for (int li = 0; li < a.n_loops_launch; ++li) {
-      const int bits = a.bits[li];
-      if (bits == 2) residual_scores<D, NB, 2>(a, li, buf + off, qtB, qoff, qmul, my_loop, sc, m, g, k);
-      else if (bits == 4) residual_scores<D, NB, 4>(a, li, buf + off, qtB, qoff, qmul, my_loop, sc, m, g, k);
-      off += loop_lds_bytes(D, bits);
-    }
+    for (int li = 0; li < a.n4; ++li)
+      residual_scores<D, NB, 4>(a, li, buf + slot_lds_offset<D>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+    for (int li = a.n4; li < a.n4 + a.n2; ++li)
+      residual_scores<D, NB, 2>(a, li, buf + slot_lds_offset<D>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
   }
 
   // ---- online softmax (log2 domain); row statistics live in the row's 4 lanes
@@ -608,13 +611,10 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
 
   // ---- residual PV
   if constexpr (RESID) {
-    int off = Gm::VT_BYTES;
-    for (int li = 0; li < a.n_loops_launch; ++li) {
-      const int bits = a.bits[li];
-      if (bits == 2) residual_pv<D, NB, 2>(a, li, buf + off, p, my_loop, o_res, m, g, k);
-      else if (bits == 4) residual_pv<D, NB, 4>(a, li, buf + off, p, my_loop, o_res, m, g, k);
-      off += loop_lds_bytes(D, bits);
-    }
+    for (int li = 0; li < a.n4; ++li)
+      residual_pv<D, NB, 4>(a, li, buf + slot_lds_offset<D>(a, li), p, my_loop, o_res, m, g, k);
+    for (int li = a.n4; li < a.n4 + a.n2; ++li)
+      residual_pv<D, NB, 2>(a, li, buf + slot_lds_offset<D>(a, li), p, my_loop, o_res, m, g, k);
   }
 }
 
@@ -653,7 +653,7 @@ void rq_decode_partial_mfma(DecodeArgs a) {
     const int lb = my_loop[nb] >= 0 ? a.bits[my_loop[nb]] : 0;
     qmul[nb] = lb == 4 ? 16.0f : 4.0f;
     int64_t qrow = -1;
-    if (row < R) qrow = ((int64_t)(a.loop_base + row / G + z) * a.batch + b) * a.n_q_heads + kvh * G + row % G;
+    if (row < R) qrow = ((int64_t)(a.loop_id[row / G] + z) * a.batch + b) * a.n_q_heads + kvh * G + row % G;
 #pragma unroll
     for (int ks = 0; ks < NG; ++ks) {
       qB[nb][ks] = qrow >= 0 ? *reinterpret_cast<const uint4*>(a.q + qrow * D + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
@@ -765,7 +765,7 @@ void rq_decode_partial_mfma(DecodeArgs a) {
     for (int i = threadIdx.x; i < R * SREC; i += 256) {
       const int r = i / SREC, e = i % SREC;
       if (pass == 1 && e >= D) continue;
-      const int loop = a.loop_base + r / G + z;
+      const int loop = a.loop_id[r / G] + z;
       const int hq = kvh * G + r % G;
       float* dst = a.ws + ((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.n_splits + split) * REC + e0;
       const float* s0 = slots + r * SREC + (pass == 0 ? e : 2 + e);
@@ -787,7 +787,7 @@ void rq_decode_partial_mfma(DecodeArgs a) {
     if (a.zero_residual) {
       for (int i = threadIdx.x; i < R * D; i += 256) {
         const int r = i / D, e = i % D;
-        const int loop = a.loop_base + r / G + z;
+        const int loop = a.loop_id[r / G] + z;
         const int hq = kvh * G + r % G;
         a.ws[((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.n_splits + split) * REC + D + 2 + e] = 0.0f;
       }
