@@ -69,6 +69,9 @@ __device__ __forceinline__ uint32_t pack_rtz(float lo, float hi) {
 __device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) * __builtin_bit_cast(f16x2_t, b));
 }
+// 2^x by v_exp_f32 alone (no denormal-range fix-up): softmax weights below
+// 2^-126 of the running maximum count as zero. 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float half_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
 __device__ __forceinline__ float half_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
 
@@ -109,6 +112,7 @@ __device__ __forceinline__ void wave_sync_lds() {
 constexpr uint32_t kLutInt2 = 0x3E38B8BEu;    // fp16 high bytes of -1.5, -0.5, 0.5, 1.5
 constexpr uint32_t kLutInt4Hi = 0x4640C0C6u;  // fp16 high bytes of -6, -2, 2, 6 (4 * INT2 level)
 constexpr int kTile = 32;
+constexpr int kTile16 = 16;  // tokens per MFMA row block
 
 template <int D>
 struct MfmaGeom {
@@ -363,13 +367,16 @@ __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, con
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if (li * G >= 16 * nb + 16 || li * G + G <= 16 * nb) continue;  // no row of loop li here
+      // all group products first, so the MFMAs issue back to back
+      f32x4_t c[NG];
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) c[ks] = mma_f16(kx[ks], qtB[nb][ks], f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
-        const f32x4_t c = mma_f16(kx[ks], qtB[nb][ks], f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float s = (ks & 1) ? half_hi(sw[i][ks >> 1]) : half_lo(sw[i][ks >> 1]);
-          sc[bk][nb][i] = fmaf(s, fmaf(c[i], qm[nb], qo[nb][ks]), sc[bk][nb][i]);
+          sc[bk][nb][i] = fmaf(s, fmaf(c[ks][i], qm[nb], qo[nb][ks]), sc[bk][nb][i]);
         }
       }
     }
@@ -538,22 +545,25 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     float zz[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zz[j] = sc[j >> 2][nb][j & 3] * a.scale_log2;
+    if (t0 + 2 * kTile16 > t_end) {  // tail tile: tokens past the split end take no weight
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (t0 + 16 * (j >> 2) + 4 * g + (j & 3) >= t_end) zz[j] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
-      zz[j] = t < t_end ? sc[j >> 2][nb][j & 3] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, zz[j]);
-    }
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, zz[j]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run[nb], mx);
-    const float alpha = exp2f(m_run[nb] - m_new);
+    const float alpha = fast_exp2(m_run[nb] - m_new);
     m_run[nb] = m_new;
     float ls = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      p[nb][j] = exp2f(zz[j] - m_new);
+      p[nb][j] = fast_exp2(zz[j] - m_new);
       ls += p[nb][j];
     }
     l_run[nb] = fmaf(l_run[nb], alpha, ls);
