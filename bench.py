@@ -16,7 +16,10 @@ measured kernel):
   8 TB/s HBM peak;
 * the bf16-KV baseline decode (rq_decode_attn_bf16) over the same loops;
 * one call per loop (per-loop mode);
-* rq_reconstruct of one loop.
+* rq_reconstruct of one loop;
+* the rotation-only baseline (rq_encode_rotonly of every loop of K with no
+  reference): its encode rate, and its per-loop reconstruction error and
+  cache bytes beside those of the residual codec.
 
 `roofline` covers the kernel that takes the largest share of the step (the
 encoder). Its achieved rate is algorithmic bytes per launch divided by the
@@ -84,6 +87,19 @@ def decode_bytes(w, bits_per_loop):
 def bf16_decode_bytes(w, n_loops):
     th = w.batch * w.n_kv_heads * w.seq_len
     return n_loops * th * 4 * w.head_dim + n_loops * w.batch * w.n_q_heads * w.head_dim * (2 + 4)
+
+
+def rotonly_encode_bytes(w, bits):
+    """One rq_encode_rotonly launch: per state x, codes, scales (no reference)."""
+    n = w.batch * w.n_kv_heads * w.seq_len * w.head_dim
+    return n * sum(2 + b / 8 + 2 / 32 for b in bits)
+
+
+def cache_bytes_per_token_head(w, bits_per_loop, with_reference):
+    """K and V bytes one cached position of one KV head takes across all loops."""
+    d = w.head_dim
+    per = sum(d * b / 8 + 2 * d / 32 for b in bits_per_loop if b)
+    return 2 * ((2 * d if with_reference else 0) + per)
 
 
 def reconstruct_bytes(w, bits):
@@ -393,6 +409,41 @@ def main():
                                    "vs_bf16_all_loop": bf_ms / per_loop_total}
         result["reconstruct"] = {"loop": res_loops[0], "bits": bits[0], "ms": rc_ms,
                                  "GBps": reconstruct_bytes(w, bits[0]) / (rc_ms * 1e-3) / 1e9}
+
+        # Rotation-only baseline (no reference: every loop, the final one
+        # included, quantized directly after the rotation) at the same widths,
+        # the final loop at the table's INT2. K tensor; errors |x_hat - x| / |x|
+        # per loop, from the GPU reconstructions.
+        ro_bits = [b if b else 2 for b in w.bits]
+        ro = {}
+
+        def enc_ro():
+            ro["out"] = rq.encode_rotonly(kx, ro_bits, stream=stream)
+
+        ro_ms = timed(enc_ro, max(5, args.reps // 2))
+        ro_codes, ro_scales = ro["out"]
+        err_rq, err_ro = [], []
+        for l in range(w.n_loops):
+            xl = kx[l].float()
+            nx = torch.linalg.vector_norm(xl).item()
+            xr = rq.reconstruct_rotonly(ro_codes[l], ro_scales[l], ro_bits[l], stream=stream)
+            err_ro.append(torch.linalg.vector_norm(xr - xl).item() / nx)
+            if w.bits[l]:
+                i = res_loops.index(l)
+                xq = rq.reconstruct(kref, kc[i], ks[i], w.bits[l], stream=stream)
+                err_rq.append(torch.linalg.vector_norm(xq - xl).item() / nx)
+            else:
+                err_rq.append(0.0)
+            del xl, xr
+        ro_b = rotonly_encode_bytes(w, ro_bits)
+        result["rotation_only_baseline"] = {
+            "bits": ro_bits, "encode_ms": ro_ms, "encode_GBps": ro_b / (ro_ms * 1e-3) / 1e9,
+            "encode_frac_peak": ro_b / (ro_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "rel_error_per_loop": err_ro, "rq_rel_error_per_loop": err_rq,
+            "bytes_per_token_head": cache_bytes_per_token_head(w, ro_bits, False),
+            "rq_bytes_per_token_head": cache_bytes_per_token_head(w, list(w.bits), True),
+            "bf16_bytes_per_token_head": 2 * 2 * w.head_dim * w.n_loops,
+        }
     if cpu is not None:
         result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)

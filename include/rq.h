@@ -14,6 +14,8 @@
  *   rq_decode_attn     fused reconstruct + single-query decode attention
  *   rq_decode_attn_bf16  the same decode attention over plain bf16 K/V per
  *                        loop (the uncompressed baseline)
+ *   rq_encode_rotonly / rq_reconstruct_rotonly  the rotation-only baseline:
+ *                        the same codec without a reference
  *
  * FORMAT (RQ_FORMAT_VERSION 1)
  *   Dense tensors are [batch][n_kv_heads][seq_len][head_dim], head_dim
@@ -112,6 +114,25 @@ int rq_encode(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, 
  *   RQ_OUT_BF16 writes bf16 bits rounded to nearest even. */
 int rq_reconstruct(const rq_shape* shape, int32_t bits, const uint16_t* ref, const uint32_t* codes,
                    const uint16_t* scales, int32_t out_dtype, void* out, void* stream);
+
+/* Rotation-only baseline: the same codec with a zero reference. Each of
+ * n_states states (every loop, the final one included) is rotated and
+ * quantized directly, with no bf16 reference kept. This is the comparison
+ * point the ResidualQuant page names (newx.sg page, Abstract: the residuals
+ * are set against a rotation-based baseline at the same bit widths).
+ *   x[i]      bf16 [B][Hkv][S][D] (host array of n_states device pointers)
+ *   bits[i]   2 or 4 (host array)
+ *   codes[i], scales[i]  out, as in rq_encode
+ * Codes and scales are those rq_encode gives for the same states against an
+ * all-zero reference. Errors as rq_encode. */
+int rq_encode_rotonly(const rq_shape* shape, int32_t n_states, const uint16_t* const* x, const int32_t* bits,
+                      uint32_t* const* codes, uint16_t* const* scales, void* stream);
+
+/* Materialise one rotation-only state: out = H (s * q), the output of
+ * rq_reconstruct with an all-zero reference. bits must be 2 or 4
+ * (RQ_EUNSUPPORTED otherwise); output types as rq_reconstruct. */
+int rq_reconstruct_rotonly(const rq_shape* shape, int32_t bits, const uint32_t* codes, const uint16_t* scales,
+                           int32_t out_dtype, void* out, void* stream);
 
 /* Split count rq_decode_attn / rq_decode_attn_bf16 will use for a request of
  * n_splits (0 = automatic). Host only. Returns <= 0 on invalid arguments. */

@@ -18,6 +18,7 @@ import torch
 
 __all__ = [
     "LoopView", "RQError", "encode", "encode_into", "reconstruct", "decode_attn", "decode_attn_bf16",
+    "encode_rotonly", "reconstruct_rotonly",
     "decode_workspace_bytes", "decode_splits", "format_version", "library_path",
     "RQ_OK", "RQ_EINVAL", "RQ_EUNSUPPORTED", "RQ_EALIGN", "RQ_EWORKSPACE", "RQ_EHIP", "MAX_LOOPS",
 ]
@@ -73,6 +74,8 @@ def _load():
     sig = {
         "rq_encode": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, ctypes.POINTER(I32), P, PP, PP, P]),
         "rq_reconstruct": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, P, P, P, I32, P, P]),
+        "rq_encode_rotonly": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, ctypes.POINTER(I32), PP, PP, P]),
+        "rq_reconstruct_rotonly": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, P, P, I32, P, P]),
         "rq_decode_attn_splits": (I32, [ctypes.POINTER(_Shape), I32, I32, I32]),
         "rq_decode_attn_workspace": (SZ, [ctypes.POINTER(_Shape), I32, I32, I32]),
         "rq_decode_attn": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, P, P, ctypes.POINTER(_LoopView),
@@ -175,6 +178,55 @@ def encode(xs: Sequence[torch.Tensor], ref: torch.Tensor, bits: Sequence[int], s
     scales = [torch.empty((b, h, s, d // GROUP), dtype=torch.float16, device=ref.device) for _ in bits]
     encode_into(xs, ref, bits, codes, scales, stream)
     return codes, scales
+
+
+def encode_rotonly(xs: Sequence[torch.Tensor], bits: Sequence[int], stream=None):
+    """Rotation-only baseline: quantize each state xs[i] (bf16 [B,Hkv,S,D]) directly
+    after the rotation, with no reference. Returns (codes, scales) as encode()."""
+    lib = _load()
+    if len(xs) == 0 or len(xs) != len(bits):
+        raise ValueError("xs and bits must have one entry per state")
+    x0 = xs[0]
+    shp = _shape_of(x0)
+    b, h, s, d = x0.shape
+    for x in bits:
+        if int(x) not in (2, 4):
+            raise ValueError("bit widths must be 2 or 4")
+    codes = [torch.empty((b, h, s, d * int(x) // 32), dtype=torch.int32, device=x0.device) for x in bits]
+    scales = [torch.empty((b, h, s, d // GROUP), dtype=torch.float16, device=x0.device) for _ in bits]
+    for i, x in enumerate(xs):
+        _need(x, f"xs[{i}]", torch.bfloat16, x0.shape, x0.device)
+    n = len(xs)
+    bits_arr = (ctypes.c_int32 * n)(*[int(x) for x in bits])
+    st = lib.rq_encode_rotonly(ctypes.byref(shp), n, _ptr_array(xs), bits_arr, _ptr_array(codes),
+                               _ptr_array(scales), _stream(x0.device, stream))
+    _check(st, "rq_encode_rotonly")
+    return codes, scales
+
+
+def reconstruct_rotonly(codes: torch.Tensor, scales: torch.Tensor, bits: int, out_dtype: torch.dtype = torch.float32,
+                        out: Optional[torch.Tensor] = None, stream=None):
+    """Rotation-only state: out = H (s * q)."""
+    lib = _load()
+    if bits not in (2, 4):
+        raise ValueError("bits must be 2 or 4")
+    if codes.dim() != 4:
+        raise ValueError("codes must be [batch, n_kv_heads, seq_len, head_dim*bits/32]")
+    b, h, s, w = codes.shape
+    d = w * 32 // bits
+    shp = _Shape(b, h, s, d)
+    _need(codes, "codes", torch.int32, (b, h, s, w))
+    _need(scales, "scales", torch.float16, (b, h, s, d // GROUP), codes.device)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((b, h, s, d), dtype=out_dtype, device=codes.device)
+    _need(out, "out", out_dtype, (b, h, s, d), codes.device)
+    kind = RQ_OUT_F32 if out_dtype == torch.float32 else RQ_OUT_BF16
+    st = lib.rq_reconstruct_rotonly(ctypes.byref(shp), int(bits), _ptr(codes), _ptr(scales), kind, _ptr(out),
+                                    _stream(codes.device, stream))
+    _check(st, "rq_reconstruct_rotonly")
+    return out
 
 
 def reconstruct(ref: torch.Tensor, codes: Optional[torch.Tensor], scales: Optional[torch.Tensor], bits: int,

@@ -95,23 +95,21 @@ void fill_common(DecodeArgs& a, const rq_shape* s, int32_t n_q_heads, const uint
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 }
 
-}  // namespace
-
-extern "C" {
-
-int rq_encode(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
-              const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, void* stream) {
+// Shared by rq_encode (ref = the final loop) and rq_encode_rotonly (ref = NULL:
+// a zero reference, so each state is quantized directly after the rotation).
+int encode_common(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
+                  const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, void* stream) {
   int st = check_shape(shape);
   if (st != RQ_OK) return st;
   if (n_loops < 1 || n_loops > kMaxLoops) return RQ_EINVAL;
-  if (x == nullptr || bits == nullptr || ref == nullptr || codes == nullptr || scales == nullptr) return RQ_EINVAL;
+  if (x == nullptr || bits == nullptr || codes == nullptr || scales == nullptr) return RQ_EINVAL;
   for (int i = 0; i < n_loops; ++i) {
     if (x[i] == nullptr || codes[i] == nullptr || scales[i] == nullptr) return RQ_EINVAL;
   }
   for (int i = 0; i < n_loops; ++i) {
     if (bits[i] != 2 && bits[i] != 4) return RQ_EUNSUPPORTED;
   }
-  if (!aligned16(ref)) return RQ_EALIGN;
+  if (ref != nullptr && !aligned16(ref)) return RQ_EALIGN;
   for (int i = 0; i < n_loops; ++i) {
     if (!aligned16(x[i]) || !aligned16(codes[i]) || !aligned16(scales[i])) return RQ_EALIGN;
   }
@@ -128,15 +126,15 @@ int rq_encode(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, 
   return hip_status(launch_encode(a, shape->head_dim, static_cast<hipStream_t>(stream)));
 }
 
-int rq_reconstruct(const rq_shape* shape, int32_t bits, const uint16_t* ref, const uint32_t* codes,
-                   const uint16_t* scales, int32_t out_dtype, void* out, void* stream) {
+int reconstruct_common(const rq_shape* shape, int32_t bits, const uint16_t* ref, const uint32_t* codes,
+                       const uint16_t* scales, int32_t out_dtype, void* out, void* stream) {
   int st = check_shape(shape);
   if (st != RQ_OK) return st;
-  if (ref == nullptr || out == nullptr) return RQ_EINVAL;
+  if (out == nullptr) return RQ_EINVAL;
   if (bits != 0 && bits != 2 && bits != 4) return RQ_EUNSUPPORTED;
   if (out_dtype != RQ_OUT_F32 && out_dtype != RQ_OUT_BF16) return RQ_EUNSUPPORTED;
   if (bits != 0 && (codes == nullptr || scales == nullptr)) return RQ_EINVAL;
-  if (!aligned16(ref) || !aligned16(out)) return RQ_EALIGN;
+  if ((ref != nullptr && !aligned16(ref)) || !aligned16(out)) return RQ_EALIGN;
   if (bits != 0 && (!aligned16(codes) || !aligned16(scales))) return RQ_EALIGN;
   ReconstructArgs a{};
   a.ref = ref;
@@ -146,6 +144,33 @@ int rq_reconstruct(const rq_shape* shape, int32_t bits, const uint16_t* ref, con
   a.n_vec = n_vectors(shape);
   return hip_status(launch_reconstruct(a, shape->head_dim, bits, out_dtype == RQ_OUT_BF16,
                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int rq_encode(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
+              const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, void* stream) {
+  if (ref == nullptr) return RQ_EINVAL;
+  return encode_common(shape, n_loops, x, bits, ref, codes, scales, stream);
+}
+
+int rq_reconstruct(const rq_shape* shape, int32_t bits, const uint16_t* ref, const uint32_t* codes,
+                   const uint16_t* scales, int32_t out_dtype, void* out, void* stream) {
+  if (ref == nullptr) return RQ_EINVAL;
+  return reconstruct_common(shape, bits, ref, codes, scales, out_dtype, out, stream);
+}
+
+int rq_encode_rotonly(const rq_shape* shape, int32_t n_states, const uint16_t* const* x, const int32_t* bits,
+                      uint32_t* const* codes, uint16_t* const* scales, void* stream) {
+  return encode_common(shape, n_states, x, bits, nullptr, codes, scales, stream);
+}
+
+int rq_reconstruct_rotonly(const rq_shape* shape, int32_t bits, const uint32_t* codes, const uint16_t* scales,
+                           int32_t out_dtype, void* out, void* stream) {
+  if (bits == 0) return RQ_EUNSUPPORTED;
+  return reconstruct_common(shape, bits, nullptr, codes, scales, out_dtype, out, stream);
 }
 
 int32_t rq_decode_attn_splits(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits) {

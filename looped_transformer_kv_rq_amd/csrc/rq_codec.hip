@@ -99,9 +99,11 @@ __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
   const int64_t stride = (int64_t)gridDim.x * kVecPerBlock;
   for (int64_t v = (int64_t)blockIdx.x * kVecPerBlock + threadIdx.x / kLanes; v < a.n_vec; v += stride) {
     const int64_t base = v * D + sub * PER;
-    // negated reference pair sums and differences
+    // negated reference pair sums and differences (zero without a reference)
     float nrs[PER / 2], nrd[PER / 2];
-    {
+#pragma unroll
+    for (int j = 0; j < PER / 2; ++j) nrs[j] = nrd[j] = 0.0f;
+    if (a.ref != nullptr) {
       const uint4* rp = reinterpret_cast<const uint4*>(a.ref + base);
 #pragma unroll
       for (int i = 0; i < PER / 8; ++i) {
@@ -192,7 +194,12 @@ __global__ __launch_bounds__(256) void rq_reconstruct_kernel(ReconstructArgs a) 
   for (int64_t v = (int64_t)blockIdx.x * kVecPerBlock + threadIdx.x / kLanes; v < a.n_vec; v += stride) {
     const int64_t base = v * D + g * 32;
     float x[32];
-    load_bf16x32(a.ref + base, x);
+    if (a.ref != nullptr) {
+      load_bf16x32(a.ref + base, x);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+    }
     if constexpr (BITS != 0) {
       using G = Grid<BITS>;
       const float s = f16_bits_to_f32(a.scales[v * (D / 32) + g]) * RsqrtD<D>::v;

@@ -20,13 +20,13 @@ struct EncodeArgs {
   uint32_t* codes[kMaxLoops];
   uint16_t* scales[kMaxLoops];
   int32_t bits[kMaxLoops];
-  const uint16_t* ref;
+  const uint16_t* ref;  // NULL: zero reference (rotation-only baseline)
   int32_t n_loops;
   int64_t n_vec;  // batch * n_kv_heads * seq_len
 };
 
 struct ReconstructArgs {
-  const uint16_t* ref;
+  const uint16_t* ref;  // NULL: zero reference (rotation-only baseline)
   const uint32_t* codes;
   const uint16_t* scales;
   void* out;

@@ -25,7 +25,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(rq.library_path())
     names = declared_functions()
-    assert {"rq_encode", "rq_reconstruct", "rq_decode_attn", "rq_decode_attn_bf16",
+    assert {"rq_encode", "rq_reconstruct", "rq_encode_rotonly", "rq_reconstruct_rotonly", "rq_decode_attn",
+            "rq_decode_attn_bf16",
             "rq_decode_attn_workspace", "rq_decode_attn_splits", "rq_status_str", "rq_format_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in rq.h but not exported"
@@ -102,6 +103,25 @@ def test_reconstruct_argument_checks():
     assert lib.rq_reconstruct(sh, 2, FAKE, None, FAKE, 0, FAKE, None) == rq.RQ_EINVAL
     assert lib.rq_reconstruct(sh, 2, FAKE, FAKE, FAKE, 0, None, None) == rq.RQ_EINVAL
     assert lib.rq_reconstruct(sh, 2, FAKE + 4, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EALIGN
+
+
+def test_rotonly_argument_checks():
+    lib = rq._load()
+    sh = ctypes.byref(_shape())
+    bits = (ctypes.c_int32 * 1)(2)
+    x, c, s = _ptrs(FAKE), _ptrs(FAKE), _ptrs(FAKE)
+    assert lib.rq_encode_rotonly(None, 1, x, bits, c, s, None) == rq.RQ_EINVAL
+    assert lib.rq_encode_rotonly(sh, 0, x, bits, c, s, None) == rq.RQ_EINVAL
+    assert lib.rq_encode_rotonly(sh, 1, _ptrs(0), bits, c, s, None) == rq.RQ_EINVAL
+    assert lib.rq_encode_rotonly(sh, 1, x, (ctypes.c_int32 * 1)(0), c, s, None) == rq.RQ_EUNSUPPORTED
+    assert lib.rq_encode_rotonly(sh, 1, _ptrs(FAKE + 8), bits, c, s, None) == rq.RQ_EALIGN
+    # the reference-based encoder still requires its reference
+    assert lib.rq_encode(sh, 1, x, bits, None, c, s, None) == rq.RQ_EINVAL
+    assert lib.rq_reconstruct_rotonly(sh, 0, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EUNSUPPORTED
+    assert lib.rq_reconstruct_rotonly(sh, 2, None, FAKE, 0, FAKE, None) == rq.RQ_EINVAL
+    assert lib.rq_reconstruct_rotonly(sh, 2, FAKE, FAKE, 5, FAKE, None) == rq.RQ_EUNSUPPORTED
+    assert lib.rq_reconstruct_rotonly(sh, 2, FAKE, FAKE, 0, FAKE + 4, None) == rq.RQ_EALIGN
+    assert lib.rq_reconstruct(sh, 2, None, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EINVAL
 
 
 def test_decode_argument_checks():

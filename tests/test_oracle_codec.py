@@ -129,3 +129,27 @@ def test_rotation_spreads_outlier_channels():
 def test_final_loop_is_the_reference():
     ref = np.array([[0x3F80, 0x4000]], dtype=np.uint16)
     np.testing.assert_array_equal(oracle.reconstruct(ref, None, None, 0), [[1.0, 2.0]])
+
+
+def test_rotation_only_baseline_is_the_zero_reference_case():
+    """The rotation-only baseline quantizes H x itself. With a zero reference,
+    encode's reconstruction error of x equals its rotated-domain error, and on
+    loop states close to the final loop the residual codec is far more
+    accurate at the same bit width (the ResidualQuant abstract's claim against
+    the rotation-based baseline)."""
+    rng = np.random.default_rng(7)
+    ref = workloads.f32_to_bf16_bits(rng.standard_normal((200, 128)).astype(np.float32))
+    x = workloads.f32_to_bf16_bits((workloads.bf16_bits_to_f32(ref) +
+                                    0.1 * rng.standard_normal((200, 128))).astype(np.float32))
+    zero = np.zeros_like(ref)
+    w0, s0 = oracle.encode(x, zero, 2)
+    xh0 = oracle.reconstruct(zero, w0, s0, 2)
+    y = oracle.rotate(oracle.bf16_to_f64(x))
+    q = oracle.dequantize(w0, s0, 2, 128)
+    np.testing.assert_allclose(np.linalg.norm(xh0 - oracle.bf16_to_f64(x)), np.linalg.norm(q - y), rtol=1e-10)
+    w1, s1 = oracle.encode(x, ref, 2)
+    xh1 = oracle.reconstruct(ref, w1, s1, 2)
+    xf = oracle.bf16_to_f64(x)
+    e_rot = np.linalg.norm(xh0 - xf) / np.linalg.norm(xf)
+    e_res = np.linalg.norm(xh1 - xf) / np.linalg.norm(xf)
+    assert e_res < 0.2 * e_rot
