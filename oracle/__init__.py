@@ -21,6 +21,7 @@ from .rq_oracle import (  # noqa: F401
     quantize_groups,
     reconstruct,
     reconstruction_error,
+    refit_codes,
     rotate,
     unpack_codes,
 )

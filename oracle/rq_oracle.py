@@ -123,13 +123,40 @@ def ls_scale(y: np.ndarray, q: np.ndarray) -> np.ndarray:
     return np.sum(y * q, axis=-1) / np.sum(q * q, axis=-1)
 
 
-def quantize_groups(y: np.ndarray, bits: int):
+def refit_codes(y: np.ndarray, s: np.ndarray, bits: int) -> np.ndarray:
+    """Codes of one group (last axis) at a given step s: the nearest level
+    (c - (2^(b-1) - 1/2)) s, by the same floor rule as the first assignment,
+    clipped to the grid. A group with s = 0 keeps every code at 2^(b-1)."""
+    y = np.asarray(y, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)[..., None]
+    top = 2 ** bits - 1
+    half = 2 ** (bits - 1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = np.where(s > 0, y / np.where(s > 0, s, 1.0), 0.0)
+    codes = np.clip(np.floor(u) + half, 0, top).astype(np.int64)
+    return np.where(s > 0, codes, half)
+
+
+def quantize_groups(y: np.ndarray, bits: int, refits: int = 0, steps=None):
     """y[..., n_groups, group] -> (codes, s) with s the float64 LS scale
-    (0 for all-zero groups)."""
+    (0 for all-zero groups).
+
+    refits > 0 alternates the two steps the method names: codes for a fixed
+    scale (nearest level), then the least-squares scale for fixed codes, that
+    many more times after the first fit. Each half-step can only lower
+    |y - s q|. If `steps` is a list, the step of every assignment (s0, then
+    each refit's scale) is appended to it."""
     codes, s0 = assign_codes(y, bits)
+    if steps is not None:
+        steps.append(s0)
     q = codes - level_offset(bits)
-    s = ls_scale(y, q)
-    s = np.where(s0 > 0, s, 0.0)
+    s = np.where(s0 > 0, ls_scale(y, q), 0.0)
+    for _ in range(refits):
+        if steps is not None:
+            steps.append(s)
+        codes = refit_codes(y, s, bits)
+        q = codes - level_offset(bits)
+        s = np.where(s0 > 0, ls_scale(y, q), 0.0)
     return codes, s
 
 
@@ -166,12 +193,13 @@ def rotate(r: np.ndarray) -> np.ndarray:
     return np.asarray(r, dtype=np.float64) @ hadamard(d)
 
 
-def encode(x_bits, ref_bits, bits: int, group: int = GROUP):
+def encode(x_bits, ref_bits, bits: int, group: int = GROUP, refits: int = 0):
     """Encode one loop of K or V against the reference.
 
     x_bits, ref_bits: bf16 patterns [..., D]. Returns (words uint32 [..., D*b/32],
     scale_bits uint16 (fp16) [..., D/group]). ``group`` is exposed only so the
-    tests can quantize tiny groups; the storage format fixes 32.
+    tests can quantize tiny groups; the storage format fixes 32. ``refits``
+    adds that many code/scale alternations after the first fit.
     """
     if bits not in (2, 4):
         raise ValueError("residual width must be 2 or 4")
@@ -181,7 +209,7 @@ def encode(x_bits, ref_bits, bits: int, group: int = GROUP):
     y = rotate(r)                                # orthogonal rotation
     d = y.shape[-1]
     yg = y.reshape(y.shape[:-1] + (d // group, group))
-    codes, s = quantize_groups(yg, bits)         # per-group codes + LS scale
+    codes, s = quantize_groups(yg, bits, refits)  # per-group codes + LS scale
     s16 = f64_to_f16(s)                          # fp16 storage
     words = pack_codes(codes.reshape(y.shape), bits)
     return words, s16
