@@ -17,6 +17,8 @@ measured kernel):
 * the bf16-KV baseline decode (rq_decode_attn_bf16) over the same loops;
 * one call per loop (per-loop mode);
 * rq_reconstruct of one loop;
+* rq_encode_refit of K with 0, 1 and 2 code / LS-scale refits: encode rate
+  and reconstruction error per residual loop;
 * the rotation-only baseline (rq_encode_rotonly of every loop of K with no
   reference): its encode rate, and its per-loop reconstruction error and
   cache bytes beside those of the residual codec.
@@ -409,6 +411,30 @@ def main():
                                    "vs_bf16_all_loop": bf_ms / per_loop_total}
         result["reconstruct"] = {"loop": res_loops[0], "bits": bits[0], "ms": rc_ms,
                                  "GBps": reconstruct_bytes(w, bits[0]) / (rc_ms * 1e-3) / 1e9}
+
+        # Code / LS-scale refits (rq_encode_refit): encode rate of K and the
+        # residual-relative reconstruction error |x_hat - x| / |x - x_ref| per
+        # residual loop, for 0, 1 and 2 refits.
+        refit = []
+        for k in (0, 1, 2):
+            rc_c = [torch.empty_like(t) for t in kc]
+            rc_s = [torch.empty_like(t) for t in ks]
+
+            def enc_rf(k=k, rc_c=rc_c, rc_s=rc_s):
+                rq.encode_into([kx[l] for l in res_loops], kref, bits, rc_c, rc_s, stream=stream, refits=k)
+
+            rf_ms = timed(enc_rf, max(5, args.reps // 2))
+            errs = []
+            for i, l in enumerate(res_loops):
+                xq = rq.reconstruct(kref, rc_c[i], rc_s[i], bits[i], stream=stream)
+                xl = kx[l].float()
+                errs.append(torch.linalg.vector_norm(xq - xl).item() /
+                            torch.linalg.vector_norm(xl - kref.float()).item())
+                del xq, xl
+            refit.append({"refits": k, "encode_ms": rf_ms, "encode_GBps": enc_b / (rf_ms * 1e-3) / 1e9,
+                          "residual_rel_error_per_loop": errs})
+            del rc_c, rc_s
+        result["encode_refits"] = refit
 
         # Rotation-only baseline (no reference: every loop, the final one
         # included, quantized directly after the rotation) at the same widths,

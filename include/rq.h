@@ -14,6 +14,7 @@
  *   rq_decode_attn     fused reconstruct + single-query decode attention
  *   rq_decode_attn_bf16  the same decode attention over plain bf16 K/V per
  *                        loop (the uncompressed baseline)
+ *   rq_encode_refit    rq_encode with extra code / LS-scale alternations
  *   rq_encode_rotonly / rq_reconstruct_rotonly  the rotation-only baseline:
  *                        the same codec without a reference
  *
@@ -61,6 +62,7 @@ extern "C" {
 #define RQ_FORMAT_VERSION 1
 #define RQ_GROUP 32
 #define RQ_MAX_LOOPS 8
+#define RQ_MAX_REFITS 16
 
 typedef enum rq_status {
   RQ_OK = 0,
@@ -107,6 +109,19 @@ typedef struct rq_loop_view {
  * the inputs. */
 int rq_encode(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
               const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, void* stream);
+
+/* rq_encode with `refits` extra alternations of the two least-squares
+ * half-steps after the first fit (ResidualQuant, newx.sg page, AI Summary:
+ * the scale is a least-squares fit; the alternation applies that fit in turn
+ * to the codes). Each round first reassigns every code to the nearest level
+ * at the current scale s: c = clamp(floor(y / s) + 2^(b-1), 0, 2^b - 1).
+ * Then it refits s = <y, q> / <q, q>. Neither step can raise |y - s q|.
+ * refits = 0 is rq_encode. The format is unchanged, so rq_reconstruct and
+ * rq_decode_attn read the output as they read rq_encode's.
+ *   refits  0 .. RQ_MAX_REFITS (RQ_EINVAL otherwise); other arguments as rq_encode. */
+int rq_encode_refit(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
+                    const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, int32_t refits,
+                    void* stream);
 
 /* Materialise one loop: out = ref + H (s * q) (ResidualQuant, newx.sg page,
  * Abstract: the residual format keeps reconstruction cheap).

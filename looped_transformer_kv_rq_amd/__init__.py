@@ -74,6 +74,7 @@ def _load():
     sig = {
         "rq_encode": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, ctypes.POINTER(I32), P, PP, PP, P]),
         "rq_reconstruct": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, P, P, P, I32, P, P]),
+        "rq_encode_refit": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, ctypes.POINTER(I32), P, PP, PP, I32, P]),
         "rq_encode_rotonly": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, ctypes.POINTER(I32), PP, PP, P]),
         "rq_reconstruct_rotonly": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, P, P, I32, P, P]),
         "rq_decode_attn_splits": (I32, [ctypes.POINTER(_Shape), I32, I32, I32]),
@@ -146,8 +147,8 @@ def _check(status: int, what: str):
 # ---------------------------------------------------------------------------
 
 def encode_into(xs: Sequence[torch.Tensor], ref: torch.Tensor, bits: Sequence[int],
-                codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor], stream=None) -> None:
-    """rq_encode into caller-provided outputs."""
+                codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor], stream=None, refits: int = 0) -> None:
+    """rq_encode (rq_encode_refit when refits > 0) into caller-provided outputs."""
     lib = _load()
     shp = _shape_of(ref)
     b, h, s, d = ref.shape
@@ -160,14 +161,20 @@ def encode_into(xs: Sequence[torch.Tensor], ref: torch.Tensor, bits: Sequence[in
         _need(codes[i], f"codes[{i}]", torch.int32, (b, h, s, d * int(bits[i]) // 32), ref.device)
         _need(scales[i], f"scales[{i}]", torch.float16, (b, h, s, d // GROUP), ref.device)
     bits_arr = (ctypes.c_int32 * n)(*[int(x) for x in bits])
-    st = lib.rq_encode(ctypes.byref(shp), n, _ptr_array(xs), bits_arr, _ptr(ref), _ptr_array(codes),
-                       _ptr_array(scales), _stream(ref.device, stream))
-    _check(st, "rq_encode")
+    if refits:
+        st = lib.rq_encode_refit(ctypes.byref(shp), n, _ptr_array(xs), bits_arr, _ptr(ref), _ptr_array(codes),
+                                 _ptr_array(scales), int(refits), _stream(ref.device, stream))
+        _check(st, "rq_encode_refit")
+    else:
+        st = lib.rq_encode(ctypes.byref(shp), n, _ptr_array(xs), bits_arr, _ptr(ref), _ptr_array(codes),
+                           _ptr_array(scales), _stream(ref.device, stream))
+        _check(st, "rq_encode")
 
 
-def encode(xs: Sequence[torch.Tensor], ref: torch.Tensor, bits: Sequence[int], stream=None):
-    """Encode loops xs[i] (bf16 [B,Hkv,S,D]) against the final-loop ref.
-    Returns (codes, scales): per loop int32 [B,Hkv,S,D*bits/32] and fp16 [B,Hkv,S,D/32]."""
+def encode(xs: Sequence[torch.Tensor], ref: torch.Tensor, bits: Sequence[int], stream=None, refits: int = 0):
+    """Encode loops xs[i] (bf16 [B,Hkv,S,D]) against the final-loop ref, with `refits`
+    extra code / LS-scale alternations. Returns (codes, scales): per loop int32
+    [B,Hkv,S,D*bits/32] and fp16 [B,Hkv,S,D/32]."""
     if ref.dim() != 4:
         raise ValueError("ref must be [batch, n_kv_heads, seq_len, head_dim]")
     b, h, s, d = ref.shape
@@ -176,7 +183,7 @@ def encode(xs: Sequence[torch.Tensor], ref: torch.Tensor, bits: Sequence[int], s
             raise ValueError("encode bit widths must be 2 or 4")
     codes = [torch.empty((b, h, s, d * int(x) // 32), dtype=torch.int32, device=ref.device) for x in bits]
     scales = [torch.empty((b, h, s, d // GROUP), dtype=torch.float16, device=ref.device) for _ in bits]
-    encode_into(xs, ref, bits, codes, scales, stream)
+    encode_into(xs, ref, bits, codes, scales, stream, refits)
     return codes, scales
 
 

@@ -98,10 +98,12 @@ void fill_common(DecodeArgs& a, const rq_shape* s, int32_t n_q_heads, const uint
 // Shared by rq_encode (ref = the final loop) and rq_encode_rotonly (ref = NULL:
 // a zero reference, so each state is quantized directly after the rotation).
 int encode_common(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
-                  const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, void* stream) {
+                  const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, int32_t refits,
+                  void* stream) {
   int st = check_shape(shape);
   if (st != RQ_OK) return st;
   if (n_loops < 1 || n_loops > kMaxLoops) return RQ_EINVAL;
+  if (refits < 0 || refits > RQ_MAX_REFITS) return RQ_EINVAL;
   if (x == nullptr || bits == nullptr || codes == nullptr || scales == nullptr) return RQ_EINVAL;
   for (int i = 0; i < n_loops; ++i) {
     if (x[i] == nullptr || codes[i] == nullptr || scales[i] == nullptr) return RQ_EINVAL;
@@ -122,6 +124,7 @@ int encode_common(const rq_shape* shape, int32_t n_loops, const uint16_t* const*
   }
   a.ref = ref;
   a.n_loops = n_loops;
+  a.refits = refits;
   a.n_vec = n_vectors(shape);
   return hip_status(launch_encode(a, shape->head_dim, static_cast<hipStream_t>(stream)));
 }
@@ -153,7 +156,14 @@ extern "C" {
 int rq_encode(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
               const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, void* stream) {
   if (ref == nullptr) return RQ_EINVAL;
-  return encode_common(shape, n_loops, x, bits, ref, codes, scales, stream);
+  return encode_common(shape, n_loops, x, bits, ref, codes, scales, 0, stream);
+}
+
+int rq_encode_refit(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
+                    const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, int32_t refits,
+                    void* stream) {
+  if (ref == nullptr) return RQ_EINVAL;
+  return encode_common(shape, n_loops, x, bits, ref, codes, scales, refits, stream);
 }
 
 int rq_reconstruct(const rq_shape* shape, int32_t bits, const uint16_t* ref, const uint32_t* codes,
@@ -164,7 +174,7 @@ int rq_reconstruct(const rq_shape* shape, int32_t bits, const uint16_t* ref, con
 
 int rq_encode_rotonly(const rq_shape* shape, int32_t n_states, const uint16_t* const* x, const int32_t* bits,
                       uint32_t* const* codes, uint16_t* const* scales, void* stream) {
-  return encode_common(shape, n_states, x, bits, nullptr, codes, scales, stream);
+  return encode_common(shape, n_states, x, bits, nullptr, codes, scales, 0, stream);
 }
 
 int rq_reconstruct_rotonly(const rq_shape* shape, int32_t bits, const uint32_t* codes, const uint16_t* scales,

@@ -50,36 +50,47 @@ constexpr uint32_t kPairDiff = 0xBF803F80u;  // bf16 (+1, -1), low half first
 //    every partial sum is an integer below 2^16).
 //  * INT2: q^2 is 1/4 for the inner codes 1, 2 and 9/4 for 0, 3, so
 //    <q, q> = 72 - 2 * (number of inner codes), counted on the packed words.
-template <int BITS, int D>
-__device__ __forceinline__ float quantize_group(const float* y, uint32_t (&words)[BITS]) {
+//  * refits > 0 alternates the two least-squares half-steps that many more
+//    times: codes at the current scale (same floor rule, now clamped to the
+//    grid, since |y| / s may exceed the top level), then the LS scale again.
+template <int BITS, int D, bool REFIT>
+__device__ __forceinline__ float quantize_group(const float* y, int refits, uint32_t (&words)[BITS]) {
   using G = Grid<BITS>;
   constexpr int kPerHalf = G::kPerWord / 2;  // codes per 16-bit half word
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(y[i]));
-  const float inv = m > 0.0f ? G::kOff / m : 0.0f;
-  float num = 0.0f, den = 0.0f;
-  float half[2 * BITS];
+  float inv = m > 0.0f ? G::kOff / m : 0.0f;  // 1 / step of the assignment
+  float sfit = 0.0f;
+  const int passes = REFIT ? refits + 1 : 1;
+  for (int pass = 0; pass < passes; ++pass) {
+    float num = 0.0f, den = 0.0f;
+    float half[2 * BITS];
 #pragma unroll
-  for (int k = 0; k < 2 * BITS; ++k) half[k] = 0.0f;
+    for (int k = 0; k < 2 * BITS; ++k) half[k] = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float c = floorf(fmaf(y[i], inv, (float)G::kHalf));
-    const float q = c - G::kOff;
-    num = fmaf(y[i], q, num);
-    if constexpr (BITS == 4) den = fmaf(q, q, den);
-    half[i / kPerHalf] = fmaf(c, (float)(1u << (BITS * (i % kPerHalf))), half[i / kPerHalf]);
+    for (int i = 0; i < 32; ++i) {
+      // (no clamp is needed at the absmax step; the refit steps clamp)
+      float c = floorf(fmaf(y[i], inv, (float)G::kHalf));
+      if constexpr (REFIT) c = __builtin_amdgcn_fmed3f(c, 0.0f, (float)G::kTop);
+      const float q = c - G::kOff;
+      num = fmaf(y[i], q, num);
+      if constexpr (BITS == 4) den = fmaf(q, q, den);
+      half[i / kPerHalf] = fmaf(c, (float)(1u << (BITS * (i % kPerHalf))), half[i / kPerHalf]);
+    }
+#pragma unroll
+    for (int k = 0; k < BITS; ++k)
+      words[k] = (uint32_t)half[2 * k] | ((uint32_t)half[2 * k + 1] << 16);
+    if constexpr (BITS == 2) {
+      int inner = 0;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) inner += __builtin_popcount((words[k] ^ (words[k] >> 1)) & 0x55555555u);
+      den = (float)(72 - 2 * inner);
+    }
+    sfit = num / den;                       // 0 for an all-zero group
+    inv = sfit > 0.0f ? 1.0f / sfit : 0.0f;  // step of the next assignment
   }
-#pragma unroll
-  for (int k = 0; k < BITS; ++k)
-    words[k] = (uint32_t)half[2 * k] | ((uint32_t)half[2 * k + 1] << 16);
-  if constexpr (BITS == 2) {
-    int inner = 0;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) inner += __builtin_popcount((words[k] ^ (words[k] >> 1)) & 0x55555555u);
-    den = (float)(72 - 2 * inner);
-  }
-  return num / den * RsqrtD<D>::v;
+  return sfit * RsqrtD<D>::v;
 }
 
 // Encode kernel: PER coordinates of a vector per lane (PER / 32 scale
@@ -90,7 +101,7 @@ __device__ __forceinline__ float quantize_group(const float* y, uint32_t (&words
 //    difference; the reference pair sums are formed once for all loops.
 //  * Butterflies on the remaining in-lane index bits stay in registers; those
 //    on the lane bits go across lanes inside a quad (DPP).
-template <int D, int PER>
+template <int D, int PER, bool REFIT>
 __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
   constexpr int kLanes = D / PER;  // lanes per vector
   constexpr int kVecPerBlock = 256 / kLanes;
@@ -158,7 +169,7 @@ __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
 #pragma unroll
         for (int gi = 0; gi < NGL; ++gi) {
           uint32_t w2[2];
-          sc[gi] = f32_to_f16_sat(quantize_group<2, D>(y + 32 * gi, w2));
+          sc[gi] = f32_to_f16_sat(quantize_group<2, D, REFIT>(y + 32 * gi, a.refits, w2));
           wd[2 * gi] = w2[0];
           wd[2 * gi + 1] = w2[1];
         }
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
 #pragma unroll
         for (int gi = 0; gi < NGL; ++gi) {
           uint32_t w4[4];
-          sc[gi] = f32_to_f16_sat(quantize_group<4, D>(y + 32 * gi, w4));
+          sc[gi] = f32_to_f16_sat(quantize_group<4, D, REFIT>(y + 32 * gi, a.refits, w4));
 #pragma unroll
           for (int k = 0; k < 4; ++k) wd[4 * gi + k] = w4[k];
         }
@@ -255,15 +266,17 @@ static unsigned grid_for(int64_t n_vec, int vec_per_block) {
 // registers) and runs slower.
 constexpr int kEncodePer = 32;
 
-hipError_t launch_encode(const EncodeArgs& a, int head_dim, hipStream_t stream) {
+template <int D>
+static void launch_encode_d(const EncodeArgs& a, hipStream_t stream) {
   constexpr int per = kEncodePer;
-  if (head_dim == 128) {
-    hipLaunchKernelGGL((rq_encode_kernel<128, per>), dim3(grid_for(a.n_vec, 256 / (128 / per))), dim3(256), 0,
-                       stream, a);
-  } else {
-    hipLaunchKernelGGL((rq_encode_kernel<64, per>), dim3(grid_for(a.n_vec, 256 / (64 / per))), dim3(256), 0,
-                       stream, a);
-  }
+  const dim3 grid(grid_for(a.n_vec, 256 / (D / per)));
+  if (a.refits > 0) hipLaunchKernelGGL((rq_encode_kernel<D, per, true>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((rq_encode_kernel<D, per, false>), grid, dim3(256), 0, stream, a);
+}
+
+hipError_t launch_encode(const EncodeArgs& a, int head_dim, hipStream_t stream) {
+  if (head_dim == 128) launch_encode_d<128>(a, stream);
+  else launch_encode_d<64>(a, stream);
   return hipGetLastError();
 }
 

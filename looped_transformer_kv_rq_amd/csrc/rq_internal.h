@@ -22,6 +22,7 @@ struct EncodeArgs {
   int32_t bits[kMaxLoops];
   const uint16_t* ref;  // NULL: zero reference (rotation-only baseline)
   int32_t n_loops;
+  int32_t refits;       // extra code / LS-scale alternations after the first fit
   int64_t n_vec;  // batch * n_kv_heads * seq_len
 };
 

@@ -86,3 +86,39 @@ def assert_attn_close(gpu: np.ndarray, ref: np.ndarray, tol: float = ATTN_TOL):
     assert np.all(np.isfinite(gpu)), "non-finite attention output"
     assert e.max() <= tol, f"attention row error {e.max():.3e} > {tol} at row {np.unravel_index(e.argmax(), e.shape)}"
     return float(e.max())
+
+
+def refit_exempt_groups(x_bits: np.ndarray, ref_bits: np.ndarray, bits: int, refits: int) -> np.ndarray:
+    """Groups [..., D/32] holding a coordinate within BOUNDARY_EPS of a
+    threshold of any assignment step (the first fit's s0 and every refit's
+    scale). A decision taken differently at one step changes the next step's
+    scale, so the whole group is exempt; elsewhere every step's decisions
+    agree and the codes must be bit-exact."""
+    r = oracle.bf16_to_f64(x_bits) - oracle.bf16_to_f64(ref_bits)
+    y = oracle.rotate(r)
+    d = y.shape[-1]
+    yg = y.reshape(y.shape[:-1] + (d // 32, 32))
+    steps = []
+    oracle.quantize_groups(yg, bits, refits, steps=steps)
+    ks = np.arange(-(2 ** (bits - 1) - 1), 2 ** (bits - 1))
+    near = np.zeros(yg.shape[:-1], dtype=bool)
+    for s in steps:
+        dist = np.min(np.abs(yg[..., None] - s[..., None, None] * ks), axis=-1)
+        near |= (dist <= BOUNDARY_EPS).any(axis=-1)
+    return near
+
+
+def compare_codes_refit(gpu_words, gpu_scales, orc_words, orc_scales, x_bits, ref_bits, bits, refits):
+    """Parity of an encode with refits: codes and scales of every group that is
+    not exempt (refit_exempt_groups) match the oracle (codes bit-exact, scales
+    within one fp16 ulp). Returns the number of exempt groups that differ."""
+    d = x_bits.shape[-1]
+    cg = oracle.unpack_codes(gpu_words, bits)
+    co = oracle.unpack_codes(orc_words, bits)
+    gdiff = (cg != co).reshape(cg.shape[:-1] + (d // 32, 32)).any(axis=-1)
+    ulp = np.abs(gpu_scales.astype(np.int32) - orc_scales.astype(np.int32))
+    gdiff |= ulp > 1
+    exempt = refit_exempt_groups(x_bits, ref_bits, bits, refits) if gdiff.any() else np.zeros_like(gdiff)
+    bad = gdiff & ~exempt
+    assert not bad.any(), f"{int(bad.sum())} group(s) differ away from every step's decision boundaries"
+    return int((gdiff & exempt).sum())

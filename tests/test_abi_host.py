@@ -25,7 +25,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(rq.library_path())
     names = declared_functions()
-    assert {"rq_encode", "rq_reconstruct", "rq_encode_rotonly", "rq_reconstruct_rotonly", "rq_decode_attn",
+    assert {"rq_encode", "rq_reconstruct", "rq_encode_refit", "rq_encode_rotonly", "rq_reconstruct_rotonly", "rq_decode_attn",
             "rq_decode_attn_bf16",
             "rq_decode_attn_workspace", "rq_decode_attn_splits", "rq_status_str", "rq_format_version"} <= set(names)
     for n in names:
@@ -115,8 +115,12 @@ def test_rotonly_argument_checks():
     assert lib.rq_encode_rotonly(sh, 1, _ptrs(0), bits, c, s, None) == rq.RQ_EINVAL
     assert lib.rq_encode_rotonly(sh, 1, x, (ctypes.c_int32 * 1)(0), c, s, None) == rq.RQ_EUNSUPPORTED
     assert lib.rq_encode_rotonly(sh, 1, _ptrs(FAKE + 8), bits, c, s, None) == rq.RQ_EALIGN
-    # the reference-based encoder still requires its reference
+    # the reference-based encoders still require their reference
     assert lib.rq_encode(sh, 1, x, bits, None, c, s, None) == rq.RQ_EINVAL
+    assert lib.rq_encode_refit(sh, 1, x, bits, None, c, s, 1, None) == rq.RQ_EINVAL
+    assert lib.rq_encode_refit(sh, 1, x, bits, FAKE, c, s, -1, None) == rq.RQ_EINVAL
+    assert lib.rq_encode_refit(sh, 1, x, bits, FAKE, c, s, 17, None) == rq.RQ_EINVAL
+    assert lib.rq_encode_refit(sh, 1, x, (ctypes.c_int32 * 1)(3), FAKE, c, s, 2, None) == rq.RQ_EUNSUPPORTED
     assert lib.rq_reconstruct_rotonly(sh, 0, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EUNSUPPORTED
     assert lib.rq_reconstruct_rotonly(sh, 2, None, FAKE, 0, FAKE, None) == rq.RQ_EINVAL
     assert lib.rq_reconstruct_rotonly(sh, 2, FAKE, FAKE, 5, FAKE, None) == rq.RQ_EUNSUPPORTED
