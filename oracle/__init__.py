@@ -9,6 +9,7 @@ from .rq_oracle import (  # noqa: F401
     attention,
     bf16_to_f64,
     decode_attn,
+    decode_attn_varlen,
     dequantize,
     encode,
     f16_to_f64,

@@ -276,3 +276,38 @@ def decode_attn(q_bits, k_hat: list, v_hat: list, scale: float | None = None) ->
                 rows = slice(kv * g, (kv + 1) * g)
                 out[l, b, rows] = attention(q[l, b, rows], k_hat[l][b, kv], v_hat[l][b, kv], scale)
     return out
+
+
+def decode_attn_varlen(q_bits, k_hat: list, v_hat: list, seq_lens, tail_k_bits=None, tail_v_bits=None,
+                       scale: float | None = None) -> np.ndarray:
+    """Decode attention over a partly filled cache plus bf16 positions not
+    yet encoded (the serving step around the hot path; paperaft JSON page,
+    `summary`).
+
+    q_bits: bf16 [n_loops, B, Hq, D]; k_hat, v_hat: per loop float64
+    [B, Hkv, S_cap, D]; seq_lens: [B], the positions of sequence b are
+    0 .. seq_lens[b]-1; tail_k_bits, tail_v_bits: per loop bf16 [B, Hkv, T, D]
+    or None. Row (l, b, h) attends to its sequence's cached positions followed
+    by its tail. A row with no position at all is zero.
+    """
+    q = bf16_to_f64(q_bits)
+    n_loops, batch, hq, d = q.shape
+    hkv = k_hat[0].shape[1]
+    g = hq // hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros_like(q)
+    for l in range(n_loops):
+        for b in range(batch):
+            n = int(seq_lens[b])
+            for kv in range(hkv):
+                k = k_hat[l][b, kv, :n]
+                v = v_hat[l][b, kv, :n]
+                if tail_k_bits is not None:
+                    k = np.concatenate([k, bf16_to_f64(tail_k_bits[l][b, kv])], axis=0)
+                    v = np.concatenate([v, bf16_to_f64(tail_v_bits[l][b, kv])], axis=0)
+                if k.shape[0] == 0:
+                    continue
+                rows = slice(kv * g, (kv + 1) * g)
+                out[l, b, rows] = attention(q[l, b, rows], k, v, scale)
+    return out

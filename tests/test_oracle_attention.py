@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
+import workloads
 
 
 def _brute(q, k, v):
@@ -71,3 +72,50 @@ def test_decode_scale_and_loops():
     for l in range(n_loops):
         for h in range(hkv * g):
             np.testing.assert_allclose(out[l, 0, h], _brute(list(q[l, 0, h]), k[l][0, 0].tolist(), v[l][0, 0].tolist()), rtol=1e-12)
+
+
+def _bf16(rng, shape):
+    return workloads.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+
+def test_varlen_moving_a_position_into_the_tail_changes_nothing():
+    """Attention is over a set of positions: position n-1 of the prefix and the
+    same key/value given as a one-position tail give the same output."""
+    rng = np.random.default_rng(21)
+    L, B, Hkv, Hq, S, D = 2, 3, 2, 4, 9, 16
+    q = _bf16(rng, (L, B, Hq, D))
+    kb = [_bf16(rng, (B, Hkv, S, D)) for _ in range(L)]
+    vb = [_bf16(rng, (B, Hkv, S, D)) for _ in range(L)]
+    kh = [oracle.bf16_to_f64(x) for x in kb]
+    vh = [oracle.bf16_to_f64(x) for x in vb]
+    lens = np.array([9, 4, 1])
+    full = oracle.decode_attn_varlen(q, kh, vh, lens)
+    tk = [np.stack([kb[l][b, :, lens[b] - 1:lens[b]] for b in range(B)]) for l in range(L)]
+    tv = [np.stack([vb[l][b, :, lens[b] - 1:lens[b]] for b in range(B)]) for l in range(L)]
+    moved = oracle.decode_attn_varlen(q, kh, vh, lens - 1, tk, tv)
+    np.testing.assert_allclose(moved, full, rtol=1e-12, atol=1e-14)
+    # every position of the cache: the plain decode
+    np.testing.assert_allclose(oracle.decode_attn_varlen(q, kh, vh, np.full(B, S)), oracle.decode_attn(q, kh, vh),
+                               rtol=0, atol=0)
+
+
+def test_varlen_special_cases():
+    rng = np.random.default_rng(22)
+    L, B, Hkv, Hq, S, D = 1, 2, 1, 2, 5, 8
+    q = _bf16(rng, (L, B, Hq, D))
+    kh = [oracle.bf16_to_f64(_bf16(rng, (B, Hkv, S, D)))]
+    vh = [oracle.bf16_to_f64(_bf16(rng, (B, Hkv, S, D)))]
+    tk = [_bf16(rng, (B, Hkv, 1, D))]
+    tv = [_bf16(rng, (B, Hkv, 1, D))]
+    # no cached position and no tail: a zero row; one tail position only: its value
+    out = oracle.decode_attn_varlen(q, kh, vh, np.array([0, 0]))
+    assert np.all(out == 0)
+    out = oracle.decode_attn_varlen(q, kh, vh, np.array([0, 0]), tk, tv)
+    for b in range(B):
+        for h in range(Hq):
+            np.testing.assert_allclose(out[0, b, h], oracle.bf16_to_f64(tv[0][b, 0, 0]), rtol=1e-15)
+    # one cached position: its value
+    out = oracle.decode_attn_varlen(q, kh, vh, np.array([1, 1]))
+    for b in range(B):
+        for h in range(Hq):
+            np.testing.assert_allclose(out[0, b, h], vh[0][b, 0, 0], rtol=1e-15)
