@@ -19,6 +19,8 @@ measured kernel):
 * rq_reconstruct of one loop;
 * rq_encode_refit of K with 0, 1 and 2 code / LS-scale refits: encode rate
   and reconstruction error per residual loop;
+* a serving step: rq_decode_attn_varlen over ragged prefixes plus one bf16
+  tail position per loop, then rq_encode_append of that position (K and V);
 * the rotation-only baseline (rq_encode_rotonly of every loop of K with no
   reference): its encode rate, and its per-loop reconstruction error and
   cache bytes beside those of the residual codec.
@@ -469,6 +471,35 @@ def main():
             "bytes_per_token_head": cache_bytes_per_token_head(w, ro_bits, False),
             "rq_bytes_per_token_head": cache_bytes_per_token_head(w, list(w.bits), True),
             "bf16_bytes_per_token_head": 2 * 2 * w.head_dim * w.n_loops,
+        }
+
+        # Serving step (rq_decode_attn_varlen + rq_encode_append): ragged prefix
+        # lengths drawn in [S/2, S), every loop's current position as a one-position
+        # bf16 tail, then that position appended to the K and V caches. Runs last:
+        # the appends overwrite one position per sequence of the cache above.
+        lrng = np.random.default_rng(w.seed)
+        lens = lrng.integers(w.seq_len // 2, w.seq_len, size=w.batch).astype(np.int32)
+        lens_d = torch.from_numpy(lens).to(dev)
+        tk = [x[:, :, :1].contiguous() for x in kx]
+        tv = [x[:, :, :1].contiguous() for x in vx]
+        ws_v = torch.empty(rq.decode_varlen_workspace_bytes(w.batch, w.n_kv_heads, w.seq_len, w.head_dim,
+                                                            w.n_q_heads, w.n_loops, 0, 1),
+                           dtype=torch.uint8, device=dev)
+
+        def serve():
+            rq.decode_attn_varlen(q, kref, vref, views, seq_lens=lens_d, tail_k=tk, tail_v=tv, out=out,
+                                  workspace=ws_v, stream=stream)
+            rq.encode_append([tk[l] for l in res_loops], tk[-1], bits, lens_d, kref, kc, ks, stream=stream)
+            rq.encode_append([tv[l] for l in res_loops], tv[-1], bits, lens_d, vref, vc, vs, stream=stream)
+
+        sv_ms = timed(serve, args.reps)
+        per_tok = decode_bytes(w, list(w.bits)) / (w.batch * w.seq_len)  # cache bytes per (b, position)
+        sv_bytes = per_tok * float(lens.sum()) + w.batch * w.n_kv_heads * w.n_loops * 4 * w.head_dim
+        result["serving_step"] = {
+            "ms": sv_ms, "prefix_tokens": int(lens.sum()), "tail_positions_per_loop": 1,
+            "decode_GBps": sv_bytes / (sv_ms * 1e-3) / 1e9,
+            "kv_tokens_per_s": float(lens.sum() + w.batch) * w.n_loops / (sv_ms * 1e-3),
+            "what": "rq_decode_attn_varlen (ragged prefixes + 1 tail position) + rq_encode_append of K and V",
         }
     if cpu is not None:
         result["cpu_baseline"] = cpu

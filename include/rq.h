@@ -15,6 +15,8 @@
  *   rq_decode_attn_bf16  the same decode attention over plain bf16 K/V per
  *                        loop (the uncompressed baseline)
  *   rq_encode_refit    rq_encode with extra code / LS-scale alternations
+ *   rq_encode_append   encode new positions into a cache at per-sequence positions
+ *   rq_decode_attn_varlen  decode over per-sequence prefix lengths plus a bf16 tail
  *   rq_encode_rotonly / rq_reconstruct_rotonly  the rotation-only baseline:
  *                        the same codec without a reference
  *
@@ -123,6 +125,26 @@ int rq_encode_refit(const rq_shape* shape, int32_t n_loops, const uint16_t* cons
                     const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, int32_t refits,
                     void* stream);
 
+/* Append t_new new positions per sequence to a residual cache: the serving
+ * step around the hot path (ResidualQuant, paperaft JSON page, `summary`: the
+ * cache lives in this custom format inside a serving stack). A position's
+ * earlier loops can only be encoded once its final loop exists. This call
+ * encodes the new positions' loops against their final-loop states, writes
+ * the codes and scales at each sequence's write position, and copies the
+ * final-loop states into the bf16 reference cache.
+ *   cache      shape of the cache tensors; cache->seq_len is their capacity S_cap
+ *   x[i]       bf16 [B][Hkv][t_new][D]: loop i of the new positions (host array)
+ *   bits[i]    2 or 4 (host array)
+ *   ref_new    bf16 [B][Hkv][t_new][D]: the final loop of the new positions
+ *   pos        device int32 [B]: sequence b's new positions go to pos[b] + t,
+ *              t < t_new; a position outside [0, S_cap) is skipped (not written)
+ *   ref_cache  bf16 [B][Hkv][S_cap][D]: receives ref_new at those positions
+ *   codes[i], scales[i]  the cache's [B][Hkv][S_cap][...] code and scale tensors
+ * Codes and scales are those rq_encode gives for the same vectors. */
+int rq_encode_append(const rq_shape* cache, int32_t n_loops, int32_t t_new, const uint16_t* const* x,
+                     const int32_t* bits, const uint16_t* ref_new, const int32_t* pos, uint16_t* ref_cache,
+                     uint32_t* const* codes, uint16_t* const* scales, void* stream);
+
 /* Materialise one loop: out = ref + H (s * q) (ResidualQuant, newx.sg page,
  * Abstract: the residual format keeps reconstruction cheap).
  *   bits 0 copies ref. out_dtype RQ_OUT_F32 writes float [B][Hkv][S][D];
@@ -175,6 +197,30 @@ int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, co
                    const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
                    float softmax_scale, int32_t n_splits, float* out, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/* Decode attention over a partly filled residual cache, plus the positions
+ * not yet encoded: the serving-loop form of rq_decode_attn (paperaft JSON
+ * page, `summary`: decoding from the custom format in a serving stack).
+ * Sequence b attends to its first seq_lens[b] cached positions and then to
+ * tail_len positions per loop kept in bf16. In a looped model these are the
+ * current position's states of each loop, which can only be encoded once its
+ * final loop has run.
+ *   shape      the cache tensors; shape->seq_len is their capacity S_cap
+ *   seq_lens   device int32 [B], each in [0, S_cap] (values outside are clamped);
+ *              NULL means S_cap for every sequence
+ *   tail_len   0 (no tail) or the number of bf16 tail positions per sequence
+ *   tail_k[i], tail_v[i]  bf16 [B][Hkv][tail_len][D] for loop i (host arrays of
+ *              device pointers; ignored when tail_len = 0)
+ * A row with no position at all (seq_lens[b] = 0 and no tail) is all zeros.
+ * Other arguments, the output and the errors are as in rq_decode_attn. The
+ * workspace size comes from rq_decode_attn_varlen_workspace. */
+size_t rq_decode_attn_varlen_workspace(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops,
+                                       int32_t n_splits, int32_t tail_len);
+int rq_decode_attn_varlen(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                          const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
+                          const int32_t* seq_lens, int32_t tail_len, const uint16_t* const* tail_k,
+                          const uint16_t* const* tail_v, float softmax_scale, int32_t n_splits, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* The uncompressed baseline: the same decode attention where loop i attends
  * over its own bf16 K/V, k[i] and v[i] (host arrays of device pointers, each

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "LoopView", "RQError", "encode", "encode_into", "reconstruct", "decode_attn", "decode_attn_bf16",
-    "encode_rotonly", "reconstruct_rotonly",
+    "encode_rotonly", "reconstruct_rotonly", "encode_append", "decode_attn_varlen",
+    "decode_varlen_workspace_bytes",
     "decode_workspace_bytes", "decode_splits", "format_version", "library_path",
     "RQ_OK", "RQ_EINVAL", "RQ_EUNSUPPORTED", "RQ_EALIGN", "RQ_EWORKSPACE", "RQ_EHIP", "MAX_LOOPS",
 ]
@@ -75,6 +76,11 @@ def _load():
         "rq_encode": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, ctypes.POINTER(I32), P, PP, PP, P]),
         "rq_reconstruct": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, P, P, P, I32, P, P]),
         "rq_encode_refit": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, ctypes.POINTER(I32), P, PP, PP, I32, P]),
+        "rq_encode_append": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, PP, ctypes.POINTER(I32), P, P, P, PP,
+                                             PP, P]),
+        "rq_decode_attn_varlen_workspace": (SZ, [ctypes.POINTER(_Shape), I32, I32, I32, I32]),
+        "rq_decode_attn_varlen": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, P, P, ctypes.POINTER(_LoopView),
+                                                 P, I32, PP, PP, F, I32, P, P, SZ, P]),
         "rq_encode_rotonly": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, ctypes.POINTER(I32), PP, PP, P]),
         "rq_reconstruct_rotonly": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, P, P, I32, P, P]),
         "rq_decode_attn_splits": (I32, [ctypes.POINTER(_Shape), I32, I32, I32]),
@@ -280,20 +286,8 @@ def _workspace(ref, n_q_heads, n_loops, n_splits, workspace):
     return workspace
 
 
-def decode_attn(q: torch.Tensor, k_ref: torch.Tensor, v_ref: torch.Tensor, loops: Sequence[LoopView],
-                softmax_scale: Optional[float] = None, n_splits: int = 0, out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Fused reconstruct + single-query decode attention over the residual cache.
-    q: bf16 [n_loops, B, Hq, D]; returns float32 [n_loops, B, Hq, D]."""
-    lib = _load()
-    shp = _shape_of(k_ref)
+def _loop_views(loops, n_loops, k_ref):
     b, h, s, d = k_ref.shape
-    if q.dim() != 4:
-        raise ValueError("q must be [n_loops, batch, n_q_heads, head_dim]")
-    n_loops, _, hq, _ = q.shape
-    _need(q, "q", torch.bfloat16, (n_loops, b, hq, d), k_ref.device)
-    _need(k_ref, "k_ref", torch.bfloat16, k_ref.shape)
-    _need(v_ref, "v_ref", torch.bfloat16, k_ref.shape, k_ref.device)
     if len(loops) != n_loops:
         raise ValueError("one LoopView per loop of q")
     views = (_LoopView * n_loops)()
@@ -308,6 +302,101 @@ def decode_attn(q: torch.Tensor, k_ref: torch.Tensor, v_ref: torch.Tensor, loops
             views[i].k_scales = lv.k_scales.data_ptr()
             views[i].v_codes = lv.v_codes.data_ptr()
             views[i].v_scales = lv.v_scales.data_ptr()
+    return views
+
+
+def decode_varlen_workspace_bytes(batch: int, n_kv_heads: int, s_cap: int, head_dim: int, n_q_heads: int,
+                                  n_loops: int, n_splits: int = 0, tail_len: int = 0) -> int:
+    shp = _Shape(batch, n_kv_heads, s_cap, head_dim)
+    return _load().rq_decode_attn_varlen_workspace(ctypes.byref(shp), n_q_heads, n_loops, n_splits, tail_len)
+
+
+def decode_attn_varlen(q: torch.Tensor, k_ref: torch.Tensor, v_ref: torch.Tensor, loops: Sequence[LoopView],
+                       seq_lens: Optional[torch.Tensor] = None, tail_k: Optional[Sequence[torch.Tensor]] = None,
+                       tail_v: Optional[Sequence[torch.Tensor]] = None, softmax_scale: Optional[float] = None,
+                       n_splits: int = 0, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Decode over a partly filled cache [B, Hkv, S_cap, D]: sequence b attends to its first
+    seq_lens[b] positions (int32 device [B]; None = all) and then to the bf16 tail positions
+    tail_k[i] / tail_v[i] ([B, Hkv, T, D] per loop; None = no tail)."""
+    lib = _load()
+    shp = _shape_of(k_ref)
+    b, h, s, d = k_ref.shape
+    n_loops, _, hq, _ = q.shape
+    _need(q, "q", torch.bfloat16, (n_loops, b, hq, d), k_ref.device)
+    _need(k_ref, "k_ref", torch.bfloat16, k_ref.shape)
+    _need(v_ref, "v_ref", torch.bfloat16, k_ref.shape, k_ref.device)
+    views = _loop_views(loops, n_loops, k_ref)
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", torch.int32, (b,), k_ref.device)
+    tail_len = 0
+    tk = tv = None
+    if tail_k is not None or tail_v is not None:
+        if tail_k is None or tail_v is None or len(tail_k) != n_loops or len(tail_v) != n_loops:
+            raise ValueError("tail_k and tail_v need one bf16 [B, Hkv, T, D] tensor per loop")
+        tail_len = tail_k[0].shape[2]
+        for i in range(n_loops):
+            _need(tail_k[i], f"tail_k[{i}]", torch.bfloat16, (b, h, tail_len, d), k_ref.device)
+            _need(tail_v[i], f"tail_v[{i}]", torch.bfloat16, (b, h, tail_len, d), k_ref.device)
+        tk, tv = _ptr_array(tail_k), _ptr_array(tail_v)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((n_loops, b, hq, d), dtype=torch.float32, device=k_ref.device)
+    _need(out, "out", torch.float32, (n_loops, b, hq, d), k_ref.device)
+    need = decode_varlen_workspace_bytes(b, h, s, d, hq, n_loops, n_splits, tail_len)
+    if need == 0:
+        raise RQError(RQ_EINVAL, "decode workspace query")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k_ref.device)
+    st = lib.rq_decode_attn_varlen(ctypes.byref(shp), hq, n_loops, _ptr(q), _ptr(k_ref), _ptr(v_ref), views,
+                                   _ptr(seq_lens), int(tail_len), tk, tv, float(softmax_scale), int(n_splits),
+                                   _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(k_ref.device, stream))
+    _check(st, "rq_decode_attn_varlen")
+    return out
+
+
+def encode_append(xs: Sequence[torch.Tensor], ref_new: torch.Tensor, bits: Sequence[int], pos: torch.Tensor,
+                  ref_cache: torch.Tensor, codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
+                  stream=None) -> None:
+    """Encode new positions (xs[i], ref_new: bf16 [B, Hkv, T, D]) into a cache of capacity S_cap at
+    positions pos[b] + t (pos: int32 device [B]); ref_new is copied into ref_cache [B, Hkv, S_cap, D]."""
+    lib = _load()
+    b, h, t, d = ref_new.shape
+    _need(ref_new, "ref_new", torch.bfloat16, ref_new.shape)
+    _need(ref_cache, "ref_cache", torch.bfloat16, (b, h, ref_cache.shape[2], d), ref_new.device)
+    s_cap = ref_cache.shape[2]
+    _need(pos, "pos", torch.int32, (b,), ref_new.device)
+    n = len(xs)
+    if not (len(bits) == len(codes) == len(scales) == n):
+        raise ValueError("xs, bits, codes and scales must have one entry per loop")
+    for i in range(n):
+        _need(xs[i], f"xs[{i}]", torch.bfloat16, ref_new.shape, ref_new.device)
+        _need(codes[i], f"codes[{i}]", torch.int32, (b, h, s_cap, d * int(bits[i]) // 32), ref_new.device)
+        _need(scales[i], f"scales[{i}]", torch.float16, (b, h, s_cap, d // GROUP), ref_new.device)
+    shp = _Shape(b, h, s_cap, d)
+    bits_arr = (ctypes.c_int32 * n)(*[int(x) for x in bits])
+    st = lib.rq_encode_append(ctypes.byref(shp), n, t, _ptr_array(xs), bits_arr, _ptr(ref_new), _ptr(pos),
+                              _ptr(ref_cache), _ptr_array(codes), _ptr_array(scales), _stream(ref_new.device, stream))
+    _check(st, "rq_encode_append")
+
+
+def decode_attn(q: torch.Tensor, k_ref: torch.Tensor, v_ref: torch.Tensor, loops: Sequence[LoopView],
+                softmax_scale: Optional[float] = None, n_splits: int = 0, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Fused reconstruct + single-query decode attention over the residual cache.
+    q: bf16 [n_loops, B, Hq, D]; returns float32 [n_loops, B, Hq, D]."""
+    lib = _load()
+    shp = _shape_of(k_ref)
+    b, h, s, d = k_ref.shape
+    if q.dim() != 4:
+        raise ValueError("q must be [n_loops, batch, n_q_heads, head_dim]")
+    n_loops, _, hq, _ = q.shape
+    _need(q, "q", torch.bfloat16, (n_loops, b, hq, d), k_ref.device)
+    _need(k_ref, "k_ref", torch.bfloat16, k_ref.shape)
+    _need(v_ref, "v_ref", torch.bfloat16, k_ref.shape, k_ref.device)
+    views = _loop_views(loops, n_loops, k_ref)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
     if out is None:

@@ -92,6 +92,9 @@ void fill_common(DecodeArgs& a, const rq_shape* s, int32_t n_q_heads, const uint
   a.seq_len = s->seq_len;
   a.n_splits = p.n_splits;
   a.tokens_per_split = p.tokens_per_split;
+  a.rec_splits = p.n_splits;
+  a.split_base = 0;
+  a.seq_lens = nullptr;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 }
 
@@ -172,6 +175,43 @@ int rq_reconstruct(const rq_shape* shape, int32_t bits, const uint16_t* ref, con
   return reconstruct_common(shape, bits, ref, codes, scales, out_dtype, out, stream);
 }
 
+int rq_encode_append(const rq_shape* cache, int32_t n_loops, int32_t t_new, const uint16_t* const* x,
+                     const int32_t* bits, const uint16_t* ref_new, const int32_t* pos, uint16_t* ref_cache,
+                     uint32_t* const* codes, uint16_t* const* scales, void* stream) {
+  int st = check_shape(cache);
+  if (st != RQ_OK) return st;
+  if (n_loops < 1 || n_loops > kMaxLoops || t_new < 1) return RQ_EINVAL;
+  if (x == nullptr || bits == nullptr || ref_new == nullptr || pos == nullptr || ref_cache == nullptr ||
+      codes == nullptr || scales == nullptr)
+    return RQ_EINVAL;
+  for (int i = 0; i < n_loops; ++i) {
+    if (x[i] == nullptr || codes[i] == nullptr || scales[i] == nullptr) return RQ_EINVAL;
+  }
+  for (int i = 0; i < n_loops; ++i) {
+    if (bits[i] != 2 && bits[i] != 4) return RQ_EUNSUPPORTED;
+  }
+  if (!aligned16(ref_new) || !aligned16(ref_cache)) return RQ_EALIGN;
+  for (int i = 0; i < n_loops; ++i) {
+    if (!aligned16(x[i]) || !aligned16(codes[i]) || !aligned16(scales[i])) return RQ_EALIGN;
+  }
+  EncodeArgs a{};
+  for (int i = 0; i < n_loops; ++i) {
+    a.x[i] = x[i];
+    a.codes[i] = codes[i];
+    a.scales[i] = scales[i];
+    a.bits[i] = bits[i];
+  }
+  a.ref = ref_new;
+  a.n_loops = n_loops;
+  a.pos = pos;
+  a.t_new = t_new;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.s_cap = cache->seq_len;
+  a.ref_out = ref_cache;
+  a.n_vec = (int64_t)cache->batch * cache->n_kv_heads * t_new;
+  return hip_status(launch_encode(a, cache->head_dim, static_cast<hipStream_t>(stream)));
+}
+
 int rq_encode_rotonly(const rq_shape* shape, int32_t n_states, const uint16_t* const* x, const int32_t* bits,
                       uint32_t* const* codes, uint16_t* const* scales, void* stream) {
   return encode_common(shape, n_states, x, bits, nullptr, codes, scales, 0, stream);
@@ -193,14 +233,31 @@ size_t rq_decode_attn_workspace(const rq_shape* shape, int32_t n_q_heads, int32_
   return workspace_bytes_for(shape, n_q_heads, n_loops, plan_splits(shape, n_splits).n_splits);
 }
 
-int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
-                   const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
-                   float softmax_scale, int32_t n_splits, float* out, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The residual-cache decode. seq_lens (device [B], or NULL for all seq_len)
+// bounds each sequence's prefix; tail_len > 0 adds tail_len bf16 positions per
+// loop (tail_k / tail_v), merged as one more split.
+int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops, const int32_t* seq_lens,
+                int32_t tail_len, const uint16_t* const* tail_k, const uint16_t* const* tail_v,
+                float softmax_scale, int32_t n_splits, float* out, void* workspace, size_t workspace_bytes,
+                void* stream) {
   int st = check_heads(shape, n_q_heads, n_loops);
   if (st != RQ_OK) return st;
   if (q == nullptr || k_ref == nullptr || v_ref == nullptr || loops == nullptr || out == nullptr) return RQ_EINVAL;
-  if (n_splits < 0 || !isfinite(softmax_scale)) return RQ_EINVAL;
+  if (n_splits < 0 || !isfinite(softmax_scale) || tail_len < 0) return RQ_EINVAL;
+  if (tail_len > 0) {
+    if (tail_k == nullptr || tail_v == nullptr) return RQ_EINVAL;
+    for (int i = 0; i < n_loops; ++i) {
+      if (tail_k[i] == nullptr || tail_v[i] == nullptr) return RQ_EINVAL;
+    }
+    rq_shape ts = *shape;
+    ts.seq_len = tail_len;
+    if (check_heads(&ts, n_q_heads, n_loops) != RQ_OK) return RQ_EUNSUPPORTED;
+  }
   for (int i = 0; i < n_loops; ++i) {
     const rq_loop_view& lv = loops[i];
     if (lv.bits != 0 && lv.bits != 2 && lv.bits != 4) return RQ_EUNSUPPORTED;
@@ -215,14 +272,20 @@ int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, co
                          !aligned16(lv.v_scales)))
       return RQ_EALIGN;
   }
+  if (tail_len > 0) {
+    for (int i = 0; i < n_loops; ++i) {
+      if (!aligned16(tail_k[i]) || !aligned16(tail_v[i])) return RQ_EALIGN;
+    }
+  }
   const SplitPlan plan = plan_splits(shape, n_splits);
-  if (workspace == nullptr || workspace_bytes < workspace_bytes_for(shape, n_q_heads, n_loops, plan.n_splits))
+  const int32_t rec_splits = plan.n_splits + (tail_len > 0 ? 1 : 0);
+  if (workspace == nullptr || workspace_bytes < workspace_bytes_for(shape, n_q_heads, n_loops, rec_splits))
     return RQ_EWORKSPACE;
   if (!aligned16(workspace)) return RQ_EALIGN;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int G = n_q_heads / shape->n_kv_heads;
-  unsigned char* prep = static_cast<unsigned char*>(workspace) + partial_bytes(shape, n_q_heads, n_loops, plan.n_splits);
+  unsigned char* prep = static_cast<unsigned char*>(workspace) + partial_bytes(shape, n_q_heads, n_loops, rec_splits);
   bool any_residual = false;
   for (int i = 0; i < n_loops; ++i) any_residual = any_residual || loops[i].bits != 0;
   if (any_residual) {
@@ -251,6 +314,8 @@ int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, co
     if (nl == 0) nl = 1;  // G == 32: one loop per launch
     DecodeArgs a{};
     fill_common(a, shape, n_q_heads, q, softmax_scale, plan, workspace);
+    a.rec_splits = rec_splits;
+    a.seq_lens = seq_lens;
     a.qprep = prep;
     a.k[0] = k_ref;
     a.v[0] = v_ref;
@@ -281,8 +346,57 @@ int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, co
     if (st != RQ_OK) return st;
     base += nl;
   }
-  return run_combine(shape, n_q_heads, n_loops, plan.n_splits, static_cast<const float*>(workspace), out,
+  if (tail_len > 0) {
+    // the tail: plain bf16 positions of every loop, one more split per row
+    rq_shape ts = *shape;
+    ts.seq_len = tail_len;
+    const SplitPlan tp{1, (tail_len + kDecodeTile - 1) / kDecodeTile * kDecodeTile};
+    DecodeArgs a{};
+    fill_common(a, &ts, n_q_heads, q, softmax_scale, tp, workspace);
+    a.rec_splits = rec_splits;
+    a.split_base = plan.n_splits;
+    for (int i = 0; i < n_loops; ++i) {
+      a.k[i] = tail_k[i];
+      a.v[i] = tail_v[i];
+    }
+    a.loop_id[0] = 0;  // blockIdx.y selects the loop
+    a.n_loops_launch = 1;
+    a.n_rows = G;
+    a.zero_residual = any_residual;
+    st = hip_status(launch_decode_partial(a, shape->head_dim, n_loops, false, s));
+    if (st != RQ_OK) return st;
+  }
+  return run_combine(shape, n_q_heads, n_loops, rec_splits, static_cast<const float*>(workspace), out,
                      any_residual, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                   const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
+                   float softmax_scale, int32_t n_splits, float* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return decode_impl(shape, n_q_heads, n_loops, q, k_ref, v_ref, loops, nullptr, 0, nullptr, nullptr,
+                     softmax_scale, n_splits, out, workspace, workspace_bytes, stream);
+}
+
+size_t rq_decode_attn_varlen_workspace(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops,
+                                       int32_t n_splits, int32_t tail_len) {
+  if (check_heads(shape, n_q_heads, n_loops) != RQ_OK || n_splits < 0 || tail_len < 0) return 0;
+  return workspace_bytes_for(shape, n_q_heads, n_loops,
+                             plan_splits(shape, n_splits).n_splits + (tail_len > 0 ? 1 : 0));
+}
+
+int rq_decode_attn_varlen(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                          const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
+                          const int32_t* seq_lens, int32_t tail_len, const uint16_t* const* tail_k,
+                          const uint16_t* const* tail_v, float softmax_scale, int32_t n_splits, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (seq_lens != nullptr && !aligned16(seq_lens)) return RQ_EALIGN;
+  return decode_impl(shape, n_q_heads, n_loops, q, k_ref, v_ref, loops, seq_lens, tail_len, tail_k, tail_v,
+                     softmax_scale, n_splits, out, workspace, workspace_bytes, stream);
 }
 
 int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,

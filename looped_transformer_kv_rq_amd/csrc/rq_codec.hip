@@ -110,15 +110,27 @@ __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
   const int64_t stride = (int64_t)gridDim.x * kVecPerBlock;
   for (int64_t v = (int64_t)blockIdx.x * kVecPerBlock + threadIdx.x / kLanes; v < a.n_vec; v += stride) {
     const int64_t base = v * D + sub * PER;
+    // Output vector. Appending: source vector (row, t) of a [rows][t_new] batch
+    // goes to cache position pos[b] + t of row = b * Hkv + h; a position past the
+    // cache's capacity (or a negative one) writes nothing.
+    int64_t vo = v;
+    if (a.pos != nullptr) {
+      const int64_t row = v / a.t_new;
+      const int64_t p = (int64_t)a.pos[row / a.n_kv_heads] + v % a.t_new;
+      if (p < 0 || p >= a.s_cap) continue;  // uniform across the vector's lanes
+      vo = row * a.s_cap + p;
+    }
     // negated reference pair sums and differences (zero without a reference)
     float nrs[PER / 2], nrd[PER / 2];
 #pragma unroll
     for (int j = 0; j < PER / 2; ++j) nrs[j] = nrd[j] = 0.0f;
     if (a.ref != nullptr) {
       const uint4* rp = reinterpret_cast<const uint4*>(a.ref + base);
+      uint4* rcopy = a.ref_out != nullptr ? reinterpret_cast<uint4*>(a.ref_out + vo * D + sub * PER) : nullptr;
 #pragma unroll
       for (int i = 0; i < PER / 8; ++i) {
         const uint4 u = rp[i];
+        if (rcopy != nullptr) rcopy[i] = u;  // the final-loop state joins the reference cache
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -173,7 +185,7 @@ __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
           wd[2 * gi] = w2[0];
           wd[2 * gi + 1] = w2[1];
         }
-        uint32_t* dst = a.codes[l] + v * (D / 16) + sub * 2 * NGL;
+        uint32_t* dst = a.codes[l] + vo * (D / 16) + sub * 2 * NGL;
         if constexpr (NGL == 2) *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
         else *reinterpret_cast<uint2*>(dst) = make_uint2(wd[0], wd[1]);
       } else {
@@ -185,11 +197,11 @@ __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) wd[4 * gi + k] = w4[k];
         }
-        uint4* dst = reinterpret_cast<uint4*>(a.codes[l] + v * (D / 8) + sub * 4 * NGL);
+        uint4* dst = reinterpret_cast<uint4*>(a.codes[l] + vo * (D / 8) + sub * 4 * NGL);
 #pragma unroll
         for (int gi = 0; gi < NGL; ++gi) dst[gi] = make_uint4(wd[4 * gi], wd[4 * gi + 1], wd[4 * gi + 2], wd[4 * gi + 3]);
       }
-      uint16_t* sdst = a.scales[l] + v * (D / 32) + sub * NGL;
+      uint16_t* sdst = a.scales[l] + vo * (D / 32) + sub * NGL;
       if constexpr (NGL == 2) *reinterpret_cast<uint32_t*>(sdst) = (uint32_t)sc[0] | ((uint32_t)sc[1] << 16);
       else *sdst = sc[0];
     }

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void rq_combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int j = 0; j < DJ; ++j) o[j] = fmaf(r[j], RsqrtD<D>::v, o[j]);
   }
-  const float inv = 1.0f / lsum;
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;  // no position at all: a zero row
   float* dst = a.out + row * D;
 #pragma unroll
   for (int j = 0; j < DJ; ++j) dst[lane + 64 * j] = o[j] * inv;

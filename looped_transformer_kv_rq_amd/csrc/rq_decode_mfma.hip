@@ -703,7 +703,8 @@ void rq_decode_partial_mfma(DecodeArgs a) {
   }
 
   const int t_begin = split * a.tokens_per_split;
-  const int t_end = min(S, t_begin + a.tokens_per_split);
+  int t_end = min(S, t_begin + a.tokens_per_split);
+  if (a.seq_lens != nullptr) t_end = min(t_end, max(0, a.seq_lens[b]));  // this sequence's prefix
   const int tlast = t_end - 1;
   const uint16_t* kbase = a.k[z] + row_base * D;
   const uint16_t* vbase = a.v[z] + row_base * D;
@@ -777,7 +778,7 @@ void rq_decode_partial_mfma(DecodeArgs a) {
       if (pass == 1 && e >= D) continue;
       const int loop = a.loop_id[r / G] + z;
       const int hq = kvh * G + r % G;
-      float* dst = a.ws + ((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.n_splits + split) * REC + e0;
+      float* dst = a.ws + ((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.rec_splits + a.split_base + split) * REC + e0;
       const float* s0 = slots + r * SREC + (pass == 0 ? e : 2 + e);
       float val;
       if (pass == 0 && e == 0) {
@@ -799,7 +800,8 @@ void rq_decode_partial_mfma(DecodeArgs a) {
         const int r = i / D, e = i % D;
         const int loop = a.loop_id[r / G] + z;
         const int hq = kvh * G + r % G;
-        a.ws[((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.n_splits + split) * REC + D + 2 + e] = 0.0f;
+        a.ws[((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.rec_splits + a.split_base + split) * REC + D + 2 + e] =
+            0.0f;
       }
     }
   }

@@ -23,6 +23,12 @@ struct EncodeArgs {
   const uint16_t* ref;  // NULL: zero reference (rotation-only baseline)
   int32_t n_loops;
   int32_t refits;       // extra code / LS-scale alternations after the first fit
+  // appending (pos != NULL): sources are [B][Hkv][t_new][D], outputs go to cache
+  // position pos[b] + t of a [B][Hkv][s_cap] cache; ref_out receives the reference
+  const int32_t* pos;
+  int32_t t_new, n_kv_heads;
+  int64_t s_cap;
+  uint16_t* ref_out;
   int64_t n_vec;  // batch * n_kv_heads * seq_len
 };
 
@@ -57,6 +63,8 @@ struct DecodeArgs {
   int32_t group;                        // G = Hq / Hkv
   int32_t n_q_heads, n_kv_heads, batch, seq_len;
   int32_t n_splits, tokens_per_split;
+  int32_t rec_splits, split_base;       // records per row in the workspace; this launch's first split
+  const int32_t* seq_lens;              // device [B] prefix lengths, or NULL (all seq_len)
   float scale_log2;                     // softmax scale * log2(e)
   int32_t lds_wave_bytes;               // per-wave LDS stride (set by the launcher)
   int32_t zero_residual;                // write a zero residual accumulator (reference-only launch)

@@ -25,7 +25,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(rq.library_path())
     names = declared_functions()
-    assert {"rq_encode", "rq_reconstruct", "rq_encode_refit", "rq_encode_rotonly", "rq_reconstruct_rotonly", "rq_decode_attn",
+    assert {"rq_encode", "rq_reconstruct", "rq_encode_refit", "rq_encode_append", "rq_decode_attn_varlen",
+            "rq_decode_attn_varlen_workspace", "rq_encode_rotonly", "rq_reconstruct_rotonly", "rq_decode_attn",
             "rq_decode_attn_bf16",
             "rq_decode_attn_workspace", "rq_decode_attn_splits", "rq_status_str", "rq_format_version"} <= set(names)
     for n in names:
@@ -126,6 +127,37 @@ def test_rotonly_argument_checks():
     assert lib.rq_reconstruct_rotonly(sh, 2, FAKE, FAKE, 5, FAKE, None) == rq.RQ_EUNSUPPORTED
     assert lib.rq_reconstruct_rotonly(sh, 2, FAKE, FAKE, 0, FAKE + 4, None) == rq.RQ_EALIGN
     assert lib.rq_reconstruct(sh, 2, None, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EINVAL
+
+
+def test_append_and_varlen_argument_checks():
+    lib = rq._load()
+    sh = ctypes.byref(_shape(b=2, h=2, s=64, d=64))
+    bits = (ctypes.c_int32 * 1)(2)
+    x, c, s = _ptrs(FAKE), _ptrs(FAKE), _ptrs(FAKE)
+    ap = lib.rq_encode_append
+    assert ap(sh, 1, 0, x, bits, FAKE, FAKE, FAKE, c, s, None) == rq.RQ_EINVAL        # t_new = 0
+    assert ap(sh, 1, 1, x, bits, FAKE, None, FAKE, c, s, None) == rq.RQ_EINVAL        # no positions
+    assert ap(sh, 1, 1, x, bits, FAKE, FAKE, None, c, s, None) == rq.RQ_EINVAL        # no reference cache
+    assert ap(sh, 1, 1, x, (ctypes.c_int32 * 1)(0), FAKE, FAKE, FAKE, c, s, None) == rq.RQ_EUNSUPPORTED
+    assert ap(sh, 1, 1, x, bits, FAKE, FAKE, FAKE + 2, c, s, None) == rq.RQ_EALIGN
+    ws = lib.rq_decode_attn_varlen_workspace
+    assert ws(sh, 4, 2, 0, 1) > ws(sh, 4, 2, 0, 0) == lib.rq_decode_attn_workspace(sh, 4, 2, 0)
+    assert ws(sh, 4, 2, 0, -1) == 0
+    need = ws(sh, 4, 2, 0, 1)
+    views = (rq._LoopView * 2)()
+    views[0].bits, views[0].k_codes, views[0].k_scales, views[0].v_codes, views[0].v_scales = 2, FAKE, FAKE, FAKE, FAKE
+    tk = _ptrs(FAKE, FAKE)
+
+    def call(lens=FAKE, tail=1, tkk=tk, tvv=tk, wsb=need):
+        return lib.rq_decode_attn_varlen(sh, 4, 2, FAKE, FAKE, FAKE, views, lens, tail, tkk, tvv, 0.125, 0, FAKE,
+                                         FAKE, wsb, None)
+
+    assert call(tail=-1) == rq.RQ_EINVAL
+    assert call(tkk=None) == rq.RQ_EINVAL
+    assert call(tvv=_ptrs(FAKE, 0)) == rq.RQ_EINVAL
+    assert call(lens=FAKE + 4) == rq.RQ_EALIGN
+    assert call(tvv=_ptrs(FAKE, FAKE + 8)) == rq.RQ_EALIGN
+    assert call(wsb=need - 1) == rq.RQ_EWORKSPACE   # the tail's records need room
 
 
 def test_decode_argument_checks():
