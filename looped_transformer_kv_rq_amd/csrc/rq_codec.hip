@@ -101,7 +101,7 @@ __device__ __forceinline__ float quantize_group(const float* y, int refits, uint
 //    difference; the reference pair sums are formed once for all loops.
 //  * Butterflies on the remaining in-lane index bits stay in registers; those
 //    on the lane bits go across lanes inside a quad (DPP).
-template <int D, int PER, bool REFIT>
+template <int D, int PER, bool REFIT, bool APPEND>
 __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
   constexpr int kLanes = D / PER;  // lanes per vector
   constexpr int kVecPerBlock = 256 / kLanes;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
     // goes to cache position pos[b] + t of row = b * Hkv + h; a position past the
     // cache's capacity (or a negative one) writes nothing.
     int64_t vo = v;
-    if (a.pos != nullptr) {
+    if constexpr (APPEND) {
       const int64_t row = v / a.t_new;
       const int64_t p = (int64_t)a.pos[row / a.n_kv_heads] + v % a.t_new;
       if (p < 0 || p >= a.s_cap) continue;  // uniform across the vector's lanes
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
     for (int j = 0; j < PER / 2; ++j) nrs[j] = nrd[j] = 0.0f;
     if (a.ref != nullptr) {
       const uint4* rp = reinterpret_cast<const uint4*>(a.ref + base);
-      uint4* rcopy = a.ref_out != nullptr ? reinterpret_cast<uint4*>(a.ref_out + vo * D + sub * PER) : nullptr;
+      uint4* rcopy = APPEND ? reinterpret_cast<uint4*>(a.ref_out + vo * D + sub * PER) : nullptr;
 #pragma unroll
       for (int i = 0; i < PER / 8; ++i) {
         const uint4 u = rp[i];
@@ -282,8 +282,9 @@ template <int D>
 static void launch_encode_d(const EncodeArgs& a, hipStream_t stream) {
   constexpr int per = kEncodePer;
   const dim3 grid(grid_for(a.n_vec, 256 / (D / per)));
-  if (a.refits > 0) hipLaunchKernelGGL((rq_encode_kernel<D, per, true>), grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((rq_encode_kernel<D, per, false>), grid, dim3(256), 0, stream, a);
+  if (a.pos != nullptr) hipLaunchKernelGGL((rq_encode_kernel<D, per, false, true>), grid, dim3(256), 0, stream, a);
+  else if (a.refits > 0) hipLaunchKernelGGL((rq_encode_kernel<D, per, true, false>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((rq_encode_kernel<D, per, false, false>), grid, dim3(256), 0, stream, a);
 }
 
 hipError_t launch_encode(const EncodeArgs& a, int head_dim, hipStream_t stream) {
