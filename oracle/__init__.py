@@ -5,6 +5,7 @@ import this package; the GPU path shares no code with it.
 """
 from .rq_oracle import (  # noqa: F401
     GROUP,
+    WIDTHS,
     assign_codes,
     attention,
     bf16_to_f64,

@@ -29,9 +29,15 @@ The pages give no equations, so the details below are readings of them:
 * Scale s = <y, q> / <q, q>, the least-squares fit for fixed codes, stored as
   IEEE fp16 (round to nearest even, saturated at 65504). An all-zero group gets
   codes 2^(b-1) and s = 0.
-* Packing: word w of a vector holds elements [16w, 16w+16) for INT2 or
-  [8w, 8w+8) for INT4. Element j of the word sits at bits [2j, 2j+2) or
-  [4j, 4j+4).
+* Widths: INT2 and INT4 (Abstract), and INT3 and INT8 for a per-(layer, loop)
+  table (the AI Summary calls the mixed precision layer-wise, the Abstract
+  loop-wise; a table over both covers either reading).
+* Packing for b in {2, 4, 8}: word w of a vector holds elements
+  [(32/b) w, (32/b)(w+1)), element j of the word at bits [b j, b j + b).
+  INT3 codes are stored as two bit planes: the low two bits of every code in
+  the INT2 layout (D/16 words), then bit 2 of every code, one bit per
+  coordinate (D/32 words; element j of word w at bit j). No code crosses a
+  word boundary.
 * Reconstruction is x_hat = x_ref + H (s16 * q), using the stored fp16 scale.
 * Decode attention is exact softmax attention over all cached positions, with
   scale 1/sqrt(D). Query head h reads kv head floor(h / G).
@@ -93,8 +99,12 @@ def hadamard(d: int) -> np.ndarray:
 # one group: code assignment and least-squares scale
 # ----------------------------------------------------------------------------
 
+WIDTHS = (2, 3, 4, 8)
+
+
 def level_offset(bits: int) -> float:
-    """q = c - level_offset(bits): 1.5 for INT2, 7.5 for INT4."""
+    """q = c - level_offset(bits): 1.5 for INT2, 3.5 for INT3, 7.5 for INT4,
+    127.5 for INT8."""
     return 2.0 ** (bits - 1) - 0.5
 
 
@@ -166,7 +176,12 @@ def quantize_groups(y: np.ndarray, bits: int, refits: int = 0, steps=None):
 
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     """codes[..., D] (ints in [0, 2^b)) -> uint32 words [..., D*b/32].
-    Element j of word w is element (32/b)*w + j of the vector, at bits [b*j, b*j+b)."""
+    b in {1, 2, 4, 8}: element j of word w is element (32/b)*w + j of the
+    vector, at bits [b*j, b*j+b). b = 3: the INT2 words of the low two bits,
+    then the one-bit words of bit 2."""
+    if bits == 3:
+        codes = np.asarray(codes, dtype=np.int64)
+        return np.concatenate([pack_codes(codes & 3, 2), pack_codes(codes >> 2, 1)], axis=-1)
     codes = np.asarray(codes, dtype=np.uint64)
     per = 32 // bits
     d = codes.shape[-1]
@@ -176,6 +191,10 @@ def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
 
 
 def unpack_codes(words: np.ndarray, bits: int) -> np.ndarray:
+    if bits == 3:
+        words = np.asarray(words, dtype=np.uint32)
+        n2 = words.shape[-1] * 2 // 3  # INT2-plane words; the rest are bit-2 words
+        return unpack_codes(words[..., :n2], 2) | (unpack_codes(words[..., n2:], 1) << 2)
     words = np.asarray(words, dtype=np.uint32).astype(np.uint64)
     per = 32 // bits
     shifts = (np.arange(per, dtype=np.uint64) * np.uint64(bits))
@@ -201,8 +220,8 @@ def encode(x_bits, ref_bits, bits: int, group: int = GROUP, refits: int = 0):
     tests can quantize tiny groups; the storage format fixes 32. ``refits``
     adds that many code/scale alternations after the first fit.
     """
-    if bits not in (2, 4):
-        raise ValueError("residual width must be 2 or 4")
+    if bits not in WIDTHS:
+        raise ValueError("residual width must be 2, 3, 4 or 8")
     x = bf16_to_f64(x_bits)
     xr = bf16_to_f64(ref_bits)
     r = x - xr                                   # residual against the final loop

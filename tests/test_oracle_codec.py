@@ -24,9 +24,11 @@ def test_packing_worked_words(golden):
     assert oracle.pack_codes(np.arange(8)[None], 4)[0, 0] == p["int4_01234567"]
     assert oracle.pack_codes(np.full((1, 16), 2), 2)[0, 0] == p["int2_zero_group"]
     assert oracle.pack_codes(np.full((1, 8), 8), 4)[0, 0] == p["int4_zero_group"]
+    assert oracle.pack_codes(np.arange(4)[None], 8)[0, 0] == p["int8_0123"]
+    np.testing.assert_array_equal(oracle.pack_codes((np.arange(32) % 8)[None], 3)[0], p["int3_mod8"])
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_pack_round_trip(bits):
     c = np.random.default_rng(2).integers(0, 2 ** bits, size=(10, 128))
     w = oracle.pack_codes(c, bits)
@@ -43,6 +45,9 @@ def _x_bits(case):
     elif case["x_pattern"] == "plus_eighth_then_minus_eighth":
         x[: d // 2] = 0x3E00   # +0.125
         x[d // 2:] = 0xBE00    # -0.125
+    elif case["x_pattern"] == "minus_eighth_then_plus_eighth":
+        x[: d // 2] = 0xBE00
+        x[d // 2:] = 0x3E00
     return x
 
 
@@ -61,25 +66,30 @@ def test_golden_closed_forms(golden):
                 expect[int(k)] = v
             np.testing.assert_allclose(xh, expect, atol=1e-14, err_msg=case["name"])
         else:
+            # one nonzero rotated coordinate (peak_y) in group 1, group 0 all zero
+            e = case["sq_error"]
             s16 = oracle.f16_to_f64(np.array(case["scale_bits"][1:2], dtype=np.uint16))[0]
-            err2 = (1.5 * s16 - 1.0) ** 2 + 31 * (0.5 * s16) ** 2
+            err2 = (e["peak_level"] * s16 - e["peak_y"]) ** 2 + e["rest_count"] * (e["rest_level"] * s16) ** 2
             got = np.sum((xh - oracle.bf16_to_f64(x[0])) ** 2)
             assert abs(got - err2) < 1e-13
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("d", [64, 128])
 def test_zero_residual_reconstructs_exactly(bits, d):
     ref = workloads.f32_to_bf16_bits(np.random.default_rng(5).standard_normal((20, d)).astype(np.float32))
     words, scales = oracle.encode(ref, ref, bits)
-    zero_word = 0xAAAAAAAA if bits == 2 else 0x88888888
-    assert np.all(words == zero_word)
+    # every code is 2^(b-1): 0b10, 0b1000, 0x80; INT3 0b100 = low plane 0, bit 2 set
+    if bits == 3:
+        assert np.all(words[:, : d // 16] == 0) and np.all(words[:, d // 16:] == 0xFFFFFFFF)
+    else:
+        assert np.all(words == {2: 0xAAAAAAAA, 4: 0x88888888, 8: 0x80808080}[bits])
     assert np.all(scales == 0)
     xh = oracle.reconstruct(ref, words, scales, bits)
     np.testing.assert_array_equal(xh, oracle.bf16_to_f64(ref))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_error_equals_rotated_domain_error(bits):
     """|x_hat - x| = |s16 q - y| because H is orthogonal; the error splits over groups."""
     rng = np.random.default_rng(11)
@@ -110,6 +120,26 @@ def test_quality_on_gaussian_residuals():
     codes, s0 = oracle.assign_codes(y, 2)
     e_abs = np.linalg.norm(y - s0[..., None] * (codes - 1.5)) / np.linalg.norm(y)
     assert e_abs > errs[2] + 0.02
+
+
+def test_error_ordering_and_fine_grid_limit():
+    """On iid Gaussian residuals the error falls with every added bit, and at
+    INT8 it meets the fine-quantization limit: a uniform step D = m / 127.5
+    leaves an error of variance D^2 / 12 per coordinate, so the relative error
+    is sqrt(E[m^2] / (12 * 127.5^2)) with m the absmax of 32 unit Gaussians
+    (estimated here by sampling, without the codec)."""
+    rng = np.random.default_rng(13)
+    ref = workloads.f32_to_bf16_bits(rng.standard_normal((1000, 128)).astype(np.float32))
+    x = workloads.f32_to_bf16_bits((workloads.bf16_bits_to_f32(ref) + 0.2 * rng.standard_normal((1000, 128))).astype(np.float32))
+    y = oracle.rotate(oracle.bf16_to_f64(x) - oracle.bf16_to_f64(ref)).reshape(-1, 32)
+    errs = {}
+    for bits in (2, 3, 4, 8):
+        w, s = oracle.encode(x, ref, bits)
+        errs[bits] = oracle.reconstruction_error(oracle.reconstruct(ref, w, s, bits), x, ref)
+    assert errs[2] > errs[3] > errs[4] > errs[8]
+    m2 = np.mean(np.max(np.abs(y), axis=1) ** 2) / np.mean(y ** 2)
+    limit = np.sqrt(m2 / (12 * 127.5 ** 2))
+    assert abs(errs[8] / limit - 1.0) < 0.05, (errs[8], limit)
 
 
 def test_rotation_spreads_outlier_channels():

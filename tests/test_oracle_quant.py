@@ -17,9 +17,11 @@ def _levels(bits):
 def test_level_grids():
     np.testing.assert_array_equal(_levels(2), [-1.5, -0.5, 0.5, 1.5])
     np.testing.assert_array_equal(_levels(4), np.arange(-7.5, 8.0, 1.0))
+    np.testing.assert_array_equal(_levels(3), [-3.5, -2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 3.5])
+    np.testing.assert_array_equal(_levels(8), np.arange(-127.5, 128.0, 1.0))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_codes_are_nearest_level_per_element(bits):
     rng = np.random.default_rng(7)
     y = rng.standard_normal((400, 32)) * rng.uniform(0.01, 10, size=(400, 1))
@@ -32,7 +34,7 @@ def test_codes_are_nearest_level_per_element(bits):
     np.testing.assert_allclose(chosen, best, rtol=0, atol=1e-12 * np.abs(y).max())
 
 
-@pytest.mark.parametrize("bits,n", [(2, 1), (2, 3), (2, 6), (4, 2), (4, 3)])
+@pytest.mark.parametrize("bits,n", [(2, 1), (2, 3), (2, 6), (3, 2), (3, 4), (4, 2), (4, 3), (8, 1), (8, 2)])
 def test_joint_search_equals_separable_choice(bits, n):
     """Over all code vectors of a tiny group, the one closest to y at step s0
     is the per-element choice (the grid is separable)."""
@@ -59,9 +61,17 @@ def test_threshold_ties_and_extremes():
     y4 = np.array([[7.5, -7.5, 0.0, 3.0, -3.0, 2.5]])
     c4, _ = oracle.assign_codes(y4, 4)
     np.testing.assert_array_equal(c4[0], [15, 0, 8, 11, 5, 10])
+    # INT3: m = 3.5 -> s0 = 1, thresholds at -3..3
+    y3 = np.array([[3.5, -3.5, 0.0, 1.0, -1.0, -0.5, 2.99]])
+    c3, _ = oracle.assign_codes(y3, 3)
+    np.testing.assert_array_equal(c3[0], [7, 0, 4, 5, 3, 3, 6])
+    # INT8: m = 127.5 -> s0 = 1, thresholds at -127..127
+    y8 = np.array([[127.5, -127.5, 0.0, -0.25, 126.9, -127.0]])
+    c8, _ = oracle.assign_codes(y8, 8)
+    np.testing.assert_array_equal(c8[0], [255, 0, 128, 127, 254, 1])
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_ls_scale_is_the_least_squares_minimum(bits):
     rng = np.random.default_rng(3)
     for _ in range(30):
@@ -80,7 +90,7 @@ def test_ls_scale_is_the_least_squares_minimum(bits):
         assert s > 0
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_zero_group(bits):
     codes, s = oracle.quantize_groups(np.zeros((3, 32)), bits)
     assert np.all(codes == 2 ** (bits - 1))
@@ -102,7 +112,7 @@ def test_bf16_decoding_and_rounding():
     np.testing.assert_array_equal(oracle.f64_to_bf16(x), [0x3F80, 0x3F82, 0x3F81, 0xC020])
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_refits_never_raise_the_error_and_reach_a_fixed_point(bits):
     """Alternating the two least-squares half-steps (codes for a fixed scale,
     scale for fixed codes) cannot raise |y - s q|; after enough rounds the
@@ -131,9 +141,9 @@ def test_refit_assignment_is_nearest_level_at_the_step():
     """refit_codes picks, per element, the grid level closest to y at step s
     (brute force over all levels; ties at a threshold go up)."""
     rng = np.random.default_rng(5)
-    for bits in (2, 4):
+    for bits in (2, 3, 4, 8):
         y = rng.standard_normal((200, 32))
-        s = rng.uniform(0.2, 1.5, size=200)
+        s = rng.uniform(0.2, 1.5, size=200) / 2 ** (bits - 2)
         c = oracle.refit_codes(y, s, bits)
         lev = (np.arange(2 ** bits) - oracle.level_offset(bits))[None, None, :] * s[:, None, None]
         best = np.argmin(np.abs(y[..., None] - lev), axis=-1)
