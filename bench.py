@@ -473,6 +473,55 @@ def main():
             "bf16_bytes_per_token_head": 2 * 2 * w.head_dim * w.n_loops,
         }
 
+        # Per-(layer, loop) width table (rq_encode_layers, then each layer's
+        # decode with its row): LAYER_BITS_L4 over four layers that share the
+        # states above, so only the widths differ from layer to layer. Encode of
+        # K and V for all layers, decode per layer (cache flushed), and the
+        # residual-relative K error per (layer, loop).
+        if w.n_loops == len(workloads.LAYER_BITS_L4[0]):
+            table = workloads.LAYER_BITS_L4
+            lt = {}
+            n_lay = len(table)
+
+            def enc_layers():
+                lt["k"] = rq.encode_layers([[kx[l] for l in res_loops]] * n_lay, [kref] * n_lay,
+                                           [row[:-1] for row in table], stream=stream)
+                lt["v"] = rq.encode_layers([[vx[l] for l in res_loops]] * n_lay, [vref] * n_lay,
+                                           [row[:-1] for row in table], stream=stream)
+
+            lt_enc_ms = timed(enc_layers, max(5, args.reps // 2))
+            lt_enc_b = 2 * sum(encode_bytes(w, row[:-1]) for row in table)
+            layers = []
+            for li_, row in enumerate(table):
+                (lkc, lks), (lvc, lvs) = (lt["k"][0][li_], lt["k"][1][li_]), (lt["v"][0][li_], lt["v"][1][li_])
+                lviews = [rq.LoopView(bl, lkc[i], lks[i], lvc[i], lvs[i]) for i, bl in enumerate(row[:-1])]
+                lviews.append(rq.LoopView(0))
+
+                def dec_layer(lviews=lviews):
+                    rq.decode_attn(q, kref, vref, lviews, out=out, workspace=ws, stream=stream)
+
+                ms = timed(dec_layer, max(5, args.reps // 2))
+                gbps = decode_bytes(w, list(row)) / (ms * 1e-3) / 1e9
+                errs = []
+                for i, bl in enumerate(row[:-1]):
+                    xq = rq.reconstruct(kref, lkc[i], lks[i], bl, stream=stream)
+                    xl = kx[res_loops[i]].float()
+                    errs.append(torch.linalg.vector_norm(xq - xl).item() /
+                                torch.linalg.vector_norm(xl - kref.float()).item())
+                    del xq, xl
+                layers.append({"layer": li_, "bits": list(row), "decode_ms": ms, "decode_GBps": gbps,
+                               "decode_frac_peak": gbps / HBM_PEAK_GBPS,
+                               "kv_tokens_per_s": kv_tokens / (ms * 1e-3),
+                               "bytes_per_token_head": cache_bytes_per_token_head(w, list(row), True),
+                               "k_residual_rel_error_per_loop": errs})
+            result["layer_table"] = {
+                "table": [list(r) for r in table], "encode_all_layers_ms": lt_enc_ms,
+                "encode_GBps": lt_enc_b / (lt_enc_ms * 1e-3) / 1e9, "layers": layers,
+                "what": f"rq_encode_layers of K and V over {n_lay} layers sharing the {w.name} states, then "
+                        "rq_decode_attn per layer with its row of the table",
+            }
+            del lt
+
         # Serving step (rq_decode_attn_varlen + rq_encode_append): ragged prefix
         # lengths drawn in [S/2, S), every loop's current position as a one-position
         # bf16 tail, then that position appended to the K and V caches. Runs last:

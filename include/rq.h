@@ -5,7 +5,10 @@
  * Transformer like this: the final loop's K/V is kept as the reference, and
  * every earlier loop is kept only as a low-precision residual against it. The
  * residual is rotated and scaled by a least-squares fit. A loop-wise
- * mixed-precision table picks INT2 or INT4 per loop. The paperaft JSON page
+ * mixed-precision table picks INT2 or INT4 per loop. The AI Summary on the
+ * same page calls the mixed precision layer-wise instead; a table over
+ * (layer, loop) with the further widths INT3 and INT8 covers both readings
+ * (rq_encode_layers). The paperaft JSON page
  * (`summary`) adds that a serving stack must encode, decode and attend over
  * this custom format. This library provides exactly those operations:
  *
@@ -19,6 +22,8 @@
  *   rq_decode_attn_varlen  decode over per-sequence prefix lengths plus a bf16 tail
  *   rq_encode_rotonly / rq_reconstruct_rotonly  the rotation-only baseline:
  *                        the same codec without a reference
+ *   rq_encode_layers   rq_encode over several layers with a per-(layer, loop)
+ *                        bit-width table
  *
  * FORMAT (RQ_FORMAT_VERSION 1)
  *   Dense tensors are [batch][n_kv_heads][seq_len][head_dim], head_dim
@@ -29,12 +34,17 @@
  *   Codes: one pass at the absmax step s0 = max|y_g| / (2^(b-1) - 1/2):
  *   c = clamp(floor(y / s0) + 2^(b-1), 0, 2^b - 1). The level is
  *   q = c - (2^(b-1) - 1/2), so INT2 levels are {-1.5, -0.5, 0.5, 1.5}.
+ *   Widths: b in {2, 3, 4, 8}.
  *   Scale: s = <y_g, q_g> / <q_g, q_g>, stored as IEEE fp16 (round to nearest
  *   even, saturated at 65504). An all-zero group stores codes 2^(b-1) and
  *   s = 0, so a zero residual reconstructs the reference exactly.
- *   codes:  [batch][n_kv_heads][seq_len][head_dim*bits/32] uint32. Word w
- *           holds coordinates [(32/b)w, (32/b)(w+1)); coordinate j of the word
- *           sits at bits [b*j, b*j+b).
+ *   codes:  [batch][n_kv_heads][seq_len][head_dim*bits/32] uint32.
+ *           b = 2, 4, 8: word w holds coordinates [(32/b)w, (32/b)(w+1));
+ *           coordinate j of the word sits at bits [b*j, b*j+b).
+ *           b = 3: two bit planes, so no code crosses a word. Words
+ *           [0, head_dim/16) hold the low two bits of every code in the b = 2
+ *           layout; words [head_dim/16, 3*head_dim/32) hold bit 2 of every
+ *           code, coordinate j of word w at bit j.
  *   scales: [batch][n_kv_heads][seq_len][head_dim/32] fp16.
  *   Reconstruction: x_hat = x_ref + H (s * q).
  *
@@ -65,13 +75,14 @@ extern "C" {
 #define RQ_GROUP 32
 #define RQ_MAX_LOOPS 8
 #define RQ_MAX_REFITS 16
+#define RQ_MAX_LAYERS 4096
 
 typedef enum rq_status {
   RQ_OK = 0,
   RQ_EINVAL = -1,        /* null pointer, non-positive size, n_q_heads % n_kv_heads != 0,
                             n_loops outside [1, RQ_MAX_LOOPS], non-finite softmax scale */
-  RQ_EUNSUPPORTED = -2,  /* head_dim not in {64, 128}, bits not in {0, 2, 4} (not 0 for
-                            rq_encode), query heads per kv head above 32, bad out_dtype,
+  RQ_EUNSUPPORTED = -2,  /* head_dim not in {64, 128}, bits not in {0, 2, 3, 4, 8} (not 0
+                            for the encoders), query heads per kv head above 32, bad out_dtype,
                             decode with seq_len * head_dim * 2 above 2^31 - 1 bytes */
   RQ_EALIGN = -3,        /* a pointer is not 16-byte aligned */
   RQ_EWORKSPACE = -4,    /* workspace NULL or smaller than the size query returned */
@@ -89,7 +100,7 @@ typedef struct rq_shape {
 
 /* One loop of the cache as rq_decode_attn reads it. bits = 0 marks the final
    loop (the reference itself; code and scale pointers are ignored and may be
-   NULL). bits = 2 or 4 is a residual loop in the format above. */
+   NULL). bits = 2, 3, 4 or 8 is a residual loop in the format above. */
 typedef struct rq_loop_view {
   int32_t bits;
   const uint32_t* k_codes;
@@ -103,7 +114,7 @@ typedef struct rq_loop_view {
  * loops are stored as rotated, least-squares-scaled low-bit residuals).
  * The reference is read once for all loops.
  *   x[i]      bf16 [B][Hkv][S][D], loop i's states (host array of n_loops device pointers)
- *   bits[i]   2 or 4 (host array)
+ *   bits[i]   2, 3, 4 or 8 (host array)
  *   ref       bf16 [B][Hkv][S][D], the final loop
  *   codes[i]  out: uint32 [B][Hkv][S][D*bits[i]/32]
  *   scales[i] out: fp16  [B][Hkv][S][D/32]
@@ -134,7 +145,7 @@ int rq_encode_refit(const rq_shape* shape, int32_t n_loops, const uint16_t* cons
  * final-loop states into the bf16 reference cache.
  *   cache      shape of the cache tensors; cache->seq_len is their capacity S_cap
  *   x[i]       bf16 [B][Hkv][t_new][D]: loop i of the new positions (host array)
- *   bits[i]    2 or 4 (host array)
+ *   bits[i]    2, 3, 4 or 8 (host array)
  *   ref_new    bf16 [B][Hkv][t_new][D]: the final loop of the new positions
  *   pos        device int32 [B]: sequence b's new positions go to pos[b] + t,
  *              t < t_new; a position outside [0, S_cap) is skipped (not written)
@@ -158,7 +169,7 @@ int rq_reconstruct(const rq_shape* shape, int32_t bits, const uint16_t* ref, con
  * point the ResidualQuant page names (newx.sg page, Abstract: the residuals
  * are set against a rotation-based baseline at the same bit widths).
  *   x[i]      bf16 [B][Hkv][S][D] (host array of n_states device pointers)
- *   bits[i]   2 or 4 (host array)
+ *   bits[i]   2, 3, 4 or 8 (host array)
  *   codes[i], scales[i]  out, as in rq_encode
  * Codes and scales are those rq_encode gives for the same states against an
  * all-zero reference. Errors as rq_encode. */
@@ -166,10 +177,28 @@ int rq_encode_rotonly(const rq_shape* shape, int32_t n_states, const uint16_t* c
                       uint32_t* const* codes, uint16_t* const* scales, void* stream);
 
 /* Materialise one rotation-only state: out = H (s * q), the output of
- * rq_reconstruct with an all-zero reference. bits must be 2 or 4
+ * rq_reconstruct with an all-zero reference. bits must be 2, 3, 4 or 8
  * (RQ_EUNSUPPORTED otherwise); output types as rq_reconstruct. */
 int rq_reconstruct_rotonly(const rq_shape* shape, int32_t bits, const uint32_t* codes, const uint16_t* scales,
                            int32_t out_dtype, void* out, void* stream);
+
+/* Encode the residual caches of n_layers layers with a per-(layer, loop)
+ * bit-width table (ResidualQuant, newx.sg page: the Abstract calls the mixed
+ * precision loop-wise, the AI Summary layer-wise; a table over both holds
+ * either). Each layer has its own final-loop reference and n_loops earlier
+ * loops; the call is n_layers rq_encode calls on the stream, with every
+ * argument of every layer checked before the first launch. Decoding a layer
+ * takes that layer's row of the table as its loops' bits.
+ *   n_layers     1 .. RQ_MAX_LAYERS
+ *   x            host array [n_layers * n_loops] of device pointers, layer-major:
+ *                x[l * n_loops + i] is loop i of layer l, bf16 [B][Hkv][S][D]
+ *   bits_table   host array [n_layers * n_loops]: 2, 3, 4 or 8
+ *   ref          host array [n_layers]: layer l's final loop, bf16 [B][Hkv][S][D]
+ *   codes, scales  host arrays [n_layers * n_loops] of outputs, as in rq_encode
+ * All layers share `shape`. Errors as rq_encode. */
+int rq_encode_layers(const rq_shape* shape, int32_t n_layers, int32_t n_loops, const uint16_t* const* x,
+                     const int32_t* bits_table, const uint16_t* const* ref, uint32_t* const* codes,
+                     uint16_t* const* scales, void* stream);
 
 /* Split count rq_decode_attn / rq_decode_attn_bf16 will use for a request of
  * n_splits (0 = automatic). Host only. Returns <= 0 on invalid arguments. */

@@ -18,16 +18,19 @@ import torch
 
 __all__ = [
     "LoopView", "RQError", "encode", "encode_into", "reconstruct", "decode_attn", "decode_attn_bf16",
-    "encode_rotonly", "reconstruct_rotonly", "encode_append", "decode_attn_varlen",
+    "encode_rotonly", "reconstruct_rotonly", "encode_append", "decode_attn_varlen", "encode_layers",
     "decode_varlen_workspace_bytes",
     "decode_workspace_bytes", "decode_splits", "format_version", "library_path",
     "RQ_OK", "RQ_EINVAL", "RQ_EUNSUPPORTED", "RQ_EALIGN", "RQ_EWORKSPACE", "RQ_EHIP", "MAX_LOOPS",
+    "WIDTHS",
 ]
 
 RQ_OK, RQ_EINVAL, RQ_EUNSUPPORTED, RQ_EALIGN, RQ_EWORKSPACE, RQ_EHIP = 0, -1, -2, -3, -4, -5
 RQ_OUT_F32, RQ_OUT_BF16 = 0, 1
 MAX_LOOPS = 8
+MAX_LAYERS = 4096
 GROUP = 32
+WIDTHS = (2, 3, 4, 8)  # residual code widths
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "librq.so")
@@ -82,6 +85,8 @@ def _load():
         "rq_decode_attn_varlen": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, P, P, ctypes.POINTER(_LoopView),
                                                  P, I32, PP, PP, F, I32, P, P, SZ, P]),
         "rq_encode_rotonly": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, ctypes.POINTER(I32), PP, PP, P]),
+        "rq_encode_layers": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, PP, ctypes.POINTER(I32), PP, PP, PP,
+                                            P]),
         "rq_reconstruct_rotonly": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, P, P, I32, P, P]),
         "rq_decode_attn_splits": (I32, [ctypes.POINTER(_Shape), I32, I32, I32]),
         "rq_decode_attn_workspace": (SZ, [ctypes.POINTER(_Shape), I32, I32, I32]),
@@ -185,8 +190,8 @@ def encode(xs: Sequence[torch.Tensor], ref: torch.Tensor, bits: Sequence[int], s
         raise ValueError("ref must be [batch, n_kv_heads, seq_len, head_dim]")
     b, h, s, d = ref.shape
     for x in bits:
-        if int(x) not in (2, 4):
-            raise ValueError("encode bit widths must be 2 or 4")
+        if int(x) not in WIDTHS:
+            raise ValueError(f"encode bit widths must be in {WIDTHS}")
     codes = [torch.empty((b, h, s, d * int(x) // 32), dtype=torch.int32, device=ref.device) for x in bits]
     scales = [torch.empty((b, h, s, d // GROUP), dtype=torch.float16, device=ref.device) for _ in bits]
     encode_into(xs, ref, bits, codes, scales, stream, refits)
@@ -203,8 +208,8 @@ def encode_rotonly(xs: Sequence[torch.Tensor], bits: Sequence[int], stream=None)
     shp = _shape_of(x0)
     b, h, s, d = x0.shape
     for x in bits:
-        if int(x) not in (2, 4):
-            raise ValueError("bit widths must be 2 or 4")
+        if int(x) not in WIDTHS:
+            raise ValueError(f"bit widths must be in {WIDTHS}")
     codes = [torch.empty((b, h, s, d * int(x) // 32), dtype=torch.int32, device=x0.device) for x in bits]
     scales = [torch.empty((b, h, s, d // GROUP), dtype=torch.float16, device=x0.device) for _ in bits]
     for i, x in enumerate(xs):
@@ -221,8 +226,8 @@ def reconstruct_rotonly(codes: torch.Tensor, scales: torch.Tensor, bits: int, ou
                         out: Optional[torch.Tensor] = None, stream=None):
     """Rotation-only state: out = H (s * q)."""
     lib = _load()
-    if bits not in (2, 4):
-        raise ValueError("bits must be 2 or 4")
+    if bits not in WIDTHS:
+        raise ValueError(f"bits must be in {WIDTHS}")
     if codes.dim() != 4:
         raise ValueError("codes must be [batch, n_kv_heads, seq_len, head_dim*bits/32]")
     b, h, s, w = codes.shape
@@ -380,6 +385,40 @@ def encode_append(xs: Sequence[torch.Tensor], ref_new: torch.Tensor, bits: Seque
     st = lib.rq_encode_append(ctypes.byref(shp), n, t, _ptr_array(xs), bits_arr, _ptr(ref_new), _ptr(pos),
                               _ptr(ref_cache), _ptr_array(codes), _ptr_array(scales), _stream(ref_new.device, stream))
     _check(st, "rq_encode_append")
+
+
+def encode_layers(xs: Sequence[Sequence[torch.Tensor]], refs: Sequence[torch.Tensor],
+                  bits_table: Sequence[Sequence[int]], stream=None):
+    """Encode several layers' caches with a per-(layer, loop) bit table: xs[l][i] is loop i of
+    layer l and refs[l] its final loop (bf16 [B, Hkv, S, D], one shape for all layers);
+    bits_table[l][i] in WIDTHS. Returns (codes, scales) indexed [l][i] as encode()."""
+    lib = _load()
+    n_layers = len(refs)
+    if n_layers == 0 or len(xs) != n_layers or len(bits_table) != n_layers:
+        raise ValueError("xs, refs and bits_table must have one entry per layer")
+    n = len(xs[0])
+    if any(len(row) != n for row in xs) or any(len(row) != n for row in bits_table):
+        raise ValueError("every layer must have the same number of loops")
+    r0 = refs[0]
+    shp = _shape_of(r0)
+    b, h, s, d = r0.shape
+    codes, scales = [], []
+    for l in range(n_layers):
+        _need(refs[l], f"refs[{l}]", torch.bfloat16, r0.shape, r0.device)
+        for i in range(n):
+            if int(bits_table[l][i]) not in WIDTHS:
+                raise ValueError(f"bit widths must be in {WIDTHS}")
+            _need(xs[l][i], f"xs[{l}][{i}]", torch.bfloat16, r0.shape, r0.device)
+        codes.append([torch.empty((b, h, s, d * int(x) // 32), dtype=torch.int32, device=r0.device)
+                      for x in bits_table[l]])
+        scales.append([torch.empty((b, h, s, d // GROUP), dtype=torch.float16, device=r0.device)
+                       for _ in bits_table[l]])
+    flat = lambda rows: [t for row in rows for t in row]  # noqa: E731  (layer-major)
+    bits_arr = (ctypes.c_int32 * (n_layers * n))(*[int(x) for row in bits_table for x in row])
+    st = lib.rq_encode_layers(ctypes.byref(shp), n_layers, n, _ptr_array(flat(xs)), bits_arr, _ptr_array(refs),
+                              _ptr_array(flat(codes)), _ptr_array(flat(scales)), _stream(r0.device, stream))
+    _check(st, "rq_encode_layers")
+    return codes, scales
 
 
 def decode_attn(q: torch.Tensor, k_ref: torch.Tensor, v_ref: torch.Tensor, loops: Sequence[LoopView],

@@ -13,6 +13,9 @@ using namespace rq;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// residual code widths of the format: 2 and 4, and 3 and 8 for per-(layer, loop) tables
+bool residual_width(int32_t b) { return b == 2 || b == 3 || b == 4 || b == 8; }
+
 // RQ_OK, RQ_EINVAL or RQ_EUNSUPPORTED
 int check_shape(const rq_shape* s) {
   if (s == nullptr) return RQ_EINVAL;
@@ -98,11 +101,9 @@ void fill_common(DecodeArgs& a, const rq_shape* s, int32_t n_q_heads, const uint
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 }
 
-// Shared by rq_encode (ref = the final loop) and rq_encode_rotonly (ref = NULL:
-// a zero reference, so each state is quantized directly after the rotation).
-int encode_common(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
-                  const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, int32_t refits,
-                  void* stream) {
+// Argument checks of an encode (no HIP call).
+int encode_check(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
+                 const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, int32_t refits) {
   int st = check_shape(shape);
   if (st != RQ_OK) return st;
   if (n_loops < 1 || n_loops > kMaxLoops) return RQ_EINVAL;
@@ -112,12 +113,22 @@ int encode_common(const rq_shape* shape, int32_t n_loops, const uint16_t* const*
     if (x[i] == nullptr || codes[i] == nullptr || scales[i] == nullptr) return RQ_EINVAL;
   }
   for (int i = 0; i < n_loops; ++i) {
-    if (bits[i] != 2 && bits[i] != 4) return RQ_EUNSUPPORTED;
+    if (!residual_width(bits[i])) return RQ_EUNSUPPORTED;
   }
   if (ref != nullptr && !aligned16(ref)) return RQ_EALIGN;
   for (int i = 0; i < n_loops; ++i) {
     if (!aligned16(x[i]) || !aligned16(codes[i]) || !aligned16(scales[i])) return RQ_EALIGN;
   }
+  return RQ_OK;
+}
+
+// Shared by rq_encode (ref = the final loop) and rq_encode_rotonly (ref = NULL:
+// a zero reference, so each state is quantized directly after the rotation).
+int encode_common(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
+                  const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, int32_t refits,
+                  void* stream) {
+  const int st = encode_check(shape, n_loops, x, bits, ref, codes, scales, refits);
+  if (st != RQ_OK) return st;
   EncodeArgs a{};
   for (int i = 0; i < n_loops; ++i) {
     a.x[i] = x[i];
@@ -137,7 +148,7 @@ int reconstruct_common(const rq_shape* shape, int32_t bits, const uint16_t* ref,
   int st = check_shape(shape);
   if (st != RQ_OK) return st;
   if (out == nullptr) return RQ_EINVAL;
-  if (bits != 0 && bits != 2 && bits != 4) return RQ_EUNSUPPORTED;
+  if (bits != 0 && !residual_width(bits)) return RQ_EUNSUPPORTED;
   if (out_dtype != RQ_OUT_F32 && out_dtype != RQ_OUT_BF16) return RQ_EUNSUPPORTED;
   if (bits != 0 && (codes == nullptr || scales == nullptr)) return RQ_EINVAL;
   if ((ref != nullptr && !aligned16(ref)) || !aligned16(out)) return RQ_EALIGN;
@@ -188,7 +199,7 @@ int rq_encode_append(const rq_shape* cache, int32_t n_loops, int32_t t_new, cons
     if (x[i] == nullptr || codes[i] == nullptr || scales[i] == nullptr) return RQ_EINVAL;
   }
   for (int i = 0; i < n_loops; ++i) {
-    if (bits[i] != 2 && bits[i] != 4) return RQ_EUNSUPPORTED;
+    if (!residual_width(bits[i])) return RQ_EUNSUPPORTED;
   }
   if (!aligned16(ref_new) || !aligned16(ref_cache)) return RQ_EALIGN;
   for (int i = 0; i < n_loops; ++i) {
@@ -210,6 +221,26 @@ int rq_encode_append(const rq_shape* cache, int32_t n_loops, int32_t t_new, cons
   a.ref_out = ref_cache;
   a.n_vec = (int64_t)cache->batch * cache->n_kv_heads * t_new;
   return hip_status(launch_encode(a, cache->head_dim, static_cast<hipStream_t>(stream)));
+}
+
+int rq_encode_layers(const rq_shape* shape, int32_t n_layers, int32_t n_loops, const uint16_t* const* x,
+                     const int32_t* bits_table, const uint16_t* const* ref, uint32_t* const* codes,
+                     uint16_t* const* scales, void* stream) {
+  if (n_layers < 1 || n_layers > RQ_MAX_LAYERS || n_loops < 1 || n_loops > kMaxLoops) return RQ_EINVAL;
+  if (x == nullptr || bits_table == nullptr || ref == nullptr || codes == nullptr || scales == nullptr)
+    return RQ_EINVAL;
+  for (int l = 0; l < n_layers; ++l) {
+    if (ref[l] == nullptr) return RQ_EINVAL;
+    const int64_t o = (int64_t)l * n_loops;
+    const int st = encode_check(shape, n_loops, x + o, bits_table + o, ref[l], codes + o, scales + o, 0);
+    if (st != RQ_OK) return st;
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    const int64_t o = (int64_t)l * n_loops;
+    const int st = encode_common(shape, n_loops, x + o, bits_table + o, ref[l], codes + o, scales + o, 0, stream);
+    if (st != RQ_OK) return st;
+  }
+  return RQ_OK;
 }
 
 int rq_encode_rotonly(const rq_shape* shape, int32_t n_states, const uint16_t* const* x, const int32_t* bits,
@@ -260,7 +291,7 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
   }
   for (int i = 0; i < n_loops; ++i) {
     const rq_loop_view& lv = loops[i];
-    if (lv.bits != 0 && lv.bits != 2 && lv.bits != 4) return RQ_EUNSUPPORTED;
+    if (lv.bits != 0 && !residual_width(lv.bits)) return RQ_EUNSUPPORTED;
     if (lv.bits != 0 && (lv.k_codes == nullptr || lv.k_scales == nullptr || lv.v_codes == nullptr ||
                          lv.v_scales == nullptr))
       return RQ_EINVAL;
@@ -322,10 +353,10 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
     a.n_loops_launch = nl;
     a.n_rows = nl * G;
     bool residual = false;
-    // slots in the order INT4, INT2, reference-only: the kernel runs one
-    // branch-free loop per width
+    // slots in the order INT8, INT4, INT3, INT2, reference-only: the kernel
+    // runs one branch-free loop per width
     int li = 0;
-    for (const int want : {4, 2, 0}) {
+    for (const int want : {8, 4, 3, 2, 0}) {
       for (int j = 0; j < nl; ++j) {
         const rq_loop_view& lv = loops[base + j];
         if (lv.bits != want) continue;
@@ -335,7 +366,9 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
         a.ks[li] = lv.k_scales;
         a.vc[li] = lv.v_codes;
         a.vs[li] = lv.v_scales;
+        if (want == 8) ++a.n8;
         if (want == 4) ++a.n4;
+        if (want == 3) ++a.n3;
         if (want == 2) ++a.n2;
         residual = residual || lv.bits != 0;
         ++li;

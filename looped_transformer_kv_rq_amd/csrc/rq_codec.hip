@@ -2,7 +2,15 @@
 //
 // Encode (ResidualQuant, newx.sg page, Abstract): each earlier loop's K or V is
 // stored as a residual against the final loop. The residual is rotated, given
-// a least-squares scale per group and stored with 2 or 4 bits per coordinate.
+// a least-squares scale per group and stored with 2 or 4 bits per coordinate
+// (3 or 8 for a per-(layer, loop) table; AI Summary: layer-wise precision).
+//
+// Code words of one vector (W = D b / 32 of them):
+//  * b in {2, 4, 8}: word w holds coordinates [(32/b) w, (32/b)(w+1)), the
+//    coordinate j of the word at bits [b j, b j + b);
+//  * b = 3: two bit planes, so no code crosses a word. Words [0, D/16) hold
+//    the low two bits of every code in the INT2 layout, words [D/16, 3D/32)
+//    bit 2 of every code (coordinate j of word w at bit j).
 //
 // Work layout: a head_dim vector is handled by D/32 consecutive lanes, and
 // lane g holds coordinates [32g, 32g+32). The Walsh-Hadamard butterflies on
@@ -26,8 +34,20 @@ struct Grid {
   static constexpr int kHalf = 1 << (BITS - 1);      // code of level +1/2
   static constexpr int kTop = (1 << BITS) - 1;
   static constexpr float kOff = kHalf - 0.5f;         // level = code - kOff
-  static constexpr int kPerWord = 32 / BITS;          // codes per uint32
+  static constexpr int kPerWord = 32 / BITS;          // codes per uint32 (b = 2, 4, 8)
 };
+
+// Code of coordinate i (0..31) of a group from its BITS packed words (for
+// b = 3: the two INT2-plane words, then the bit-2 word).
+template <int BITS>
+__device__ __forceinline__ uint32_t group_code(const uint32_t (&words)[BITS], int i) {
+  if constexpr (BITS == 3) {
+    return ((words[i / 16] >> (2 * (i % 16))) & 3u) | (((words[2] >> i) & 1u) << 2);
+  } else {
+    using G = Grid<BITS>;
+    return (words[i / G::kPerWord] >> (BITS * (i % G::kPerWord))) & (uint32_t)G::kTop;
+  }
+}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -47,7 +67,8 @@ constexpr uint32_t kPairDiff = 0xBF803F80u;  // bf16 (+1, -1), low half first
 //    [0, 2^b - 1] and needs no clamp. An all-zero group takes 1 / s0 = 0,
 //    which gives every code 2^(b-1) and num = 0, so s = 0.
 //  * Packing sums c * 2^(b i) in fp32 over 16-bit halves of a word (exact:
-//    every partial sum is an integer below 2^16).
+//    every partial sum is an integer below 2^16). INT3 packs its two planes
+//    with integer shifts.
 //  * INT2: q^2 is 1/4 for the inner codes 1, 2 and 9/4 for 0, 3, so
 //    <q, q> = 72 - 2 * (number of inner codes), counted on the packed words.
 //  * refits > 0 alternates the two least-squares half-steps that many more
@@ -56,7 +77,7 @@ constexpr uint32_t kPairDiff = 0xBF803F80u;  // bf16 (+1, -1), low half first
 template <int BITS, int D, bool REFIT>
 __device__ __forceinline__ float quantize_group(const float* y, int refits, uint32_t (&words)[BITS]) {
   using G = Grid<BITS>;
-  constexpr int kPerHalf = G::kPerWord / 2;  // codes per 16-bit half word
+  constexpr int kPerHalf = BITS == 3 ? 1 : G::kPerWord / 2;  // codes per 16-bit half word
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(y[i]));
@@ -68,6 +89,7 @@ __device__ __forceinline__ float quantize_group(const float* y, int refits, uint
     float half[2 * BITS];
 #pragma unroll
     for (int k = 0; k < 2 * BITS; ++k) half[k] = 0.0f;
+    uint32_t plane[3] = {0u, 0u, 0u};  // INT3: low-bit words, bit-2 word
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       // (no clamp is needed at the absmax step; the refit steps clamp)
@@ -75,12 +97,23 @@ __device__ __forceinline__ float quantize_group(const float* y, int refits, uint
       if constexpr (REFIT) c = __builtin_amdgcn_fmed3f(c, 0.0f, (float)G::kTop);
       const float q = c - G::kOff;
       num = fmaf(y[i], q, num);
-      if constexpr (BITS == 4) den = fmaf(q, q, den);
-      half[i / kPerHalf] = fmaf(c, (float)(1u << (BITS * (i % kPerHalf))), half[i / kPerHalf]);
+      if constexpr (BITS != 2) den = fmaf(q, q, den);
+      if constexpr (BITS == 3) {
+        const uint32_t ci = (uint32_t)c;
+        plane[i / 16] |= (ci & 3u) << (2 * (i % 16));
+        plane[2] |= (ci >> 2) << i;
+      } else {
+        half[i / kPerHalf] = fmaf(c, (float)(1u << (BITS * (i % kPerHalf))), half[i / kPerHalf]);
+      }
     }
+    if constexpr (BITS == 3) {
 #pragma unroll
-    for (int k = 0; k < BITS; ++k)
-      words[k] = (uint32_t)half[2 * k] | ((uint32_t)half[2 * k + 1] << 16);
+      for (int k = 0; k < 3; ++k) words[k] = plane[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < BITS; ++k)
+        words[k] = (uint32_t)half[2 * k] | ((uint32_t)half[2 * k + 1] << 16);
+    }
     if constexpr (BITS == 2) {
       int inner = 0;
 #pragma unroll
@@ -101,7 +134,9 @@ __device__ __forceinline__ float quantize_group(const float* y, int refits, uint
 //    difference; the reference pair sums are formed once for all loops.
 //  * Butterflies on the remaining in-lane index bits stay in registers; those
 //    on the lane bits go across lanes inside a quad (DPP).
-template <int D, int PER, bool REFIT, bool APPEND>
+//  * WIDE instantiations also take INT3 and INT8 loops; the INT2/INT4-only
+//    ones carry no code for them.
+template <int D, int PER, bool REFIT, bool APPEND, bool WIDE>
 __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
   constexpr int kLanes = D / PER;  // lanes per vector
   constexpr int kVecPerBlock = 256 / kLanes;
@@ -188,6 +223,26 @@ __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
         uint32_t* dst = a.codes[l] + vo * (D / 16) + sub * 2 * NGL;
         if constexpr (NGL == 2) *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
         else *reinterpret_cast<uint2*>(dst) = make_uint2(wd[0], wd[1]);
+      } else if (WIDE && bits == 3) {
+        // low-bit plane at word 2g of the vector, bit-2 plane at word D/16 + g
+        uint32_t* vec = a.codes[l] + vo * (3 * D / 32);
+#pragma unroll
+        for (int gi = 0; gi < NGL; ++gi) {
+          uint32_t w3[3];
+          sc[gi] = f32_to_f16_sat(quantize_group<3, D, REFIT>(y + 32 * gi, a.refits, w3));
+          const int grp = sub * NGL + gi;
+          *reinterpret_cast<uint2*>(vec + 2 * grp) = make_uint2(w3[0], w3[1]);
+          vec[D / 16 + grp] = w3[2];
+        }
+      } else if (WIDE && bits == 8) {
+        uint4* dst = reinterpret_cast<uint4*>(a.codes[l] + vo * (D / 4) + sub * 8 * NGL);
+#pragma unroll
+        for (int gi = 0; gi < NGL; ++gi) {
+          uint32_t w8[8];
+          sc[gi] = f32_to_f16_sat(quantize_group<8, D, REFIT>(y + 32 * gi, a.refits, w8));
+          dst[2 * gi] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+          dst[2 * gi + 1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+        }
       } else {
         uint32_t wd[4 * NGL];
 #pragma unroll
@@ -226,21 +281,24 @@ __global__ __launch_bounds__(256) void rq_reconstruct_kernel(ReconstructArgs a) 
     if constexpr (BITS != 0) {
       using G = Grid<BITS>;
       const float s = f16_bits_to_f32(a.scales[v * (D / 32) + g]) * RsqrtD<D>::v;
-      const uint32_t* src = a.codes + v * (D * BITS / 32) + g * BITS;
+      const uint32_t* vec = a.codes + v * (D * BITS / 32);
       uint32_t words[BITS];
       if constexpr (BITS == 2) {
-        const uint2 w = *reinterpret_cast<const uint2*>(src);
+        const uint2 w = *reinterpret_cast<const uint2*>(vec + 2 * g);
         words[0] = w.x; words[1] = w.y;
+      } else if constexpr (BITS == 3) {
+        const uint2 w = *reinterpret_cast<const uint2*>(vec + 2 * g);
+        words[0] = w.x; words[1] = w.y; words[2] = vec[D / 16 + g];
       } else {
-        const uint4 w = *reinterpret_cast<const uint4*>(src);
-        words[0] = w.x; words[1] = w.y; words[2] = w.z; words[3] = w.w;
+#pragma unroll
+        for (int k = 0; k < BITS / 4; ++k) {
+          const uint4 w = *reinterpret_cast<const uint4*>(vec + BITS * g + 4 * k);
+          words[4 * k] = w.x; words[4 * k + 1] = w.y; words[4 * k + 2] = w.z; words[4 * k + 3] = w.w;
+        }
       }
       float z[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const uint32_t c = (words[i / G::kPerWord] >> (BITS * (i % G::kPerWord))) & (uint32_t)G::kTop;
-        z[i] = s * ((float)c - G::kOff);
-      }
+      for (int i = 0; i < 32; ++i) z[i] = s * ((float)group_code<BITS>(words, i) - G::kOff);
       fwht_groups<D>(z, g);
 #pragma unroll
       for (int i = 0; i < 32; ++i) x[i] += z[i];
@@ -278,13 +336,24 @@ static unsigned grid_for(int64_t n_vec, int vec_per_block) {
 // registers) and runs slower.
 constexpr int kEncodePer = 32;
 
-template <int D>
-static void launch_encode_d(const EncodeArgs& a, hipStream_t stream) {
+template <int D, bool WIDE>
+static void launch_encode_dw(const EncodeArgs& a, hipStream_t stream) {
   constexpr int per = kEncodePer;
   const dim3 grid(grid_for(a.n_vec, 256 / (D / per)));
-  if (a.pos != nullptr) hipLaunchKernelGGL((rq_encode_kernel<D, per, false, true>), grid, dim3(256), 0, stream, a);
-  else if (a.refits > 0) hipLaunchKernelGGL((rq_encode_kernel<D, per, true, false>), grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((rq_encode_kernel<D, per, false, false>), grid, dim3(256), 0, stream, a);
+  if (a.pos != nullptr)
+    hipLaunchKernelGGL((rq_encode_kernel<D, per, false, true, WIDE>), grid, dim3(256), 0, stream, a);
+  else if (a.refits > 0)
+    hipLaunchKernelGGL((rq_encode_kernel<D, per, true, false, WIDE>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((rq_encode_kernel<D, per, false, false, WIDE>), grid, dim3(256), 0, stream, a);
+}
+
+template <int D>
+static void launch_encode_d(const EncodeArgs& a, hipStream_t stream) {
+  bool wide = false;
+  for (int l = 0; l < a.n_loops; ++l) wide = wide || a.bits[l] == 3 || a.bits[l] == 8;
+  if (wide) launch_encode_dw<D, true>(a, stream);
+  else launch_encode_dw<D, false>(a, stream);
 }
 
 hipError_t launch_encode(const EncodeArgs& a, int head_dim, hipStream_t stream) {
@@ -301,8 +370,12 @@ static void launch_reconstruct_d(const ReconstructArgs& a, int bits, int out_bf1
     if (out_bf16) RQ_RECON(0, true); else RQ_RECON(0, false);
   } else if (bits == 2) {
     if (out_bf16) RQ_RECON(2, true); else RQ_RECON(2, false);
-  } else {
+  } else if (bits == 3) {
+    if (out_bf16) RQ_RECON(3, true); else RQ_RECON(3, false);
+  } else if (bits == 4) {
     if (out_bf16) RQ_RECON(4, true); else RQ_RECON(4, false);
+  } else {
+    if (out_bf16) RQ_RECON(8, true); else RQ_RECON(8, false);
   }
 #undef RQ_RECON
 }

@@ -2,7 +2,8 @@
 //
 // ResidualQuant (newx.sg page, Abstract): an earlier loop's K/V is the bf16
 // final-loop reference plus a rotated INT2/INT4 residual with a least-squares
-// fp16 scale per 32 coordinates. One call attends every loop's queries over
+// fp16 scale per 32 coordinates (INT3/INT8 too for a per-(layer, loop) table,
+// AI Summary). One call attends every loop's queries over
 // the cache and streams the reference once for all of them. The rotation H
 // (normalised Walsh-Hadamard) is symmetric, so
 //   score  = q . k_ref + (H q) . (s * lev)
@@ -25,8 +26,9 @@
 //    halves (error ~2^-16), and V^T is read from the LDS tile;
 //  * residual PV, O_res^T += lev^T (P s)^T (fp16). Levels decode exactly
 //    through a v_perm byte table (INT2: {-1.5,-0.5,0.5,1.5}; INT4 as
-//    4 lev_hi + lev_lo). Rows of other loops carry P s = 0, so every loop
-//    shares one accumulator.
+//    4 lev_hi + lev_lo; INT3 from an eight-entry table). INT8 levels are
+//    formed as 2 lev = (1024 + 2c) - 1279 in fp16 against P s / 2. Rows of
+//    other loops carry P s = 0, so every loop shares one accumulator.
 // The MFMA output layout (lane l holds rows 4 (l / 16) + i of column l % 16)
 // gives each lane one query row and four tokens per 16-token block. The
 // softmax statistics of a row therefore stay within the row's four lanes,
@@ -111,6 +113,8 @@ __device__ __forceinline__ void wave_sync_lds() {
 
 constexpr uint32_t kLutInt2 = 0x3E38B8BEu;    // fp16 high bytes of -1.5, -0.5, 0.5, 1.5
 constexpr uint32_t kLutInt4Hi = 0x4640C0C6u;  // fp16 high bytes of -6, -2, 2, 6 (4 * INT2 level)
+constexpr uint32_t kLutInt3Lo = 0xB8BEC1C3u;  // fp16 high bytes of -3.5, -2.5, -1.5, -0.5
+constexpr uint32_t kLutInt3Hi = 0x43413E38u;  // fp16 high bytes of 0.5, 1.5, 2.5, 3.5
 constexpr int kTile = 32;
 constexpr int kTile16 = 16;  // tokens per MFMA row block
 
@@ -137,11 +141,26 @@ __host__ __device__ constexpr int loop_lds_bytes(int d, int bits) {
 }
 
 // LDS offset of residual slot li's tile data inside a wave's buffer: the V
-// tile, then the INT4 slots, then the INT2 slots.
-template <int D>
+// tile, then the slots in the launcher's order INT8, INT4, INT3, INT2.
+template <int D, bool WIDE>
 __device__ __forceinline__ int slot_lds_offset(const DecodeArgs& a, int li) {
   constexpr int L4 = loop_lds_bytes(D, 4), L2 = loop_lds_bytes(D, 2);
-  return MfmaGeom<D>::VT_BYTES + (li < a.n4 ? li * L4 : a.n4 * L4 + (li - a.n4) * L2);
+  if constexpr (!WIDE) {
+    return MfmaGeom<D>::VT_BYTES + (li < a.n4 ? li * L4 : a.n4 * L4 + (li - a.n4) * L2);
+  } else {
+    constexpr int L8 = loop_lds_bytes(D, 8), L3 = loop_lds_bytes(D, 3);
+    int off = MfmaGeom<D>::VT_BYTES;
+    int k = min(li, a.n8);
+    off += k * L8;
+    li -= k;
+    k = min(li, a.n4);
+    off += k * L4;
+    li -= k;
+    k = min(li, a.n3);
+    off += k * L3;
+    li -= k;
+    return off + li * L2;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -208,7 +227,8 @@ __global__ __launch_bounds__(256) void rq_query_prep(QueryPrepArgs a) {
   if (lane < NG) {
     float s = 0.0f;
     for (int d = 0; d < 32; ++d) s += buf[wave][32 * lane + d];
-    const float off = bits == 4 ? 23.5f : 5.5f;
+    // 2^b + 2^(b-1) - 1/2 (unused for a reference-only loop)
+    const float off = bits > 0 ? (float)(1 << bits) + (float)(1 << (bits - 1)) - 0.5f : 0.0f;
     reinterpret_cast<float*>(rec + 2 * D)[lane] = -off * s;
   }
 }
@@ -250,13 +270,25 @@ __device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned
     for (int i = 0; i < W / 2; ++i) bdma4(vc_r, vc_lane, tc + 8 * i, vc_l + 256 * i);
     return;
   }
-  // K code words in 16-byte chunks: chunk c -> token c / (W/4), words 4 (c % (W/4))
+  if constexpr (W % 4 == 0) {
+    // K code words in 16-byte chunks: chunk c -> token c / (W/4), words 4 (c % (W/4))
 #pragma unroll
-  for (int i = 0; i * 64 < 8 * W; ++i) {
-    const int c = 64 * i + lane;
-    if (8 * W >= 64 * (i + 1) || c < 8 * W) {
-      const int tok = c / (W / 4), q4 = c % (W / 4);
-      dma16(a.kc[li] + (row_base + min(t0 + tok, tlast)) * W + 4 * q4, kc_l + 1024 * i);
+    for (int i = 0; i * 64 < 8 * W; ++i) {
+      const int c = 64 * i + lane;
+      if (8 * W >= 64 * (i + 1) || c < 8 * W) {
+        const int tok = c / (W / 4), q4 = c % (W / 4);
+        dma16(a.kc[li] + (row_base + min(t0 + tok, tlast)) * W + 4 * q4, kc_l + 1024 * i);
+      }
+    }
+  } else {
+    // (INT3 at D = 64: 6 words per token) one word per lane: word idx -> token idx / W
+#pragma unroll
+    for (int i = 0; i * 64 < 32 * W; ++i) {
+      const int idx = 64 * i + lane;
+      if (32 * W >= 64 * (i + 1) || idx < 32 * W) {
+        const int tok = idx / W, wd = idx % W;
+        dma4(a.kc[li] + (row_base + min(t0 + tok, tlast)) * W + wd, kc_l + 256 * i);
+      }
     }
   }
   // scales, 4 bytes per lane: lane -> token lane / (NG/2), pair lane % (NG/2)
@@ -281,10 +313,15 @@ struct Consts {
   uint32_t m4;    // 0x03C003C0: INT4 field at bits 6-9 of each half
   uint32_t one;   // 0x3C003C00: fp16 1.0 in both halves
   uint32_t sel0;  // 0x000C000C: v_perm "zero byte" in bytes 0 and 2
+  uint32_t m3lo;  // 0x01800180: INT3 low bits at bits 7-8 of each half
+  uint32_t m3hi;  // 0x02000200: INT3 bit 2 at bit 9 of each half
+  uint32_t m3s;   // 0x04000400: INT3 bit 2 at bit 2 of table-index bytes 1 and 3
 };
+template <bool WIDE>
 __device__ __forceinline__ Consts make_consts() {
-  Consts c{0x03000300u, 0x03C003C0u, 0x3C003C00u, 0x000C000Cu};
+  Consts c{0x03000300u, 0x03C003C0u, 0x3C003C00u, 0x000C000Cu, 0x01800180u, 0x02000200u, 0x04000400u};
   asm volatile("" : "+v"(c.m2), "+v"(c.m4), "+v"(c.one), "+v"(c.sel0));
+  if constexpr (WIDE) asm volatile("" : "+v"(c.m3lo), "+v"(c.m3hi), "+v"(c.m3s));
   return c;
 }
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) { return (x & m) | o; }
@@ -334,6 +371,38 @@ __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, con
         kx[ks].y = and_or(w >> 2, k.m2, k.one);
         kx[ks].z = and_or(w >> 4, k.m2, k.one);
         kx[ks].w = and_or(w >> 6, k.m2, k.one);
+      }
+    } else if constexpr (BITS == 8) {
+      // element 2i <- byte i of word 8ks + 4(g>>1) + (g&1), element 2i+1 <- byte i of the word
+      // two later. One v_perm puts both bytes at bytes 0 and 2; shifted up by 2 and or-ed into
+      // 1.0 they give the fp16 values 1 + c/256.
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(cw);
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) {
+        const uint32_t wa = row[8 * ks + 4 * (g >> 1) + (g & 1)];
+        const uint32_t wb = row[8 * ks + 4 * (g >> 1) + (g & 1) + 2];
+        kx[ks].x = (vperm(wb, wa, 0x0C040C00u) << 2) | k.one;
+        kx[ks].y = (vperm(wb, wa, 0x0C050C01u) << 2) | k.one;
+        kx[ks].z = (vperm(wb, wa, 0x0C060C02u) << 2) | k.one;
+        kx[ks].w = (vperm(wb, wa, 0x0C070C03u) << 2) | k.one;
+      }
+    } else if constexpr (BITS == 3) {
+      // The low two bits as in INT2 (plane words 2ks + (g>>1)), one bit lower: bits 7-8. Bit 2
+      // comes from byte 2(g>>1) (element 2i) and byte 2(g>>1)+1 (element 2i+1) of the group's
+      // bit-plane word, bit 4(g&1) + i of each, moved to bit 9. The fp16 values are 1 + c/8.
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(cw);
+      const uint32_t pre = (g & 1) ? 0u : 8u;
+      const uint32_t hsel = (uint32_t)(2 * (g >> 1)) | 0x0C000C00u | ((uint32_t)(2 * (g >> 1) + 1) << 16);
+      const uint32_t hsh = 9u - 4u * (uint32_t)(g & 1);
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) {
+        const uint32_t w = row[2 * ks + (g >> 1)] << pre;
+        const uint32_t hb = row[D / 16 + ks];
+        const uint32_t t = vperm(hb, hb, hsel) << hsh;
+        kx[ks].x = and_or(t, k.m3hi, and_or(w >> 1, k.m3lo, k.one));
+        kx[ks].y = and_or(t >> 1, k.m3hi, and_or(w >> 3, k.m3lo, k.one));
+        kx[ks].z = and_or(t >> 2, k.m3hi, and_or(w >> 5, k.m3lo, k.one));
+        kx[ks].w = and_or(t >> 3, k.m3hi, and_or(w >> 7, k.m3lo, k.one));
       }
     } else {
       // element 2i <- nibble 4(g&1) + i of word 4ks + 2(g>>1), element 2i+1 <- same nibble of
@@ -412,22 +481,29 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
     }
   }
   // A rows: coordinate 32grp + 16hf + m. Its code sits in byte `cb` of word
-  // wv (INT2: byte m/4 of word 2grp + hf; INT4: byte (m%8)/2 of word
-  // 4grp + 2hf + m/8), `sh` bits up.
+  // wv (INT2 and the INT3 low plane: byte m/4 of word 2grp + hf; INT4: byte
+  // (m%8)/2 of word 4grp + 2hf + m/8; INT8: byte m%4 of word 8grp + 4hf +
+  // m/4), `sh` bits up.
   uint32_t selx;
   uint32_t sh;
-  if constexpr (BITS == 2) {
+  if constexpr (BITS == 2 || BITS == 3) {
     selx = ((uint32_t)(m >> 2) << 8) | ((uint32_t)(4 + (m >> 2)) << 24);
     sh = 2u * (uint32_t)(m & 3);
+  } else if constexpr (BITS == 8) {
+    selx = (uint32_t)(m & 3) | 0x0C000C00u | ((uint32_t)(4 + (m & 3)) << 16);  // bytes 0 and 2
+    sh = 0u;
   } else {
     const int f = m & 7;
     selx = ((uint32_t)(f >> 1) << 8) | ((uint32_t)(4 + (f >> 1)) << 24);
     sh = 4u * (uint32_t)(f & 1);
   }
+  // INT3 bit 2 of coordinate 16hf + m: byte 2hf + m/8 of the bit-plane word, moved to bit 10
+  const uint32_t hsh = 10u - (uint32_t)(m & 7);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     if (li * G >= 16 * nb + 16 || li * G + G <= 16 * nb) continue;
-    const float mem = my_loop[nb] == li ? 1.0f : 0.0f;
+    // INT8 levels enter doubled (2c - 255), so P carries the factor 1/2
+    const float mem = my_loop[nb] == li ? (BITS == 8 ? 0.5f : 1.0f) : 0.0f;
     uint32_t p16[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p16[i] = pack_rtz(p[nb][2 * i] * mem, p[nb][2 * i + 1] * mem);
@@ -441,7 +517,21 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
       bop.w = mul_f16x2(p16[3], vperm(vsw[7][grp >> 1], vsw[6][grp >> 1], hsel));
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int wv = BITS == 2 ? 2 * grp + hf : 4 * grp + 2 * hf + (m >> 3);
+        if constexpr (BITS == 8) {
+          const int wv = 8 * grp + 4 * hf + (m >> 2);
+          const uint4 wa = *reinterpret_cast<const uint4*>(vc_l + (wv * 32 + 4 * g) * 4);
+          const uint4 wb = *reinterpret_cast<const uint4*>(vc_l + (wv * 32 + 16 + 4 * g) * 4);
+          // fp16 (1024 + 2c) - 1279 = 2c - 255, exact
+          const f16x2_t off = {(_Float16)-1279.0f, (_Float16)-1279.0f};
+          uint4 a8;
+          a8.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, (vperm(wa.y, wa.x, selx) << 1) | 0x64006400u) + off);
+          a8.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, (vperm(wa.w, wa.z, selx) << 1) | 0x64006400u) + off);
+          a8.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, (vperm(wb.y, wb.x, selx) << 1) | 0x64006400u) + off);
+          a8.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, (vperm(wb.w, wb.z, selx) << 1) | 0x64006400u) + off);
+          o_res[nb][2 * grp + hf] = mma_f16(a8, bop, o_res[nb][2 * grp + hf]);
+          continue;
+        }
+        const int wv = (BITS == 2 || BITS == 3) ? 2 * grp + hf : 4 * grp + 2 * hf + (m >> 3);
         const uint4 wa = *reinterpret_cast<const uint4*>(vc_l + (wv * 32 + 4 * g) * 4);
         const uint4 wb = *reinterpret_cast<const uint4*>(vc_l + (wv * 32 + 16 + 4 * g) * 4);
         // bytes 1 and 3 of y = the code bytes of two tokens, code at bits 8.. and 24..
@@ -450,10 +540,22 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
         const uint32_t y2 = vperm(wb.y, wb.x, selx) >> sh;
         const uint32_t y3 = vperm(wb.w, wb.z, selx) >> sh;
         uint4 alo;
-        alo.x = vperm(0u, kLutInt2, and_or(y0, k.m2, k.sel0));
-        alo.y = vperm(0u, kLutInt2, and_or(y1, k.m2, k.sel0));
-        alo.z = vperm(0u, kLutInt2, and_or(y2, k.m2, k.sel0));
-        alo.w = vperm(0u, kLutInt2, and_or(y3, k.m2, k.sel0));
+        if constexpr (BITS == 3) {
+          // table index c = low bits | bit 2 << 2 in bytes 1 and 3
+          const int wh = D / 16 + grp;
+          const uint4 ha = *reinterpret_cast<const uint4*>(vc_l + (wh * 32 + 4 * g) * 4);
+          const uint4 hb = *reinterpret_cast<const uint4*>(vc_l + (wh * 32 + 16 + 4 * g) * 4);
+          const uint32_t hsel = (uint32_t)(2 * hf + (m >> 3)) | 0x0C000C00u | ((uint32_t)(4 + 2 * hf + (m >> 3)) << 16);
+          alo.x = vperm(kLutInt3Hi, kLutInt3Lo, and_or(vperm(ha.y, ha.x, hsel) << hsh, k.m3s, and_or(y0, k.m2, k.sel0)));
+          alo.y = vperm(kLutInt3Hi, kLutInt3Lo, and_or(vperm(ha.w, ha.z, hsel) << hsh, k.m3s, and_or(y1, k.m2, k.sel0)));
+          alo.z = vperm(kLutInt3Hi, kLutInt3Lo, and_or(vperm(hb.y, hb.x, hsel) << hsh, k.m3s, and_or(y2, k.m2, k.sel0)));
+          alo.w = vperm(kLutInt3Hi, kLutInt3Lo, and_or(vperm(hb.w, hb.z, hsel) << hsh, k.m3s, and_or(y3, k.m2, k.sel0)));
+        } else {
+          alo.x = vperm(0u, kLutInt2, and_or(y0, k.m2, k.sel0));
+          alo.y = vperm(0u, kLutInt2, and_or(y1, k.m2, k.sel0));
+          alo.z = vperm(0u, kLutInt2, and_or(y2, k.m2, k.sel0));
+          alo.w = vperm(0u, kLutInt2, and_or(y3, k.m2, k.sel0));
+        }
         o_res[nb][2 * grp + hf] = mma_f16(alo, bop, o_res[nb][2 * grp + hf]);
         if constexpr (BITS == 4) {
           uint4 ahi;
@@ -470,7 +572,7 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
 
 // Issue every load of one tile: the residual loops' codes and scales and the
 // V reference tile by LDS DMA into `buf`, the K reference into registers.
-template <int D, bool RESID, bool FULL>
+template <int D, bool RESID, bool WIDE, bool FULL>
 __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* buf, const uint16_t* kbase,
                                            const uint16_t* vbase, int64_t row_base, int t0, int tlast, int lane,
                                            int m, int g, uint4 (&ka)[2][D / 32]) {
@@ -478,10 +580,23 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* b
   constexpr int NG = Gm::NG;
   if constexpr (RESID) {
     // INT4 slots first, then INT2 (the launcher orders them): no branch per loop
-    for (int li = 0; li < a.n4; ++li)
-      stage_loop<D, 4, FULL>(a, li, buf + slot_lds_offset<D>(a, li), row_base, t0, tlast, lane);
-    for (int li = a.n4; li < a.n4 + a.n2; ++li)
-      stage_loop<D, 2, FULL>(a, li, buf + slot_lds_offset<D>(a, li), row_base, t0, tlast, lane);
+    if constexpr (WIDE) {
+      // slots INT8, INT4, INT3, INT2
+      const int e8 = a.n8, e4 = e8 + a.n4, e3 = e4 + a.n3, e2 = e3 + a.n2;
+      for (int li = 0; li < e8; ++li)
+        stage_loop<D, 8, FULL>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
+      for (int li = e8; li < e4; ++li)
+        stage_loop<D, 4, FULL>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
+      for (int li = e4; li < e3; ++li)
+        stage_loop<D, 3, FULL>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
+      for (int li = e3; li < e2; ++li)
+        stage_loop<D, 2, FULL>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
+    } else {
+      for (int li = 0; li < a.n4; ++li)
+        stage_loop<D, 4, FULL>(a, li, buf + slot_lds_offset<D, false>(a, li), row_base, t0, tlast, lane);
+      for (int li = a.n4; li < a.n4 + a.n2; ++li)
+        stage_loop<D, 2, FULL>(a, li, buf + slot_lds_offset<D, false>(a, li), row_base, t0, tlast, lane);
+    }
   }
   if constexpr (FULL) {
     // the tile's 32 vectors are contiguous: 2D bytes each, one 16-byte chunk per lane
@@ -513,7 +628,7 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* b
 }
 
 // Scores, online softmax and PV of one staged tile.
-template <int D, int NB, bool RESID>
+template <int D, int NB, bool RESID, bool WIDE>
 __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned char* buf, int t0, int t_end,
                                              int m, int g, const uint4 (&ka)[2][D / 32], const uint4 (&qB)[NB][D / 32],
                                              const uint4 (&qtB)[NB][D / 32], const float (&qoff)[NB][D / 32],
@@ -534,10 +649,22 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
       sc[bk][nb] = acc;
     }
   if constexpr (RESID) {
-    for (int li = 0; li < a.n4; ++li)
-      residual_scores<D, NB, 4>(a, li, buf + slot_lds_offset<D>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
-    for (int li = a.n4; li < a.n4 + a.n2; ++li)
-      residual_scores<D, NB, 2>(a, li, buf + slot_lds_offset<D>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+    if constexpr (WIDE) {
+      const int e8 = a.n8, e4 = e8 + a.n4, e3 = e4 + a.n3, e2 = e3 + a.n2;
+      for (int li = 0; li < e8; ++li)
+        residual_scores<D, NB, 8>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+      for (int li = e8; li < e4; ++li)
+        residual_scores<D, NB, 4>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+      for (int li = e4; li < e3; ++li)
+        residual_scores<D, NB, 3>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+      for (int li = e3; li < e2; ++li)
+        residual_scores<D, NB, 2>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+    } else {
+      for (int li = 0; li < a.n4; ++li)
+        residual_scores<D, NB, 4>(a, li, buf + slot_lds_offset<D, false>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+      for (int li = a.n4; li < a.n4 + a.n2; ++li)
+        residual_scores<D, NB, 2>(a, li, buf + slot_lds_offset<D, false>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+    }
   }
 
   // ---- online softmax (log2 domain); row statistics live in the row's 4 lanes
@@ -621,14 +748,28 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
 
   // ---- residual PV
   if constexpr (RESID) {
-    for (int li = 0; li < a.n4; ++li)
-      residual_pv<D, NB, 4>(a, li, buf + slot_lds_offset<D>(a, li), p, my_loop, o_res, m, g, k);
-    for (int li = a.n4; li < a.n4 + a.n2; ++li)
-      residual_pv<D, NB, 2>(a, li, buf + slot_lds_offset<D>(a, li), p, my_loop, o_res, m, g, k);
+    if constexpr (WIDE) {
+      const int e8 = a.n8, e4 = e8 + a.n4, e3 = e4 + a.n3, e2 = e3 + a.n2;
+      for (int li = 0; li < e8; ++li)
+        residual_pv<D, NB, 8>(a, li, buf + slot_lds_offset<D, true>(a, li), p, my_loop, o_res, m, g, k);
+      for (int li = e8; li < e4; ++li)
+        residual_pv<D, NB, 4>(a, li, buf + slot_lds_offset<D, true>(a, li), p, my_loop, o_res, m, g, k);
+      for (int li = e4; li < e3; ++li)
+        residual_pv<D, NB, 3>(a, li, buf + slot_lds_offset<D, true>(a, li), p, my_loop, o_res, m, g, k);
+      for (int li = e3; li < e2; ++li)
+        residual_pv<D, NB, 2>(a, li, buf + slot_lds_offset<D, true>(a, li), p, my_loop, o_res, m, g, k);
+    } else {
+      for (int li = 0; li < a.n4; ++li)
+        residual_pv<D, NB, 4>(a, li, buf + slot_lds_offset<D, false>(a, li), p, my_loop, o_res, m, g, k);
+      for (int li = a.n4; li < a.n4 + a.n2; ++li)
+        residual_pv<D, NB, 2>(a, li, buf + slot_lds_offset<D, false>(a, li), p, my_loop, o_res, m, g, k);
+    }
   }
 }
 
-template <int D, int NB, bool RESID>
+// WIDE instantiations also take INT8 and INT3 loops; the others carry no code
+// for them.
+template <int D, int NB, bool RESID, bool WIDE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RESID && NB == 2 ? 1 : 2,
                                                                      RESID && NB == 1 ? 2 : 4)))
 void rq_decode_partial_mfma(DecodeArgs a) {
@@ -661,7 +802,7 @@ void rq_decode_partial_mfma(DecodeArgs a) {
     const int row = 16 * nb + m;
     my_loop[nb] = row < R ? row / G : -1;
     const int lb = my_loop[nb] >= 0 ? a.bits[my_loop[nb]] : 0;
-    qmul[nb] = lb == 4 ? 16.0f : 4.0f;
+    qmul[nb] = (float)(1 << lb);  // 2^b
     int64_t qrow = -1;
     if (row < R) qrow = ((int64_t)(a.loop_id[row / G] + z) * a.batch + b) * a.n_q_heads + kvh * G + row % G;
 #pragma unroll
@@ -710,14 +851,14 @@ void rq_decode_partial_mfma(DecodeArgs a) {
   const uint16_t* vbase = a.v[z] + row_base * D;
   constexpr int kStep = 4 * kTile;  // tokens between a wave's consecutive tiles
 
-  const Consts kc = make_consts();
+  const Consts kc = make_consts<WIDE>();
   uint4 ka[2][NG];
   for (int t0 = t_begin + wave * kTile; t0 < t_end; t0 += kStep) {
-    if (t0 + kTile <= S) issue_tile<D, RESID, true>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
-    else issue_tile<D, RESID, false>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
+    if (t0 + kTile <= S) issue_tile<D, RESID, WIDE, true>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
+    else issue_tile<D, RESID, WIDE, false>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
     wait_vmem();
     wave_sync_lds();
-    compute_tile<D, NB, RESID>(a, buf, t0, t_end, m, g, ka, qB, qtB, qoff, qmul, my_loop, o_ref, o_res, m_run, l_run,
+    compute_tile<D, NB, RESID, WIDE>(a, buf, t0, t_end, m, g, ka, qB, qtB, qoff, qmul, my_loop, o_ref, o_res, m_run, l_run,
                                kc);
     wait_lds();
     wave_sync_lds();  // the buffer is free for the next tile's DMA
@@ -829,23 +970,24 @@ static int block_lds_bytes(int d, int nb, int wave_bytes) {
   return merge > tiles ? merge : tiles;
 }
 
-template <int D, int NB, bool RESID>
+template <int D, int NB, bool RESID, bool WIDE>
 static void launch_mfma_kernel(const DecodeArgs& a, dim3 grid, int lds, hipStream_t stream) {
   static bool attr_set = false;  // lift the default dynamic-LDS cap once per instantiation
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rq_decode_partial_mfma<D, NB, RESID>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rq_decode_partial_mfma<D, NB, RESID, WIDE>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxBlockLds);
     attr_set = true;
   }
-  hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID>), grid, dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID, WIDE>), grid, dim3(256), lds, stream, a);
 }
 
 template <int D, int NB>
 static void launch_mfma_d(DecodeArgs a, dim3 grid, bool residual, hipStream_t stream) {
   a.lds_wave_bytes = decode_wave_lds_bytes(D, a.bits, residual ? a.n_loops_launch : 0);
   const int lds = block_lds_bytes(D, NB, a.lds_wave_bytes);
-  if (residual) launch_mfma_kernel<D, NB, true>(a, grid, lds, stream);
-  else launch_mfma_kernel<D, NB, false>(a, grid, lds, stream);
+  if (!residual) launch_mfma_kernel<D, NB, false, false>(a, grid, lds, stream);
+  else if (a.n8 + a.n3 > 0) launch_mfma_kernel<D, NB, true, true>(a, grid, lds, stream);
+  else launch_mfma_kernel<D, NB, true, false>(a, grid, lds, stream);
 }
 
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, int n_z, bool residual, hipStream_t stream) {

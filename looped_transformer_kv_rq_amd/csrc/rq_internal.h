@@ -43,13 +43,13 @@ struct ReconstructArgs {
 // One decode launch covers `n_rows` query rows per (batch, kv head): rows
 // r = li * G + j for slot li in [0, n_loops_launch) and j in [0, G). Row r
 // reads the query of loop loop_id[li] + blockIdx.y, query head kvh * G + j.
-// Slots are ordered INT4, INT2, reference-only. In the bf16 baseline each
-// launch has one slot (loop_id 0) and blockIdx.y picks the loop.
+// Slots are ordered INT8, INT4, INT3, INT2, reference-only. In the bf16
+// baseline each launch has one slot (loop_id 0) and blockIdx.y picks the loop.
 struct DecodeArgs {
   const uint16_t* q;                    // [n_loops_total][B][Hq][D]
   const uint16_t* k[kMaxLoops];         // per blockIdx.z: the K this block streams
   const uint16_t* v[kMaxLoops];
-  int32_t bits[kMaxLoops];              // per slot li: 4, then 2, then 0 (reference only)
+  int32_t bits[kMaxLoops];              // per slot li: 8, 4, 3, 2, then 0 (reference only)
   const uint32_t* kc[kMaxLoops];
   const uint16_t* ks[kMaxLoops];
   const uint32_t* vc[kMaxLoops];
@@ -57,7 +57,7 @@ struct DecodeArgs {
   float* ws;                            // partials [n_loops_total][B][Hq][n_splits][2D + 2]
   const unsigned char* qprep;           // rotated-query records [n_loops_total][B][Hq] (residual launches)
   int32_t loop_id[kMaxLoops];           // per slot: the call's loop index of its rows (+ blockIdx.y)
-  int32_t n4, n2;                       // slots [0, n4) are INT4, [n4, n4 + n2) INT2, the rest bits 0
+  int32_t n8, n4, n3, n2;               // slot counts per width, in slot order; the rest bits 0
   int32_t n_loops_launch;               // slots (loops) whose rows this launch holds
   int32_t n_rows;                       // n_loops_launch * G
   int32_t group;                        // G = Hq / Hkv

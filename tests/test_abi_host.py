@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"rq_encode", "rq_reconstruct", "rq_encode_refit", "rq_encode_append", "rq_decode_attn_varlen",
             "rq_decode_attn_varlen_workspace", "rq_encode_rotonly", "rq_reconstruct_rotonly", "rq_decode_attn",
-            "rq_decode_attn_bf16",
+            "rq_decode_attn_bf16", "rq_encode_layers",
             "rq_decode_attn_workspace", "rq_decode_attn_splits", "rq_status_str", "rq_format_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in rq.h but not exported"
@@ -89,8 +89,8 @@ def test_encode_argument_checks():
     assert call(n=9) == rq.RQ_EINVAL
     assert call(ref=None) == rq.RQ_EINVAL
     assert call(x=_ptrs(0)) == rq.RQ_EINVAL
-    assert call(bits=(ctypes.c_int32 * 1)(3)) == rq.RQ_EUNSUPPORTED
-    assert call(bits=(ctypes.c_int32 * 1)(0)) == rq.RQ_EUNSUPPORTED
+    for b in (0, 1, 5, 6, 7, 16):  # widths are 2, 3, 4 and 8
+        assert call(bits=(ctypes.c_int32 * 1)(b)) == rq.RQ_EUNSUPPORTED
     assert call(ref=FAKE + 8) == rq.RQ_EALIGN
     assert call(scales=_ptrs(FAKE + 2)) == rq.RQ_EALIGN
 
@@ -99,7 +99,8 @@ def test_reconstruct_argument_checks():
     lib = rq._load()
     sh = ctypes.byref(_shape())
     assert lib.rq_reconstruct(None, 2, FAKE, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EINVAL
-    assert lib.rq_reconstruct(sh, 3, FAKE, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EUNSUPPORTED
+    assert lib.rq_reconstruct(sh, 5, FAKE, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EUNSUPPORTED
+    assert lib.rq_reconstruct(sh, 1, FAKE, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EUNSUPPORTED
     assert lib.rq_reconstruct(sh, 2, FAKE, FAKE, FAKE, 7, FAKE, None) == rq.RQ_EUNSUPPORTED
     assert lib.rq_reconstruct(sh, 2, FAKE, None, FAKE, 0, FAKE, None) == rq.RQ_EINVAL
     assert lib.rq_reconstruct(sh, 2, FAKE, FAKE, FAKE, 0, None, None) == rq.RQ_EINVAL
@@ -121,7 +122,7 @@ def test_rotonly_argument_checks():
     assert lib.rq_encode_refit(sh, 1, x, bits, None, c, s, 1, None) == rq.RQ_EINVAL
     assert lib.rq_encode_refit(sh, 1, x, bits, FAKE, c, s, -1, None) == rq.RQ_EINVAL
     assert lib.rq_encode_refit(sh, 1, x, bits, FAKE, c, s, 17, None) == rq.RQ_EINVAL
-    assert lib.rq_encode_refit(sh, 1, x, (ctypes.c_int32 * 1)(3), FAKE, c, s, 2, None) == rq.RQ_EUNSUPPORTED
+    assert lib.rq_encode_refit(sh, 1, x, (ctypes.c_int32 * 1)(5), FAKE, c, s, 2, None) == rq.RQ_EUNSUPPORTED
     assert lib.rq_reconstruct_rotonly(sh, 0, FAKE, FAKE, 0, FAKE, None) == rq.RQ_EUNSUPPORTED
     assert lib.rq_reconstruct_rotonly(sh, 2, None, FAKE, 0, FAKE, None) == rq.RQ_EINVAL
     assert lib.rq_reconstruct_rotonly(sh, 2, FAKE, FAKE, 5, FAKE, None) == rq.RQ_EUNSUPPORTED
@@ -182,7 +183,7 @@ def test_decode_argument_checks():
     assert call(wsb=need - 1) == rq.RQ_EWORKSPACE
     assert call(out=FAKE + 4) == rq.RQ_EALIGN
     bad = (rq._LoopView * 2)()
-    bad[0].bits = 3
+    bad[0].bits = 5
     assert call(v=bad) == rq.RQ_EUNSUPPORTED
     bad[0].bits = 2  # residual loop without its code pointers
     assert call(v=bad) == rq.RQ_EINVAL
@@ -199,3 +200,27 @@ def test_python_side_rejects_cpu_tensors():
         rq.encode([ref], ref, [2])
     with pytest.raises(ValueError):
         rq.encode([ref], ref, [3])
+
+
+def test_encode_layers_argument_checks():
+    """Every layer's arguments are checked before the first launch: a bad entry
+    in the last layer fails the call although the first layer is valid."""
+    lib = rq._load()
+    sh = ctypes.byref(_shape())
+    enc = lib.rq_encode_layers
+    x2, c2, s2 = _ptrs(FAKE, FAKE, FAKE, FAKE), _ptrs(FAKE, FAKE, FAKE, FAKE), _ptrs(FAKE, FAKE, FAKE, FAKE)
+    refs = _ptrs(FAKE, FAKE)
+    good = (ctypes.c_int32 * 4)(8, 3, 4, 2)
+    assert enc(sh, 0, 2, x2, good, refs, c2, s2, None) == rq.RQ_EINVAL            # no layers
+    assert enc(sh, 4097, 1, x2, good, refs, c2, s2, None) == rq.RQ_EINVAL         # above RQ_MAX_LAYERS
+    assert enc(sh, 2, 0, x2, good, refs, c2, s2, None) == rq.RQ_EINVAL            # no loops
+    assert enc(sh, 2, 9, x2, good, refs, c2, s2, None) == rq.RQ_EINVAL            # above RQ_MAX_LOOPS
+    assert enc(None, 2, 2, x2, good, refs, c2, s2, None) == rq.RQ_EINVAL
+    assert enc(sh, 2, 2, x2, None, refs, c2, s2, None) == rq.RQ_EINVAL
+    assert enc(sh, 2, 2, x2, good, None, c2, s2, None) == rq.RQ_EINVAL
+    assert enc(sh, 2, 2, x2, good, _ptrs(FAKE, 0), c2, s2, None) == rq.RQ_EINVAL   # layer 1 has no reference
+    assert enc(sh, 2, 2, x2, (ctypes.c_int32 * 4)(2, 2, 2, 5), refs, c2, s2, None) == rq.RQ_EUNSUPPORTED
+    assert enc(sh, 2, 2, x2, (ctypes.c_int32 * 4)(2, 2, 2, 0), refs, c2, s2, None) == rq.RQ_EUNSUPPORTED
+    assert enc(sh, 2, 2, _ptrs(FAKE, FAKE, FAKE, 0), good, refs, c2, s2, None) == rq.RQ_EINVAL
+    assert enc(sh, 2, 2, x2, good, refs, c2, _ptrs(FAKE, FAKE, FAKE, FAKE + 2), None) == rq.RQ_EALIGN
+    assert enc(sh, 2, 2, x2, good, _ptrs(FAKE, FAKE + 8), c2, s2, None) == rq.RQ_EALIGN

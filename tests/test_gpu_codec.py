@@ -28,7 +28,7 @@ def _random_case(b, h, s, d, sigma=0.1, seed=0):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("s", [1, 37, 300])
 def test_encode_small_shapes(d, bits, s):
     print(f"encode d={d} bits={bits} s={s}", flush=True)
@@ -130,7 +130,7 @@ def test_encode_full_size_sampled_rows(name, rows):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("bits", [0, 2, 4])
+@pytest.mark.parametrize("bits", [0, 2, 3, 4, 8])
 def test_reconstruct_matches_oracle_on_oracle_codes(d, bits):
     x, ref = _random_case(2, 2, 70, d, sigma=0.2, seed=bits + d)
     if bits:

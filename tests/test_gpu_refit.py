@@ -23,7 +23,7 @@ def _case(b, h, s, d, sigma, seed):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("refits", [1, 3])
 def test_refit_matches_oracle(d, bits, refits):
     print(f"refit d={d} bits={bits} refits={refits}", flush=True)

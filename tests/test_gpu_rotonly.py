@@ -45,7 +45,7 @@ def test_rotonly_equals_encode_against_zero_reference():
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_rotonly_reconstruct_matches_oracle(d, bits):
     x = _states(2, 2, 70, d, 1, seed=3 * d + bits)[0]
     zero = np.zeros_like(x)

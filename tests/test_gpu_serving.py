@@ -20,11 +20,12 @@ def _bf16(rng, shape, scale=1.0):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("t_new", [1, 3])
-def test_append_writes_exactly_the_new_positions(d, t_new):
-    print(f"append d={d} t_new={t_new}", flush=True)
+@pytest.mark.parametrize("bits", [(2, 4), (8, 3)])
+def test_append_writes_exactly_the_new_positions(d, t_new, bits):
+    print(f"append d={d} t_new={t_new} bits={bits}", flush=True)
     rng = np.random.default_rng(d + t_new)
     B, H, S = 4, 2, 40
-    bits = [2, 4]
+    bits = list(bits)
     ref_new = _bf16(rng, (B, H, t_new, d))
     xs = [workloads.f32_to_bf16_bits((workloads.bf16_bits_to_f32(ref_new) + 0.2 * rng.standard_normal(
         ref_new.shape)).astype(np.float32)) for _ in bits]

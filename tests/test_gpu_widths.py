@@ -1,0 +1,158 @@
+"""GPU parity of the INT3 and INT8 widths in the fused decode, and of the
+per-(layer, loop) width table (rq_encode_layers), against the oracle.
+
+The encoders, reconstruct, refit, append and rotation-only tests cover the new
+widths in their own files (their width parametrisations include 3 and 8)."""
+import numpy as np
+import pytest
+import torch
+
+import looped_transformer_kv_rq_amd as rq
+import oracle
+import workloads
+from rq_parity import assert_attn_close, compare_codes, to_dev, to_host_u16, to_host_words, words_to_dev
+from test_gpu_decode import _all_rows, _run_case
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------------------- decode, random packed codes
+# Random code words reach every code value of every width; the scales are
+# fp16 values in [0.01, 0.1].
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bits", [(8, 3, 2, 0), (3, 3, 3, 0), (8, 8, 0), (4, 3, 0), (8, 4, 3, 2, 0)])
+@pytest.mark.parametrize("hq", [8, 16])
+def test_decode_wide_tables(d, bits, hq):
+    """G = 4 (one 16-row block per launch) and 8 (two blocks once there are
+    three or more loops), every width order, both head sizes."""
+    print(f"decode wide d={d} bits={bits} hq={hq}", flush=True)
+    n = len(bits)
+    sig = tuple([0.1] * (n - 1) + [0.0])
+    w = workloads.Workload("wide", 95, n, 2, 2, hq, d, 131, bits, sig)
+    _run_case(w, range(n), _all_rows(w))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("s", [1, 63, 65, 200])
+def test_decode_wide_ragged_lengths(d, s):
+    w = workloads.Workload("wide_ragged", 96, 3, 2, 2, 8, d, s, (8, 3, 0), (0.2, 0.1, 0.0))
+    _run_case(w, range(3), _all_rows(w))
+
+
+def test_decode_wide_one_loop_and_split_counts():
+    w = workloads.Workload("wide_splits", 97, 3, 1, 2, 8, 128, 1000, (3, 8, 0), (0.1, 0.1, 0.0))
+    for loop in range(3):
+        _run_case(w, [loop], _all_rows(w))
+    for n in (1, 3, 16):
+        _run_case(w, range(3), _all_rows(w), n_splits=n)
+
+
+# --------------------------------------------------------------------------- decode after a GPU encode
+
+def _states(b, h, s, d, sigmas, seed):
+    rng = np.random.default_rng(seed)
+    ref = workloads.f32_to_bf16_bits(rng.standard_normal((b, h, s, d)).astype(np.float32))
+    xs = [workloads.f32_to_bf16_bits((workloads.bf16_bits_to_f32(ref) + sg * rng.standard_normal(
+        (b, h, s, d))).astype(np.float32)) for sg in sigmas]
+    return xs + [ref]
+
+
+def _oracle_decode(q_bits, ks, vs, bits, enc_k, enc_v):
+    """Oracle decode over the oracle's reconstruction from the given codes."""
+    k_hat, v_hat = [], []
+    for l, bl in enumerate(bits):
+        if bl:
+            k_hat.append(oracle.reconstruct(ks[-1], *enc_k[l], bl))
+            v_hat.append(oracle.reconstruct(vs[-1], *enc_v[l], bl))
+        else:
+            k_hat.append(oracle.bf16_to_f64(ks[-1]))
+            v_hat.append(oracle.bf16_to_f64(vs[-1]))
+    return oracle.decode_attn(q_bits, k_hat, v_hat)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_encode_then_decode_wide(d):
+    """GPU encode at (8, 3, 4) then the fused decode; the oracle decodes the GPU's
+    own codes (so code decisions at a threshold cannot differ)."""
+    bits = (8, 3, 4, 0)
+    b, h, hq, s = 2, 2, 8, 257
+    ks = _states(b, h, s, d, (0.2, 0.1, 0.05), seed=d)
+    vs = _states(b, h, s, d, (0.2, 0.1, 0.05), seed=d + 1)
+    kd, vd = [to_dev(x) for x in ks], [to_dev(x) for x in vs]
+    kc, kss = rq.encode(kd[:-1], kd[-1], bits[:-1])
+    vc, vss = rq.encode(vd[:-1], vd[-1], bits[:-1])
+    views = [rq.LoopView(bl, kc[l], kss[l], vc[l], vss[l]) for l, bl in enumerate(bits[:-1])] + [rq.LoopView(0)]
+    q = workloads.f32_to_bf16_bits(np.random.default_rng(7).standard_normal((4, b, hq, d)).astype(np.float32))
+    out = rq.decode_attn(to_dev(q), kd[-1], vd[-1], views).cpu().numpy()
+    enc_k = [(to_host_words(kc[l]), to_host_u16(kss[l])) for l in range(3)]
+    enc_v = [(to_host_words(vc[l]), to_host_u16(vss[l])) for l in range(3)]
+    # the GPU's codes are the oracle's away from thresholds
+    for l, bl in enumerate(bits[:-1]):
+        ow, os_ = oracle.encode(ks[l], ks[-1], bl)
+        compare_codes(enc_k[l][0], enc_k[l][1], ow, os_, ks[l], ks[-1], bl)
+    assert_attn_close(out, _oracle_decode(q, ks, vs, bits, enc_k, enc_v))
+
+
+# --------------------------------------------------------------------------- per-(layer, loop) table
+
+def test_encode_layers_equals_per_layer_encodes():
+    table = [(8, 4, 2), (3, 3, 2), (2, 8, 3)]
+    layers = [_states(2, 2, 70, 128, (0.2, 0.1, 0.05), seed=30 + l) for l in range(3)]
+    dev = [[to_dev(x) for x in st] for st in layers]
+    codes, scales = rq.encode_layers([st[:-1] for st in dev], [st[-1] for st in dev], table)
+    for l, row in enumerate(table):
+        c1, s1 = rq.encode(dev[l][:-1], dev[l][-1], row)
+        for i, bl in enumerate(row):
+            assert torch.equal(codes[l][i], c1[i])
+            assert torch.equal(scales[l][i].view(torch.int16), s1[i].view(torch.int16))
+            ow, os_ = oracle.encode(layers[l][i], layers[l][-1], bl)
+            compare_codes(to_host_words(codes[l][i]), to_host_u16(scales[l][i]), ow, os_, layers[l][i],
+                          layers[l][-1], bl)
+
+
+def test_layer_table_full_size_sampled_rows():
+    """The launches the benchmark's layer-table leg times: every layer of
+    LAYER_BITS_L4 encoded over the K and V states of l4_b16_s4k (one call for
+    all layers), then each layer's decode with its row of the table."""
+    w = workloads.WORKLOADS["l4_b16_s4k"]
+    table = workloads.LAYER_BITS_L4
+    rows = [(0, 0), (11, 6)]
+    q_bits = workloads.q_tensor(w)
+    qd = to_dev(q_bits)
+    enc = {}
+    for tensor in (workloads.TENSOR_K, workloads.TENSOR_V):
+        xs = workloads.kv_tensors(w, tensor)
+        xd = [to_dev(x) for x in xs]
+        codes, scales = rq.encode_layers([xd[:-1]] * len(table), [xd[-1]] * len(table),
+                                         [row[:-1] for row in table])
+        torch.cuda.synchronize()
+        for (b, h) in rows:
+            st = workloads.kv_rows_all_loops(w, b, h, tensor)
+            for l, row in enumerate(table):
+                for i, bl in enumerate(row[:-1]):
+                    ow, os_ = oracle.encode(st[i], st[-1], bl)
+                    compare_codes(to_host_words(codes[l][i][b, h]), to_host_u16(scales[l][i][b, h]), ow, os_,
+                                  st[i], st[-1], bl)
+        enc[tensor] = (xd[-1], codes, scales)
+        del xd
+    kref, kc, ksc = enc[workloads.TENSOR_K]
+    vref, vc, vsc = enc[workloads.TENSOR_V]
+    g = w.group_size
+    for l, row in enumerate(table):
+        views = [rq.LoopView(bl, kc[l][i], ksc[l][i], vc[l][i], vsc[l][i]) for i, bl in enumerate(row[:-1])]
+        out = rq.decode_attn(qd, kref, vref, views + [rq.LoopView(0)]).cpu().numpy()
+        for (b, h) in rows:
+            k_st = workloads.kv_rows_all_loops(w, b, h, workloads.TENSOR_K)
+            v_st = workloads.kv_rows_all_loops(w, b, h, workloads.TENSOR_V)
+            scale = 1.0 / np.sqrt(w.head_dim)
+            for i, bl in enumerate(row):
+                if bl:
+                    k = oracle.reconstruct(k_st[-1], to_host_words(kc[l][i][b, h]), to_host_u16(ksc[l][i][b, h]), bl)
+                    v = oracle.reconstruct(v_st[-1], to_host_words(vc[l][i][b, h]), to_host_u16(vsc[l][i][b, h]), bl)
+                else:
+                    k, v = oracle.bf16_to_f64(k_st[-1]), oracle.bf16_to_f64(v_st[-1])
+                q = oracle.bf16_to_f64(q_bits[i, b, h * g:(h + 1) * g])
+                assert_attn_close(out[i, b, h * g:(h + 1) * g], oracle.attention(q, k, v, scale))
+    del enc, kc, vc, ksc, vsc
+    torch.cuda.empty_cache()

@@ -70,6 +70,8 @@ def test_packed_rows():
     words, scales = workloads.packed_row(w, 0, 0, 0, 0)
     assert words.shape == (64, 16) and words.dtype == np.uint32  # INT4 loop
     sv = scales.view(np.float16).astype(np.float64)
-    assert sv.min() >= 0.0099 and sv.max() <= 0.1001
-    words1, _ = workloads.packed_row(w, 0, 0, 0, 1)
+    assert sv.min() >= 0.2 * 0.0099 and sv.max() <= 0.2 * 0.1001  # INT4: 1.5 / 7.5 of INT2's range
+    words1, s1 = workloads.packed_row(w, 0, 0, 0, 1)
     assert words1.shape == (64, 8)  # INT2 loop
+    sv1 = s1.view(np.float16).astype(np.float64)
+    assert sv1.min() >= 0.0099 and sv1.max() <= 0.1001

@@ -78,6 +78,12 @@ WORKLOADS = {
     "peak_batch": Workload("peak_batch", 5, 8, 4, 4, 16, 128, 16384, (4, 2, 2, 2, 2, 2, 2, 0), _sigma_geometric(8)),
 }
 
+# A per-(layer, loop) width table for four layers of the l4_b16_s4k shape. The
+# pages fill such a table by calibration, which is out of scope; this one is
+# synthetic: wider codes in earlier layers and in loops far from the final
+# loop, every width once. Row l is layer l's bits per loop (0: the reference).
+LAYER_BITS_L4 = ((8, 4, 2, 0), (4, 3, 2, 0), (3, 3, 2, 0), (2, 2, 2, 0))
+
 HEAVY_SCALE = 20.0
 HEAVY_CHANNELS = 4
 
@@ -189,15 +195,24 @@ def kv_tensors(w: Workload, tensor: int) -> list:
     return outs
 
 
+# Scale range of a random packed group, relative to INT2's [0.01, 0.1]: the
+# largest level of a b-bit grid is 2^(b-1) - 1/2, and these factors make it
+# times the scale span the same range at every width (an encoder's step shrinks
+# the same way with the width).
+PACKED_SCALE_FACTOR = {2: 1.0, 3: 1.5 / 3.5, 4: 1.5 / 7.5, 8: 1.5 / 127.5}
+
+
 def packed_row(w: Workload, b: int, h: int, tensor: int, loop: int):
     """Decode-only input for a residual loop: uniformly random code words
     [S, D*bits/32] (uint32) and fp16 scale bits [S, D/32] with values drawn
-    uniformly from [0.01, 0.1]. Used where the bf16 loop states would not fit
-    (the peak-batch workload) and to exercise every code pattern."""
+    uniformly from [0.01, 0.1] * PACKED_SCALE_FACTOR[bits]. Used where the bf16
+    loop states would not fit (the peak-batch workload) and to exercise every
+    code pattern."""
     bits = w.bits[loop]
     rng = _rng(w, b, h, TENSOR_PACKED_K + tensor, loop)
     words = rng.integers(0, 2**32, size=(w.seq_len, w.head_dim * bits // 32), dtype=np.uint64).astype(np.uint32)
-    scales = rng.uniform(0.01, 0.1, size=(w.seq_len, w.head_dim // GROUP)).astype(np.float16).view(np.uint16)
+    f = PACKED_SCALE_FACTOR[bits]
+    scales = rng.uniform(0.01 * f, 0.1 * f, size=(w.seq_len, w.head_dim // GROUP)).astype(np.float16).view(np.uint16)
     return words, scales
 
 
