@@ -212,8 +212,8 @@ def copy_probe():
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps first: the clocks settle within about 20")
     ap.add_argument("--workload", default="l4_b16_s4k", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--reps", type=int, default=20, help="repetitions of each side measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -286,25 +286,34 @@ def main():
         enc_k(); enc_v(); dec()
     torch.cuda.synchronize()
 
+    # The timed steps: one pair of events around all of them and nothing
+    # between the launches.
     Ev = torch.cuda.Event
-    marks = [[Ev(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start, stop = Ev(enable_timing=True), Ev(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
+    for _ in range(args.steps):
+        enc_k(); enc_v(); dec()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    step_ms = start.elapsed_time(stop) / args.steps
+
+    # Per-kernel split of a step, from a separate pass with an event between
+    # every two launches (each marker adds a drain, so this pass runs slower).
+    marks = [[Ev(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for k in range(args.steps):
         m = marks[k]
         m[0].record(stream); enc_k()
         m[1].record(stream); enc_v()
         m[2].record(stream); dec()
         m[3].record(stream)
-    stop.record(stream)
     torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t_wall
-    step_ms = start.elapsed_time(stop) / args.steps
     enc_in_step_ms = statistics.mean([m[0].elapsed_time(m[1]) for m in marks] +
                                      [m[1].elapsed_time(m[2]) for m in marks])
     dec_in_step_ms = statistics.mean([m[2].elapsed_time(m[3]) for m in marks])
+    marked_step_ms = statistics.mean([m[0].elapsed_time(m[3]) for m in marks])
 
     # The encoder's roofline figure: back-to-back launches (K, V, K, V, ...)
     # bracketed by one pair of events, so no event marker sits between two
@@ -404,6 +413,9 @@ def main():
         }
         result["encode"] = {"GBps": enc_gbps, "ms_per_launch": enc_ms, "ms_per_launch_in_step": enc_in_step_ms,
                             "launches_per_step": 2}
+        result["step_split"] = {"encode_ms": 2 * enc_in_step_ms, "decode_ms": dec_in_step_ms,
+                                "step_ms_with_markers": marked_step_ms,
+                                "what": "a separate pass with an event between launches"}
         result["bf16_baseline"] = {
             "kv_tokens_per_s": kv_tokens / (bf_ms * 1e-3), "ms": bf_ms,
             "GBps": bf_b / (bf_ms * 1e-3) / 1e9, "frac_peak": bf_b / (bf_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -550,6 +562,44 @@ def main():
             "kv_tokens_per_s": float(lens.sum() + w.batch) * w.n_loops / (sv_ms * 1e-3),
             "what": "rq_decode_attn_varlen (ragged prefixes + 1 tail position) + rq_encode_append of K and V",
         }
+
+        # The same serving step over a block-paged copy of the cache: blocks of
+        # 128 positions in a shuffled order, the table mapping each sequence's
+        # blocks (rq_decode_attn_paged + rq_encode_append_paged).
+        P = 128
+        nbs = w.seq_len // P
+        perm = torch.from_numpy(np.random.default_rng(w.seed + 1).permutation(w.batch * nbs)).to(dev)
+        table = perm.view(w.batch, nbs).to(torch.int32).contiguous()
+
+        def paged(t):  # [B, H, S, row] -> [B*S/P, H, P, row], logical block n at physical perm[n]
+            blocks = t.view(w.batch, w.n_kv_heads, nbs, P, t.shape[-1]).permute(0, 2, 1, 3, 4)
+            blocks = blocks.reshape(w.batch * nbs, w.n_kv_heads, P, t.shape[-1])
+            out_t = torch.empty_like(blocks)
+            out_t[perm] = blocks
+            return out_t
+
+        kref_p, vref_p = paged(kref), paged(vref)
+        kc_p, ks_p = [paged(t) for t in kc], [paged(t) for t in ks]
+        vc_p, vs_p = [paged(t) for t in vc], [paged(t) for t in vs]
+        views_p = [rq.LoopView(bl, kc_p[i], ks_p[i], vc_p[i], vs_p[i]) for i, bl in enumerate(bits)]
+        views_p.append(rq.LoopView(0))
+
+        def serve_paged():
+            rq.decode_attn_paged(q, kref_p, vref_p, views_p, table, seq_lens=lens_d, tail_k=tk, tail_v=tv, out=out,
+                                 workspace=ws_v, stream=stream)
+            rq.encode_append_paged([tk[l] for l in res_loops], tk[-1], bits, lens_d, table, kref_p, kc_p, ks_p,
+                                   stream=stream)
+            rq.encode_append_paged([tv[l] for l in res_loops], tv[-1], bits, lens_d, table, vref_p, vc_p, vs_p,
+                                   stream=stream)
+
+        svp_ms = timed(serve_paged, args.reps)
+        result["serving_step_paged"] = {
+            "ms": svp_ms, "block_size": P, "blocks": w.batch * nbs, "prefix_tokens": int(lens.sum()),
+            "decode_GBps": sv_bytes / (svp_ms * 1e-3) / 1e9,
+            "kv_tokens_per_s": float(lens.sum() + w.batch) * w.n_loops / (svp_ms * 1e-3),
+            "what": "serving_step over a block-paged cache (shuffled blocks of 128 positions)",
+        }
+        del kref_p, vref_p, kc_p, ks_p, vc_p, vs_p
     if cpu is not None:
         result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)

@@ -24,6 +24,8 @@
  *                        the same codec without a reference
  *   rq_encode_layers   rq_encode over several layers with a per-(layer, loop)
  *                        bit-width table
+ *   rq_encode_append_paged / rq_decode_attn_paged  the serving step over a
+ *                        block-paged cache
  *
  * FORMAT (RQ_FORMAT_VERSION 1)
  *   Dense tensors are [batch][n_kv_heads][seq_len][head_dim], head_dim
@@ -98,6 +100,20 @@ typedef struct rq_shape {
   int32_t head_dim; /* 64 or 128 */
 } rq_shape;
 
+/* A block-paged cache (the serving-step calls *_paged). Every paged tensor is
+   [n_blocks][n_kv_heads][block_size][row] (row: head_dim bf16 for the
+   reference, head_dim*bits/32 words for codes, head_dim/32 fp16 for scales),
+   and position t of sequence b lives in block block_table[b * max_blocks +
+   t / block_size] at offset t % block_size. Blocks may be shared or in any
+   order; a table entry outside [0, n_blocks) marks a block that is not there:
+   its positions take no attention weight and appends to it write nothing. */
+typedef struct rq_pages {
+  const int32_t* block_table; /* device int32 [batch][max_blocks] */
+  int32_t max_blocks;         /* table entries per sequence */
+  int32_t block_size;         /* positions per block: a power of two, at least 64 */
+  int32_t n_blocks;           /* blocks in every paged tensor */
+} rq_pages;
+
 /* One loop of the cache as rq_decode_attn reads it. bits = 0 marks the final
    loop (the reference itself; code and scale pointers are ignored and may be
    NULL). bits = 2, 3, 4 or 8 is a residual loop in the format above. */
@@ -155,6 +171,21 @@ int rq_encode_refit(const rq_shape* shape, int32_t n_loops, const uint16_t* cons
 int rq_encode_append(const rq_shape* cache, int32_t n_loops, int32_t t_new, const uint16_t* const* x,
                      const int32_t* bits, const uint16_t* ref_new, const int32_t* pos, uint16_t* ref_cache,
                      uint32_t* const* codes, uint16_t* const* scales, void* stream);
+
+/* rq_encode_append into a block-paged cache (rq_pages).
+ *   cache      batch, n_kv_heads and head_dim of the cache; cache->seq_len is
+ *              the capacity of one sequence, pages->max_blocks * pages->block_size
+ *              (RQ_EINVAL otherwise)
+ *   ref_pages  bf16 [n_blocks][Hkv][block_size][D]: receives ref_new
+ *   codes[i], scales[i]  paged tensors [n_blocks][Hkv][block_size][...]
+ *   block_size not a power of two of at least 64: RQ_EUNSUPPORTED.
+ * A position outside [0, capacity), or in a block whose table entry is not
+ * valid, is skipped. Other arguments and the output values as rq_encode_append;
+ * with t_new = S and pos = 0 this is the encode of a whole prefill into pages. */
+int rq_encode_append_paged(const rq_shape* cache, const rq_pages* pages, int32_t n_loops, int32_t t_new,
+                           const uint16_t* const* x, const int32_t* bits, const uint16_t* ref_new,
+                           const int32_t* pos, uint16_t* ref_pages, uint32_t* const* codes,
+                           uint16_t* const* scales, void* stream);
 
 /* Materialise one loop: out = ref + H (s * q) (ResidualQuant, newx.sg page,
  * Abstract: the residual format keeps reconstruction cheap).
@@ -250,6 +281,20 @@ int rq_decode_attn_varlen(const rq_shape* shape, int32_t n_q_heads, int32_t n_lo
                           const int32_t* seq_lens, int32_t tail_len, const uint16_t* const* tail_k,
                           const uint16_t* const* tail_v, float softmax_scale, int32_t n_splits, float* out,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* rq_decode_attn_varlen over a block-paged cache (rq_pages): k_ref, v_ref and
+ * every loop view's code and scale tensors are paged tensors
+ * [n_blocks][Hkv][block_size][...]; the tail tensors stay dense
+ * [B][Hkv][tail_len][D]. shape->seq_len is the capacity of one sequence,
+ * pages->max_blocks * pages->block_size (RQ_EINVAL otherwise); block_size not a
+ * power of two of at least 64 is RQ_EUNSUPPORTED. The workspace size comes
+ * from rq_decode_attn_varlen_workspace with the same shape. The result is that
+ * of rq_decode_attn_varlen over the cache the table describes. */
+int rq_decode_attn_paged(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                         const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
+                         const rq_pages* pages, const int32_t* seq_lens, int32_t tail_len,
+                         const uint16_t* const* tail_k, const uint16_t* const* tail_v, float softmax_scale,
+                         int32_t n_splits, float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The uncompressed baseline: the same decode attention where loop i attends
  * over its own bf16 K/V, k[i] and v[i] (host arrays of device pointers, each

@@ -19,6 +19,7 @@ import torch
 __all__ = [
     "LoopView", "RQError", "encode", "encode_into", "reconstruct", "decode_attn", "decode_attn_bf16",
     "encode_rotonly", "reconstruct_rotonly", "encode_append", "decode_attn_varlen", "encode_layers",
+    "encode_append_paged", "decode_attn_paged",
     "decode_varlen_workspace_bytes",
     "decode_workspace_bytes", "decode_splits", "format_version", "library_path",
     "RQ_OK", "RQ_EINVAL", "RQ_EUNSUPPORTED", "RQ_EALIGN", "RQ_EWORKSPACE", "RQ_EHIP", "MAX_LOOPS",
@@ -51,6 +52,11 @@ class _Shape(ctypes.Structure):
 class _LoopView(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
                 ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p)]
+
+
+class _Pages(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("n_blocks", ctypes.c_int32)]
 
 
 class LoopView(NamedTuple):
@@ -87,6 +93,10 @@ def _load():
         "rq_encode_rotonly": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, ctypes.POINTER(I32), PP, PP, P]),
         "rq_encode_layers": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, PP, ctypes.POINTER(I32), PP, PP, PP,
                                             P]),
+        "rq_encode_append_paged": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Pages), I32, I32, PP,
+                                                  ctypes.POINTER(I32), P, P, P, PP, PP, P]),
+        "rq_decode_attn_paged": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, P, P, ctypes.POINTER(_LoopView),
+                                                ctypes.POINTER(_Pages), P, I32, PP, PP, F, I32, P, P, SZ, P]),
         "rq_reconstruct_rotonly": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, P, P, I32, P, P]),
         "rq_decode_attn_splits": (I32, [ctypes.POINTER(_Shape), I32, I32, I32]),
         "rq_decode_attn_workspace": (SZ, [ctypes.POINTER(_Shape), I32, I32, I32]),
@@ -360,6 +370,89 @@ def decode_attn_varlen(q: torch.Tensor, k_ref: torch.Tensor, v_ref: torch.Tensor
                                    _stream(k_ref.device, stream))
     _check(st, "rq_decode_attn_varlen")
     return out
+
+
+def _pages_of(block_table: torch.Tensor, block_size: int, n_blocks: int, batch: int, device) -> _Pages:
+    if block_table.dim() != 2 or block_table.shape[0] != batch:
+        raise ValueError("block_table must be int32 [batch, max_blocks]")
+    _need(block_table, "block_table", torch.int32, tuple(block_table.shape), device)
+    return _Pages(block_table.data_ptr(), block_table.shape[1], int(block_size), int(n_blocks))
+
+
+def decode_attn_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, loops: Sequence[LoopView],
+                      block_table: torch.Tensor, seq_lens: Optional[torch.Tensor] = None,
+                      tail_k: Optional[Sequence[torch.Tensor]] = None, tail_v: Optional[Sequence[torch.Tensor]] = None,
+                      softmax_scale: Optional[float] = None, n_splits: int = 0, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """decode_attn_varlen over a block-paged cache: k_pages, v_pages bf16 [n_blocks, Hkv, P, D] and
+    the loop views' codes / scales [n_blocks, Hkv, P, ...]; block_table int32 device [B, max_blocks]
+    (position t of sequence b is in block block_table[b, t // P] at offset t % P). Tails stay
+    dense [B, Hkv, T, D]."""
+    lib = _load()
+    n_blocks, h, p, d = k_pages.shape
+    n_loops, b, hq, _ = q.shape
+    _need(q, "q", torch.bfloat16, (n_loops, b, hq, d), k_pages.device)
+    _need(k_pages, "k_pages", torch.bfloat16, k_pages.shape)
+    _need(v_pages, "v_pages", torch.bfloat16, k_pages.shape, k_pages.device)
+    pages = _pages_of(block_table, p, n_blocks, b, k_pages.device)
+    s_cap = pages.max_blocks * p
+    shp = _Shape(b, h, s_cap, d)
+    views = _loop_views(loops, n_loops, k_pages)
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", torch.int32, (b,), k_pages.device)
+    tail_len = 0
+    tk = tv = None
+    if tail_k is not None or tail_v is not None:
+        if tail_k is None or tail_v is None or len(tail_k) != n_loops or len(tail_v) != n_loops:
+            raise ValueError("tail_k and tail_v need one bf16 [B, Hkv, T, D] tensor per loop")
+        tail_len = tail_k[0].shape[2]
+        for i in range(n_loops):
+            _need(tail_k[i], f"tail_k[{i}]", torch.bfloat16, (b, h, tail_len, d), k_pages.device)
+            _need(tail_v[i], f"tail_v[{i}]", torch.bfloat16, (b, h, tail_len, d), k_pages.device)
+        tk, tv = _ptr_array(tail_k), _ptr_array(tail_v)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((n_loops, b, hq, d), dtype=torch.float32, device=k_pages.device)
+    _need(out, "out", torch.float32, (n_loops, b, hq, d), k_pages.device)
+    need = decode_varlen_workspace_bytes(b, h, s_cap, d, hq, n_loops, n_splits, tail_len)
+    if need == 0:
+        raise RQError(RQ_EINVAL, "decode workspace query")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k_pages.device)
+    st = lib.rq_decode_attn_paged(ctypes.byref(shp), hq, n_loops, _ptr(q), _ptr(k_pages), _ptr(v_pages), views,
+                                  ctypes.byref(pages), _ptr(seq_lens), int(tail_len), tk, tv, float(softmax_scale),
+                                  int(n_splits), _ptr(out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(k_pages.device, stream))
+    _check(st, "rq_decode_attn_paged")
+    return out
+
+
+def encode_append_paged(xs: Sequence[torch.Tensor], ref_new: torch.Tensor, bits: Sequence[int], pos: torch.Tensor,
+                        block_table: torch.Tensor, ref_pages: torch.Tensor, codes: Sequence[torch.Tensor],
+                        scales: Sequence[torch.Tensor], stream=None) -> None:
+    """encode_append into a block-paged cache: ref_pages bf16 [n_blocks, Hkv, P, D], codes[i] /
+    scales[i] [n_blocks, Hkv, P, ...], block_table int32 device [B, max_blocks]."""
+    lib = _load()
+    b, h, t, d = ref_new.shape
+    n_blocks, _, p, _ = ref_pages.shape
+    _need(ref_new, "ref_new", torch.bfloat16, ref_new.shape)
+    _need(ref_pages, "ref_pages", torch.bfloat16, (n_blocks, h, p, d), ref_new.device)
+    _need(pos, "pos", torch.int32, (b,), ref_new.device)
+    pages = _pages_of(block_table, p, n_blocks, b, ref_new.device)
+    n = len(xs)
+    if not (len(bits) == len(codes) == len(scales) == n):
+        raise ValueError("xs, bits, codes and scales must have one entry per loop")
+    for i in range(n):
+        _need(xs[i], f"xs[{i}]", torch.bfloat16, ref_new.shape, ref_new.device)
+        _need(codes[i], f"codes[{i}]", torch.int32, (n_blocks, h, p, d * int(bits[i]) // 32), ref_new.device)
+        _need(scales[i], f"scales[{i}]", torch.float16, (n_blocks, h, p, d // GROUP), ref_new.device)
+    shp = _Shape(b, h, pages.max_blocks * p, d)
+    bits_arr = (ctypes.c_int32 * n)(*[int(x) for x in bits])
+    st = lib.rq_encode_append_paged(ctypes.byref(shp), ctypes.byref(pages), n, t, _ptr_array(xs), bits_arr,
+                                    _ptr(ref_new), _ptr(pos), _ptr(ref_pages), _ptr_array(codes), _ptr_array(scales),
+                                    _stream(ref_new.device, stream))
+    _check(st, "rq_encode_append_paged")
 
 
 def encode_append(xs: Sequence[torch.Tensor], ref_new: torch.Tensor, bits: Sequence[int], pos: torch.Tensor,

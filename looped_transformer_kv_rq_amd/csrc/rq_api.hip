@@ -186,11 +186,36 @@ int rq_reconstruct(const rq_shape* shape, int32_t bits, const uint16_t* ref, con
   return reconstruct_common(shape, bits, ref, codes, scales, out_dtype, out, stream);
 }
 
-int rq_encode_append(const rq_shape* cache, int32_t n_loops, int32_t t_new, const uint16_t* const* x,
-                     const int32_t* bits, const uint16_t* ref_new, const int32_t* pos, uint16_t* ref_cache,
-                     uint32_t* const* codes, uint16_t* const* scales, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// RQ_OK if `pages` describes a paged cache of capacity shape->seq_len.
+int check_pages(const rq_shape* shape, const rq_pages* pages) {
+  if (pages == nullptr || pages->block_table == nullptr) return RQ_EINVAL;
+  const int32_t p = pages->block_size;
+  if (p < 64 || (p & (p - 1)) != 0) return RQ_EUNSUPPORTED;
+  if (pages->max_blocks < 1 || pages->n_blocks < 1) return RQ_EINVAL;
+  if ((int64_t)pages->max_blocks * p != shape->seq_len) return RQ_EINVAL;
+  if (!aligned16(pages->block_table)) return RQ_EALIGN;
+  return RQ_OK;
+}
+
+int log2_of(int32_t p) {
+  int l = 0;
+  while ((1 << l) < p) ++l;
+  return l;
+}
+
+int append_impl(const rq_shape* cache, const rq_pages* pages, int32_t n_loops, int32_t t_new,
+                const uint16_t* const* x, const int32_t* bits, const uint16_t* ref_new, const int32_t* pos,
+                uint16_t* ref_cache, uint32_t* const* codes, uint16_t* const* scales, void* stream) {
   int st = check_shape(cache);
   if (st != RQ_OK) return st;
+  if (pages != nullptr) {
+    st = check_pages(cache, pages);
+    if (st != RQ_OK) return st;
+  }
   if (n_loops < 1 || n_loops > kMaxLoops || t_new < 1) return RQ_EINVAL;
   if (x == nullptr || bits == nullptr || ref_new == nullptr || pos == nullptr || ref_cache == nullptr ||
       codes == nullptr || scales == nullptr)
@@ -219,8 +244,32 @@ int rq_encode_append(const rq_shape* cache, int32_t n_loops, int32_t t_new, cons
   a.n_kv_heads = cache->n_kv_heads;
   a.s_cap = cache->seq_len;
   a.ref_out = ref_cache;
+  if (pages != nullptr) {
+    a.block_table = pages->block_table;
+    a.max_blocks = pages->max_blocks;
+    a.log2_block = log2_of(pages->block_size);
+    a.n_blocks = pages->n_blocks;
+  }
   a.n_vec = (int64_t)cache->batch * cache->n_kv_heads * t_new;
   return hip_status(launch_encode(a, cache->head_dim, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int rq_encode_append(const rq_shape* cache, int32_t n_loops, int32_t t_new, const uint16_t* const* x,
+                     const int32_t* bits, const uint16_t* ref_new, const int32_t* pos, uint16_t* ref_cache,
+                     uint32_t* const* codes, uint16_t* const* scales, void* stream) {
+  return append_impl(cache, nullptr, n_loops, t_new, x, bits, ref_new, pos, ref_cache, codes, scales, stream);
+}
+
+int rq_encode_append_paged(const rq_shape* cache, const rq_pages* pages, int32_t n_loops, int32_t t_new,
+                           const uint16_t* const* x, const int32_t* bits, const uint16_t* ref_new,
+                           const int32_t* pos, uint16_t* ref_pages, uint32_t* const* codes,
+                           uint16_t* const* scales, void* stream) {
+  if (pages == nullptr) return RQ_EINVAL;
+  return append_impl(cache, pages, n_loops, t_new, x, bits, ref_new, pos, ref_pages, codes, scales, stream);
 }
 
 int rq_encode_layers(const rq_shape* shape, int32_t n_layers, int32_t n_loops, const uint16_t* const* x,
@@ -275,9 +324,13 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
                 const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops, const int32_t* seq_lens,
                 int32_t tail_len, const uint16_t* const* tail_k, const uint16_t* const* tail_v,
                 float softmax_scale, int32_t n_splits, float* out, void* workspace, size_t workspace_bytes,
-                void* stream) {
+                void* stream, const rq_pages* pages = nullptr) {
   int st = check_heads(shape, n_q_heads, n_loops);
   if (st != RQ_OK) return st;
+  if (pages != nullptr) {
+    st = check_pages(shape, pages);
+    if (st != RQ_OK) return st;
+  }
   if (q == nullptr || k_ref == nullptr || v_ref == nullptr || loops == nullptr || out == nullptr) return RQ_EINVAL;
   if (n_splits < 0 || !isfinite(softmax_scale) || tail_len < 0) return RQ_EINVAL;
   if (tail_len > 0) {
@@ -350,6 +403,12 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
     a.qprep = prep;
     a.k[0] = k_ref;
     a.v[0] = v_ref;
+    if (pages != nullptr) {
+      a.block_table = pages->block_table;
+      a.max_blocks = pages->max_blocks;
+      a.log2_block = log2_of(pages->block_size);
+      a.n_blocks = pages->n_blocks;
+    }
     a.n_loops_launch = nl;
     a.n_rows = nl * G;
     bool residual = false;
@@ -430,6 +489,17 @@ int rq_decode_attn_varlen(const rq_shape* shape, int32_t n_q_heads, int32_t n_lo
   if (seq_lens != nullptr && !aligned16(seq_lens)) return RQ_EALIGN;
   return decode_impl(shape, n_q_heads, n_loops, q, k_ref, v_ref, loops, seq_lens, tail_len, tail_k, tail_v,
                      softmax_scale, n_splits, out, workspace, workspace_bytes, stream);
+}
+
+int rq_decode_attn_paged(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                         const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
+                         const rq_pages* pages, const int32_t* seq_lens, int32_t tail_len,
+                         const uint16_t* const* tail_k, const uint16_t* const* tail_v, float softmax_scale,
+                         int32_t n_splits, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (pages == nullptr) return RQ_EINVAL;
+  if (seq_lens != nullptr && !aligned16(seq_lens)) return RQ_EALIGN;
+  return decode_impl(shape, n_q_heads, n_loops, q, k_ref, v_ref, loops, seq_lens, tail_len, tail_k, tail_v,
+                     softmax_scale, n_splits, out, workspace, workspace_bytes, stream, pages);
 }
 
 int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,

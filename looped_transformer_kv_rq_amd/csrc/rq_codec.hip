@@ -147,13 +147,23 @@ __global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
     const int64_t base = v * D + sub * PER;
     // Output vector. Appending: source vector (row, t) of a [rows][t_new] batch
     // goes to cache position pos[b] + t of row = b * Hkv + h; a position past the
-    // cache's capacity (or a negative one) writes nothing.
+    // cache's capacity (or a negative one) writes nothing. In a paged cache the
+    // position lives in block block_table[b][p / P] at offset p % P; a position
+    // whose table entry is not a valid block writes nothing either.
     int64_t vo = v;
     if constexpr (APPEND) {
       const int64_t row = v / a.t_new;
-      const int64_t p = (int64_t)a.pos[row / a.n_kv_heads] + v % a.t_new;
+      const int64_t bq = row / a.n_kv_heads;
+      const int64_t p = (int64_t)a.pos[bq] + v % a.t_new;
       if (p < 0 || p >= a.s_cap) continue;  // uniform across the vector's lanes
-      vo = row * a.s_cap + p;
+      if (a.block_table != nullptr) {
+        const int blk = a.block_table[bq * a.max_blocks + (p >> a.log2_block)];
+        if (blk < 0 || blk >= a.n_blocks) continue;
+        vo = (((int64_t)blk * a.n_kv_heads + row % a.n_kv_heads) << a.log2_block) +
+             (p & ((1 << a.log2_block) - 1));
+      } else {
+        vo = row * a.s_cap + p;
+      }
     }
     // negated reference pair sums and differences (zero without a reference)
     float nrs[PER / 2], nrd[PER / 2];

@@ -38,6 +38,11 @@
 // registers. The V tile and every residual loop's codes and scales go to LDS
 // by DMA (global_load_lds). A tile therefore costs one memory round trip
 // however many loops it carries.
+//
+// PAGED instantiations read a block-paged cache: each tensor is
+// [n_blocks][Hkv][P][row] and position t of sequence b lives in block
+// block_table[b][t / P] at offset t % P. P is a power of two and a multiple of
+// 64, so a 32-token tile lies in one block and one table entry places it.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -769,7 +774,7 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
 
 // WIDE instantiations also take INT8 and INT3 loops; the others carry no code
 // for them.
-template <int D, int NB, bool RESID, bool WIDE>
+template <int D, int NB, bool RESID, bool WIDE, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RESID && NB == 2 ? 1 : 2,
                                                                      RESID && NB == 1 ? 2 : 4)))
 void rq_decode_partial_mfma(DecodeArgs a) {
@@ -854,8 +859,22 @@ void rq_decode_partial_mfma(DecodeArgs a) {
   const Consts kc = make_consts<WIDE>();
   uint4 ka[2][NG];
   for (int t0 = t_begin + wave * kTile; t0 < t_end; t0 += kStep) {
-    if (t0 + kTile <= S) issue_tile<D, RESID, WIDE, true>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
-    else issue_tile<D, RESID, WIDE, false>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
+    // Unclamped loads only when every token of the tile is one of this call's
+    // positions: positions past a sequence's length may hold any bits.
+    const bool full = t0 + kTile <= t_end;
+    if constexpr (PAGED) {
+      const int blk = a.block_table[(int64_t)b * a.max_blocks + (t0 >> a.log2_block)];
+      if (blk < 0 || blk >= a.n_blocks) continue;  // no valid page: the tile takes no weight
+      // vector index of token t0; the tile's tokens follow it
+      const int64_t tv = (((int64_t)blk * a.n_kv_heads + kvh) << a.log2_block) + (t0 & ((1 << a.log2_block) - 1));
+      const uint16_t* kt = a.k[z] + tv * D;
+      const uint16_t* vt = a.v[z] + tv * D;
+      if (full) issue_tile<D, RESID, WIDE, true>(a, buf, kt, vt, tv, 0, tlast - t0, lane, m, g, ka);
+      else issue_tile<D, RESID, WIDE, false>(a, buf, kt, vt, tv, 0, tlast - t0, lane, m, g, ka);
+    } else {
+      if (full) issue_tile<D, RESID, WIDE, true>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
+      else issue_tile<D, RESID, WIDE, false>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
+    }
     wait_vmem();
     wave_sync_lds();
     compute_tile<D, NB, RESID, WIDE>(a, buf, t0, t_end, m, g, ka, qB, qtB, qoff, qmul, my_loop, o_ref, o_res, m_run, l_run,
@@ -970,24 +989,30 @@ static int block_lds_bytes(int d, int nb, int wave_bytes) {
   return merge > tiles ? merge : tiles;
 }
 
-template <int D, int NB, bool RESID, bool WIDE>
+template <int D, int NB, bool RESID, bool WIDE, bool PAGED>
 static void launch_mfma_kernel(const DecodeArgs& a, dim3 grid, int lds, hipStream_t stream) {
   static bool attr_set = false;  // lift the default dynamic-LDS cap once per instantiation
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rq_decode_partial_mfma<D, NB, RESID, WIDE>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxBlockLds);
     attr_set = true;
   }
-  hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID, WIDE>), grid, dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED>), grid, dim3(256), lds, stream, a);
+}
+
+template <int D, int NB, bool PAGED>
+static void launch_mfma_dp(const DecodeArgs& a, dim3 grid, int lds, bool residual, hipStream_t stream) {
+  if (!residual) launch_mfma_kernel<D, NB, false, false, PAGED>(a, grid, lds, stream);
+  else if (a.n8 + a.n3 > 0) launch_mfma_kernel<D, NB, true, true, PAGED>(a, grid, lds, stream);
+  else launch_mfma_kernel<D, NB, true, false, PAGED>(a, grid, lds, stream);
 }
 
 template <int D, int NB>
 static void launch_mfma_d(DecodeArgs a, dim3 grid, bool residual, hipStream_t stream) {
   a.lds_wave_bytes = decode_wave_lds_bytes(D, a.bits, residual ? a.n_loops_launch : 0);
   const int lds = block_lds_bytes(D, NB, a.lds_wave_bytes);
-  if (!residual) launch_mfma_kernel<D, NB, false, false>(a, grid, lds, stream);
-  else if (a.n8 + a.n3 > 0) launch_mfma_kernel<D, NB, true, true>(a, grid, lds, stream);
-  else launch_mfma_kernel<D, NB, true, false>(a, grid, lds, stream);
+  if (a.block_table != nullptr) launch_mfma_dp<D, NB, true>(a, grid, lds, residual, stream);
+  else launch_mfma_dp<D, NB, false>(a, grid, lds, residual, stream);
 }
 
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, int n_z, bool residual, hipStream_t stream) {

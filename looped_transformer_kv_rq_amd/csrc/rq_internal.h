@@ -29,6 +29,9 @@ struct EncodeArgs {
   int32_t t_new, n_kv_heads;
   int64_t s_cap;
   uint16_t* ref_out;
+  // paged cache (block_table != NULL): outputs are [n_blocks][Hkv][2^log2_block][row]
+  const int32_t* block_table;
+  int32_t max_blocks, log2_block, n_blocks;
   int64_t n_vec;  // batch * n_kv_heads * seq_len
 };
 
@@ -65,6 +68,10 @@ struct DecodeArgs {
   int32_t n_splits, tokens_per_split;
   int32_t rec_splits, split_base;       // records per row in the workspace; this launch's first split
   const int32_t* seq_lens;              // device [B] prefix lengths, or NULL (all seq_len)
+  // paged cache (block_table != NULL): tensors are [n_blocks][Hkv][2^log2_block][row];
+  // position t of sequence b is in block block_table[b * max_blocks + (t >> log2_block)]
+  const int32_t* block_table;
+  int32_t max_blocks, log2_block, n_blocks;
   float scale_log2;                     // softmax scale * log2(e)
   int32_t lds_wave_bytes;               // per-wave LDS stride (set by the launcher)
   int32_t zero_residual;                // write a zero residual accumulator (reference-only launch)

@@ -16,6 +16,7 @@ from .rq_oracle import (  # noqa: F401
     f16_to_f64,
     f64_to_bf16,
     f64_to_f16,
+    gather_pages,
     hadamard,
     level_offset,
     ls_scale,

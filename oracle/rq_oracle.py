@@ -330,3 +330,27 @@ def decode_attn_varlen(q_bits, k_hat: list, v_hat: list, seq_lens, tail_k_bits=N
                 rows = slice(kv * g, (kv + 1) * g)
                 out[l, b, rows] = attention(q[l, b, rows], k, v, scale)
     return out
+
+
+# ----------------------------------------------------------------------------
+# block-paged caches (the serving step around the hot path)
+# ----------------------------------------------------------------------------
+
+def gather_pages(pages, block_table, block_size: int, seq_len: int) -> np.ndarray:
+    """The dense cache a block table describes (ResidualQuant, paperaft JSON
+    page, `summary`: the cache lives in a serving stack, which pages it).
+
+    pages: [n_blocks, Hkv, P, ...]; block_table: ints [B, max_blocks].
+    Returns [B, Hkv, seq_len, ...] where position t of sequence b is
+    pages[block_table[b, t // P], :, t % P]. A position whose table entry is
+    not in [0, n_blocks) is filled with zeros (it is not part of the cache)."""
+    pages = np.asarray(pages)
+    table = np.asarray(block_table)
+    n_blocks, hkv = pages.shape[0], pages.shape[1]
+    out = np.zeros((table.shape[0], hkv, seq_len) + pages.shape[3:], dtype=pages.dtype)
+    for b in range(table.shape[0]):
+        for t in range(seq_len):
+            blk = int(table[b, t // block_size])
+            if 0 <= blk < n_blocks:
+                out[b, :, t] = pages[blk, :, t % block_size]
+    return out

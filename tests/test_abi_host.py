@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"rq_encode", "rq_reconstruct", "rq_encode_refit", "rq_encode_append", "rq_decode_attn_varlen",
             "rq_decode_attn_varlen_workspace", "rq_encode_rotonly", "rq_reconstruct_rotonly", "rq_decode_attn",
-            "rq_decode_attn_bf16", "rq_encode_layers",
+            "rq_decode_attn_bf16", "rq_encode_layers", "rq_encode_append_paged", "rq_decode_attn_paged",
             "rq_decode_attn_workspace", "rq_decode_attn_splits", "rq_status_str", "rq_format_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in rq.h but not exported"
@@ -224,3 +224,38 @@ def test_encode_layers_argument_checks():
     assert enc(sh, 2, 2, _ptrs(FAKE, FAKE, FAKE, 0), good, refs, c2, s2, None) == rq.RQ_EINVAL
     assert enc(sh, 2, 2, x2, good, refs, c2, _ptrs(FAKE, FAKE, FAKE, FAKE + 2), None) == rq.RQ_EALIGN
     assert enc(sh, 2, 2, x2, good, _ptrs(FAKE, FAKE + 8), c2, s2, None) == rq.RQ_EALIGN
+
+
+def test_paged_argument_checks():
+    lib = rq._load()
+    P, max_blocks = 64, 4
+    sh = ctypes.byref(_shape(b=2, h=2, s=P * max_blocks, d=64))
+    good = rq._Pages(FAKE, max_blocks, P, 16)
+    views = (rq._LoopView * 2)()
+    views[0].bits, views[0].k_codes, views[0].k_scales, views[0].v_codes, views[0].v_scales = 8, FAKE, FAKE, FAKE, FAKE
+    need = lib.rq_decode_attn_varlen_workspace(sh, 4, 2, 0, 0)
+
+    def dec(pages=good, shape=sh):
+        pg = None if pages is None else ctypes.byref(pages)
+        return lib.rq_decode_attn_paged(shape, 4, 2, FAKE, FAKE, FAKE, views, pg, None, 0, None, None, 0.125, 0,
+                                        FAKE, FAKE, need, None)
+
+    assert dec(pages=None) == rq.RQ_EINVAL
+    assert dec(pages=rq._Pages(0, max_blocks, P, 16)) == rq.RQ_EINVAL            # no block table
+    assert dec(pages=rq._Pages(FAKE, max_blocks, 96, 16)) == rq.RQ_EUNSUPPORTED   # not a power of two
+    assert dec(pages=rq._Pages(FAKE, max_blocks, 32, 16)) == rq.RQ_EUNSUPPORTED   # below 64
+    assert dec(pages=rq._Pages(FAKE, 0, P, 16)) == rq.RQ_EINVAL
+    assert dec(pages=rq._Pages(FAKE, max_blocks, P, 0)) == rq.RQ_EINVAL
+    assert dec(pages=rq._Pages(FAKE, max_blocks - 1, P, 16)) == rq.RQ_EINVAL      # capacity != seq_len
+    assert dec(pages=rq._Pages(FAKE + 4, max_blocks, P, 16)) == rq.RQ_EALIGN
+    bits = (ctypes.c_int32 * 1)(3)
+    x, c, s = _ptrs(FAKE), _ptrs(FAKE), _ptrs(FAKE)
+
+    def app(pages=good, t_new=1):
+        pg = None if pages is None else ctypes.byref(pages)
+        return lib.rq_encode_append_paged(sh, pg, 1, t_new, x, bits, FAKE, FAKE, FAKE, c, s, None)
+
+    assert app(pages=None) == rq.RQ_EINVAL
+    assert app(t_new=0) == rq.RQ_EINVAL
+    assert app(pages=rq._Pages(FAKE, max_blocks, 100, 16)) == rq.RQ_EUNSUPPORTED
+    assert app(pages=rq._Pages(FAKE, 3, P, 16)) == rq.RQ_EINVAL

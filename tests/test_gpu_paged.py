@@ -1,0 +1,293 @@
+"""GPU parity of the block-paged serving step (rq_decode_attn_paged,
+rq_encode_append_paged) against the oracle, and of the contiguous varlen
+decode when the cache past each prefix holds non-finite bits.
+
+Paged tensors are [n_blocks, Hkv, P, row]; the tests scatter a dense cache
+into shuffled blocks, leave every block and position outside the cache
+filled with NaN / Inf bit patterns, and compare with the oracle's decode
+over the dense cache the table describes (oracle.gather_pages)."""
+import numpy as np
+import pytest
+import torch
+
+import looped_transformer_kv_rq_amd as rq
+import oracle
+import workloads
+from rq_parity import assert_attn_close, compare_codes, to_dev, to_host_u16, to_host_words, words_to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+BF16_NAN, F16_INF = 0x7FC0, 0x7C00
+
+
+def _bf16(rng, shape, scale=1.0):
+    return workloads.f32_to_bf16_bits((scale * rng.standard_normal(shape)).astype(np.float32))
+
+
+def _dense_cache(rng, B, H, S, d, bits_per_loop):
+    kref, vref = _bf16(rng, (B, H, S, d)), _bf16(rng, (B, H, S, d))
+    res = {}
+    for l, bl in enumerate(bits_per_loop):
+        if bl:
+            kx = workloads.f32_to_bf16_bits((workloads.bf16_bits_to_f32(kref) + 0.2 * rng.standard_normal(
+                kref.shape)).astype(np.float32))
+            vx = workloads.f32_to_bf16_bits((workloads.bf16_bits_to_f32(vref) + 0.2 * rng.standard_normal(
+                vref.shape)).astype(np.float32))
+            res[l] = (oracle.encode(kx, kref, bl), oracle.encode(vx, vref, bl))
+    return kref, vref, res
+
+
+def _table(rng, B, max_blocks, lens, P, spare):
+    """Shuffled physical blocks for the positions below each length; -1 for the rest."""
+    need = [(int(n) + P - 1) // P for n in lens]
+    perm = rng.permutation(sum(need) + spare)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    k = 0
+    for b in range(B):
+        for j in range(need[b]):
+            table[b, j] = perm[k]
+            k += 1
+    return table, len(perm)
+
+
+def _scatter(dense, table, lens, P, n_blocks, fill):
+    """Paged copy of dense [B, H, S, row]: positions below lens[b] only; the rest is `fill`."""
+    B, H, S = dense.shape[:3]
+    pages = np.full((n_blocks, H, P) + dense.shape[3:], fill, dtype=dense.dtype)
+    for b in range(B):
+        for t in range(int(lens[b])):
+            pages[table[b, t // P], :, t % P] = dense[b, :, t]
+    return pages
+
+
+def _hat(kref, vref, res, bits_per_loop):
+    kh, vh = [], []
+    for l, bl in enumerate(bits_per_loop):
+        if bl:
+            (kw, ks), (vw, vs) = res[l]
+            kh.append(oracle.reconstruct(kref, kw, ks, bl))
+            vh.append(oracle.reconstruct(vref, vw, vs, bl))
+        else:
+            kh.append(oracle.bf16_to_f64(kref))
+            vh.append(oracle.bf16_to_f64(vref))
+    return kh, vh
+
+
+@pytest.mark.parametrize("d,P,bits_per_loop,tail", [
+    (128, 64, (2, 4, 0), 0), (128, 128, (2, 2, 0), 1), (64, 64, (8, 3, 0), 2), (128, 256, (4, 2, 2, 0), 1)])
+def test_paged_decode_matches_oracle(d, P, bits_per_loop, tail):
+    print(f"paged d={d} P={P} bits={bits_per_loop} tail={tail}", flush=True)
+    rng = np.random.default_rng(d + P + tail)
+    L, B, H, hq, max_blocks = len(bits_per_loop), 6, 2, 8, 4
+    S = max_blocks * P
+    lens = np.array([0, 1, P - 1, P, P + 1, S], dtype=np.int32)
+    kref, vref, res = _dense_cache(rng, B, H, S, d, bits_per_loop)
+    table, n_blocks = _table(rng, B, max_blocks, lens, P, spare=2)
+    views = []
+    for l, bl in enumerate(bits_per_loop):
+        if bl:
+            (kw, ks), (vw, vs) = res[l]
+            pk = [_scatter(kw, table, lens, P, n_blocks, 0xFFFFFFFF), _scatter(ks, table, lens, P, n_blocks, F16_INF)]
+            pv = [_scatter(vw, table, lens, P, n_blocks, 0xFFFFFFFF), _scatter(vs, table, lens, P, n_blocks, F16_INF)]
+            views.append(rq.LoopView(bl, words_to_dev(pk[0]), to_dev(pk[1], torch.float16), words_to_dev(pv[0]),
+                                     to_dev(pv[1], torch.float16)))
+        else:
+            views.append(rq.LoopView(0))
+    kp = _scatter(kref, table, lens, P, n_blocks, BF16_NAN)
+    vp = _scatter(vref, table, lens, P, n_blocks, BF16_NAN)
+    q = _bf16(rng, (L, B, hq, d))
+    tk = tv = None
+    if tail:
+        tk = [_bf16(rng, (B, H, tail, d)) for _ in range(L)]
+        tv = [_bf16(rng, (B, H, tail, d)) for _ in range(L)]
+    out = rq.decode_attn_paged(to_dev(q), to_dev(kp), to_dev(vp), views, torch.from_numpy(table).to(DEV),
+                               seq_lens=torch.from_numpy(lens).to(DEV),
+                               tail_k=None if tk is None else [to_dev(x) for x in tk],
+                               tail_v=None if tv is None else [to_dev(x) for x in tv]).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    # the oracle reads the dense cache the table describes
+    assert np.array_equal(oracle.gather_pages(kp, table, P, S)[1, :, :1], kref[1, :, :1])
+    kh, vh = _hat(kref, vref, res, bits_per_loop)
+    expect = oracle.decode_attn_varlen(q, kh, vh, lens, tk, tv)
+    if not tail:
+        assert np.all(out[:, 0] == 0)  # sequence 0 has no position at all
+        assert_attn_close(out[:, 1:], expect[:, 1:])
+    else:
+        assert_attn_close(out, expect)
+
+
+def test_paged_equals_contiguous_varlen():
+    """The same cache, dense or scattered into shuffled blocks: identical results."""
+    rng = np.random.default_rng(5)
+    bits_per_loop = (2, 2, 0)
+    B, H, d, P, max_blocks = 3, 2, 128, 128, 3
+    S = P * max_blocks
+    lens = np.array([S, 200, 77], dtype=np.int32)
+    kref, vref, res = _dense_cache(rng, B, H, S, d, bits_per_loop)
+    table, n_blocks = _table(rng, B, max_blocks, np.full(B, S), P, spare=1)
+    q = to_dev(_bf16(rng, (3, B, 8, d)))
+    dense_views, paged_views = [], []
+    for l, bl in enumerate(bits_per_loop):
+        if bl:
+            (kw, ks), (vw, vs) = res[l]
+            dense_views.append(rq.LoopView(bl, words_to_dev(kw), to_dev(ks, torch.float16), words_to_dev(vw),
+                                           to_dev(vs, torch.float16)))
+            full = np.full(B, S)
+            paged_views.append(rq.LoopView(
+                bl, words_to_dev(_scatter(kw, table, full, P, n_blocks, 0)),
+                to_dev(_scatter(ks, table, full, P, n_blocks, 0), torch.float16),
+                words_to_dev(_scatter(vw, table, full, P, n_blocks, 0)),
+                to_dev(_scatter(vs, table, full, P, n_blocks, 0), torch.float16)))
+        else:
+            dense_views.append(rq.LoopView(0))
+            paged_views.append(rq.LoopView(0))
+    full = np.full(B, S)
+    lens_d = torch.from_numpy(lens).to(DEV)
+    a = rq.decode_attn_varlen(q, to_dev(kref), to_dev(vref), dense_views, seq_lens=lens_d)
+    b = rq.decode_attn_paged(q, to_dev(_scatter(kref, table, full, P, n_blocks, 0)),
+                             to_dev(_scatter(vref, table, full, P, n_blocks, 0)), paged_views,
+                             torch.from_numpy(table).to(DEV), seq_lens=lens_d)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("bits", [(2, 4), (8, 3)])
+def test_paged_append_writes_exactly_the_new_positions(bits):
+    rng = np.random.default_rng(sum(bits))
+    B, H, d, P, max_blocks, t_new = 4, 2, 128, 64, 3, 3
+    S = P * max_blocks
+    bits = list(bits)
+    ref_new = _bf16(rng, (B, H, t_new, d))
+    xs = [workloads.f32_to_bf16_bits((workloads.bf16_bits_to_f32(ref_new) + 0.2 * rng.standard_normal(
+        ref_new.shape)).astype(np.float32)) for _ in bits]
+    # sequence 0 crosses from block 0 into block 1; sequence 2 runs past the capacity;
+    # sequence 3's second block is not there (-1)
+    pos = np.array([P - 2, 5, S - 1, P - 1], dtype=np.int32)
+    table = np.array([[4, 0, 7], [2, 5, 6], [1, 3, 8], [9, -1, 10]], dtype=np.int32)
+    n_blocks = 11
+    codes = [torch.full((n_blocks, H, P, d * b // 32), 0x5A5A5A5A, dtype=torch.int32, device=DEV) for b in bits]
+    scales = [torch.full((n_blocks, H, P, d // 32), 7.0, dtype=torch.float16, device=DEV) for _ in bits]
+    ref_pages = torch.full((n_blocks, H, P, d), 3.0, dtype=torch.bfloat16, device=DEV)
+    rq.encode_append_paged([to_dev(x) for x in xs], to_dev(ref_new), bits, torch.from_numpy(pos).to(DEV),
+                           torch.from_numpy(table).to(DEV), ref_pages, codes, scales)
+    torch.cuda.synchronize()
+    written = np.zeros((n_blocks, P), dtype=bool)
+    where = {}
+    for b in range(B):
+        for t in range(t_new):
+            p = int(pos[b]) + t
+            if 0 <= p < S and table[b, p // P] >= 0:
+                blk, off = int(table[b, p // P]), p % P
+                written[blk, off] = True
+                where[(b, t)] = (blk, off)
+    assert len(where) == B * t_new - 2 - 2  # two past the capacity, two into the missing block
+    rp = to_host_u16(ref_pages)
+    for (b, t), (blk, off) in where.items():
+        np.testing.assert_array_equal(rp[blk, :, off], ref_new[b, :, t])
+    sentinel = to_host_u16(torch.full((1,), 3.0, dtype=torch.bfloat16))[0]
+    assert np.all(rp.transpose(0, 2, 1, 3)[~written] == sentinel)
+    for i, bl in enumerate(bits):
+        cw, cs = to_host_words(codes[i]), to_host_u16(scales[i])
+        assert np.all(cw.transpose(0, 2, 1, 3)[~written] == 0x5A5A5A5A)
+        ow, os_ = oracle.encode(xs[i], ref_new, bl)
+        for (b, t), (blk, off) in where.items():
+            compare_codes(cw[blk, :, off], cs[blk, :, off], ow[b, :, t], os_[b, :, t], xs[i][b, :, t],
+                          ref_new[b, :, t], bl)
+
+
+def test_paged_serving_steps_append_then_decode():
+    """Prefill into pages with one append of every sequence's prefix, then three
+    decode steps that attend over the pages plus the current position's bf16
+    loop states and append that position."""
+    rng = np.random.default_rng(43)
+    bits = [2, 4]
+    L = len(bits) + 1
+    B, H, d, hq, P, max_blocks = 3, 2, 128, 8, 64, 3
+    S = P * max_blocks
+    lens = np.array([5, 63, 120], dtype=np.int32)
+    kref_all, vref_all = _bf16(rng, (B, H, S, d)), _bf16(rng, (B, H, S, d))
+    kl = [workloads.f32_to_bf16_bits((workloads.bf16_bits_to_f32(kref_all) + 0.15 * rng.standard_normal(
+        kref_all.shape)).astype(np.float32)) for _ in bits] + [kref_all]
+    vl = [workloads.f32_to_bf16_bits((workloads.bf16_bits_to_f32(vref_all) + 0.15 * rng.standard_normal(
+        vref_all.shape)).astype(np.float32)) for _ in bits] + [vref_all]
+    table_np, n_blocks = _table(rng, B, max_blocks, np.full(B, S), P, spare=0)
+    table = torch.from_numpy(table_np).to(DEV)
+    kc = [torch.zeros((n_blocks, H, P, d * b // 32), dtype=torch.int32, device=DEV) for b in bits]
+    ks = [torch.zeros((n_blocks, H, P, d // 32), dtype=torch.float16, device=DEV) for _ in bits]
+    vc = [torch.zeros_like(t) for t in kc]
+    vs = [torch.zeros_like(t) for t in ks]
+    kref_p = torch.zeros((n_blocks, H, P, d), dtype=torch.bfloat16, device=DEV)
+    vref_p = torch.zeros_like(kref_p)
+    n0 = int(lens.max())
+    zero = torch.zeros(B, dtype=torch.int32, device=DEV)
+    for src, codes, scales, refp in ((kl, kc, ks, kref_p), (vl, vc, vs, vref_p)):
+        rq.encode_append_paged([to_dev(x[:, :, :n0]) for x in src[:-1]], to_dev(src[-1][:, :, :n0]), bits, zero,
+                               table, refp, codes, scales)
+    views = [rq.LoopView(b, kc[i], ks[i], vc[i], vs[i]) for i, b in enumerate(bits)] + [rq.LoopView(0)]
+    lens_now = lens.copy()
+    for step in range(3):
+        q = _bf16(rng, (L, B, hq, d))
+        tail_k = [np.stack([kl[l][b, :, lens_now[b]:lens_now[b] + 1] for b in range(B)]) for l in range(L)]
+        tail_v = [np.stack([vl[l][b, :, lens_now[b]:lens_now[b] + 1] for b in range(B)]) for l in range(L)]
+        out = rq.decode_attn_paged(to_dev(q), kref_p, vref_p, views, table,
+                                   seq_lens=torch.from_numpy(lens_now).to(DEV),
+                                   tail_k=[to_dev(x) for x in tail_k], tail_v=[to_dev(x) for x in tail_v])
+        # oracle: the dense cache the table describes, read back from the device pages
+        kr = oracle.gather_pages(to_host_u16(kref_p), table_np, P, S)
+        vr = oracle.gather_pages(to_host_u16(vref_p), table_np, P, S)
+        khat, vhat = [], []
+        for i, bl in enumerate(bits):
+            khat.append(oracle.reconstruct(kr, oracle.gather_pages(to_host_words(kc[i]), table_np, P, S),
+                                           oracle.gather_pages(to_host_u16(ks[i]), table_np, P, S), bl))
+            vhat.append(oracle.reconstruct(vr, oracle.gather_pages(to_host_words(vc[i]), table_np, P, S),
+                                           oracle.gather_pages(to_host_u16(vs[i]), table_np, P, S), bl))
+        khat.append(oracle.bf16_to_f64(kr))
+        vhat.append(oracle.bf16_to_f64(vr))
+        expect = oracle.decode_attn_varlen(q, khat, vhat, lens_now, tail_k, tail_v)
+        assert_attn_close(out.cpu().numpy(), expect)
+        pos = torch.from_numpy(lens_now).to(DEV)
+        for codes, scales, refp, tail in ((kc, ks, kref_p, tail_k), (vc, vs, vref_p, tail_v)):
+            rq.encode_append_paged([to_dev(tail[l]) for l in range(len(bits))], to_dev(tail[-1]), bits, pos, table,
+                                   refp, codes, scales)
+        lens_now = lens_now + 1
+    torch.cuda.synchronize()
+    kr = oracle.gather_pages(to_host_u16(kref_p), table_np, P, S)
+    for b in range(B):
+        n = int(lens_now[b])
+        np.testing.assert_array_equal(kr[b, :, :n], kl[-1][b, :, :n])
+        for i, bl in enumerate(bits):
+            cw = oracle.gather_pages(to_host_words(kc[i]), table_np, P, S)
+            cs = oracle.gather_pages(to_host_u16(ks[i]), table_np, P, S)
+            ow, os_ = oracle.encode(kl[i][b, :, :n], kl[-1][b, :, :n], bl)
+            compare_codes(cw[b, :, :n], cs[b, :, :n], ow, os_, kl[i][b, :, :n], kl[-1][b, :, :n], bl)
+
+
+def test_varlen_ignores_non_finite_bits_past_each_prefix():
+    """Contiguous cache: positions at and past seq_lens[b] hold NaN / Inf bit
+    patterns; they take no weight and cannot reach the output."""
+    rng = np.random.default_rng(17)
+    bits_per_loop = (2, 4, 0)
+    B, H, S, d = 4, 2, 256, 128
+    lens = np.array([1, 63, 100, 255], dtype=np.int32)
+    kref, vref, res = _dense_cache(rng, B, H, S, d, bits_per_loop)
+    kh, vh = _hat(kref, vref, res, bits_per_loop)
+    past = np.arange(S)[None, :] >= lens[:, None]  # [B, S]
+    mask = past[:, None, :]
+    kref[np.broadcast_to(mask, kref.shape[:3])] = BF16_NAN
+    vref[np.broadcast_to(mask, vref.shape[:3])] = BF16_NAN
+    views = []
+    for l, bl in enumerate(bits_per_loop):
+        if bl:
+            (kw, ks), (vw, vs) = res[l]
+            kw, ks, vw, vs = kw.copy(), ks.copy(), vw.copy(), vs.copy()
+            for arr, val in ((ks, F16_INF), (vs, F16_INF)):
+                arr[np.broadcast_to(mask, arr.shape[:3])] = val
+            views.append(rq.LoopView(bl, words_to_dev(kw), to_dev(ks, torch.float16), words_to_dev(vw),
+                                     to_dev(vs, torch.float16)))
+        else:
+            views.append(rq.LoopView(0))
+    q = _bf16(rng, (3, B, 8, d))
+    out = rq.decode_attn_varlen(to_dev(q), to_dev(kref), to_dev(vref), views,
+                                seq_lens=torch.from_numpy(lens).to(DEV)).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    assert_attn_close(out, oracle.decode_attn_varlen(q, kh, vh, lens))

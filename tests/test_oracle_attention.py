@@ -119,3 +119,26 @@ def test_varlen_special_cases():
     for b in range(B):
         for h in range(Hq):
             np.testing.assert_allclose(out[0, b, h], vh[0][b, 0, 0], rtol=1e-15)
+
+
+def test_gather_pages_worked_example():
+    """Two sequences, blocks of two positions: sequence 0 uses blocks 2 then 0,
+    sequence 1 uses block 1 and an entry that is not a block (-1)."""
+    pages = np.arange(3 * 1 * 2).reshape(3, 1, 2)  # block k holds positions (2k, 2k+1) of value
+    table = np.array([[2, 0], [1, -1]])
+    got = oracle.gather_pages(pages, table, 2, 4)
+    np.testing.assert_array_equal(got[0, 0], [4, 5, 0, 1])
+    np.testing.assert_array_equal(got[1, 0], [2, 3, 0, 0])
+
+
+def test_gather_pages_inverts_a_scatter():
+    rng = np.random.default_rng(3)
+    B, H, S, P, D = 3, 2, 256, 64, 5
+    dense = rng.standard_normal((B, H, S, D))
+    perm = rng.permutation(B * S // P + 2)  # two spare blocks
+    table = perm[: B * S // P].reshape(B, S // P)
+    pages = np.full((len(perm), H, P, D), np.nan)
+    for b in range(B):
+        for j in range(S // P):
+            pages[table[b, j]] = dense[b, :, j * P:(j + 1) * P]
+    np.testing.assert_array_equal(oracle.gather_pages(pages, table, P, S), dense)
