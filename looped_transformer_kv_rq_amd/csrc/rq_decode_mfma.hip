@@ -884,72 +884,69 @@ void rq_decode_partial_mfma(DecodeArgs a) {
   }
 
   // ------------------------------------------------ merge the four waves
-  // Each wave leaves (m, l) and one accumulator per row in its LDS slot; the
-  // block sums the slots in wave order (reproducible) into the partial record.
-  // The reference and residual accumulators go through the slots one after
-  // the other, so the merge needs 4 * NR * (D + 2) floats of LDS.
-  constexpr int SREC = D + 2;
+  // Each wave leaves its record for every row, [m, l, o_ref[D], o_res[D]] (the
+  // residual part only with residual loops), in its LDS slot. Then each wave
+  // merges whole rows (rows wave, wave + 4, ...), its lanes across the record:
+  // the slots are summed in wave order (reproducible), each scaled by
+  // 2^(m_w - max m), and the result is the row's partial record. The merge
+  // needs 4 * NR * (2D + 2) floats of LDS.
+  constexpr int SREC = RESID ? 2 * D + 2 : D + 2;  // record floats this launch writes
   __syncthreads();
   float* slots = reinterpret_cast<float*>(smem);
-  float* fac = slots + 4 * NR * SREC;  // [NR][5]: max, 4 wave factors
-#pragma unroll
-  for (int pass = 0; pass < (RESID ? 2 : 1); ++pass) {
+  {
     float* slot = slots + wave * NR * SREC;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       float* rs = slot + (16 * nb + m) * SREC;
-      if (pass == 0) {
-        float ls = l_run[nb];
-        ls += __shfl_xor(ls, 16);
-        ls += __shfl_xor(ls, 32);
-        if (g == 0) {
-          rs[0] = m_run[nb];
-          rs[1] = ls;
-        }
+      float ls = l_run[nb];
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      if (g == 0) {
+        rs[0] = m_run[nb];
+        rs[1] = ls;
+      }
 #pragma unroll
-        for (int hh = 0; hh < NH; ++hh)
+      for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rs[2 + 64 * hh + 4 * (4 * g + i) + r] = o_ref[nb][hh][r][i];
-      } else {
+          for (int i = 0; i < 4; ++i) rs[2 + 64 * hh + 4 * (4 * g + i) + r] = o_ref[nb][hh][r][i];
+      if constexpr (RESID) {
 #pragma unroll
         for (int k = 0; k < 2 * NG; ++k)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) rs[2 + 16 * k + 4 * g + i] = o_res[nb][k][i];
+          for (int i = 0; i < 4; ++i) rs[2 + D + 16 * k + 4 * g + i] = o_res[nb][k][i];
       }
     }
-    __syncthreads();
-    if (pass == 0 && threadIdx.x < NR) {
-      const float* s0 = slots + threadIdx.x * SREC;
-      float mm = -INFINITY;
-      for (int w = 0; w < 4; ++w) mm = fmaxf(mm, s0[w * NR * SREC]);
-      fac[threadIdx.x * 5] = mm;
-      for (int w = 0; w < 4; ++w) {
-        const float mw = s0[w * NR * SREC];
-        fac[threadIdx.x * 5 + 1 + w] = mw == -INFINITY ? 0.0f : exp2f(mw - mm);
+  }
+  __syncthreads();
+  for (int r = wave; r < R; r += 4) {
+    const float* s0 = slots + r * SREC;
+    float mw[4], mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = s0[w * NR * SREC];
+      mm = fmaxf(mm, mw[w]);
+    }
+    float fw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) fw[w] = mw[w] == -INFINITY ? 0.0f : exp2f(mw[w] - mm);
+    const int loop = a.loop_id[r / G] + z;
+    const int hq = kvh * G + r % G;
+    float* dst = a.ws + ((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.rec_splits + a.split_base + split) * REC;
+#pragma unroll
+    for (int j = 0; j * 64 < SREC; ++j) {
+      const int e = lane + 64 * j;
+      if (e < SREC) {
+        float val = mm;
+        if (e > 0) {
+          val = 0.0f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) val = fmaf(fw[w], s0[w * NR * SREC + e], val);
+        }
+        dst[e] = val;
       }
     }
-    if (pass == 0) __syncthreads();
-    // record elements of this pass: [m, l, o_ref] or [o_res]
-    const int e0 = pass == 0 ? 0 : D + 2;
-    for (int i = threadIdx.x; i < R * SREC; i += 256) {
-      const int r = i / SREC, e = i % SREC;
-      if (pass == 1 && e >= D) continue;
-      const int loop = a.loop_id[r / G] + z;
-      const int hq = kvh * G + r % G;
-      float* dst = a.ws + ((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.rec_splits + a.split_base + split) * REC + e0;
-      const float* s0 = slots + r * SREC + (pass == 0 ? e : 2 + e);
-      float val;
-      if (pass == 0 && e == 0) {
-        val = fac[r * 5];
-      } else {
-        val = 0.0f;
-        for (int w = 0; w < 4; ++w) val = fmaf(fac[r * 5 + 1 + w], s0[w * NR * SREC], val);
-      }
-      dst[e] = val;
-    }
-    __syncthreads();  // slots are rewritten by the next pass
   }
   // Without residual loops the record ends after o_ref, unless the call's
   // combine reads residual accumulators (other launches of the call carry
@@ -982,9 +979,9 @@ int query_prep_bytes(int head_dim) {
 }
 
 // LDS bytes of one block: the larger of the merge slots and 4 wave tiles
-static int block_lds_bytes(int d, int nb, int wave_bytes) {
+static int block_lds_bytes(int d, int nb, int wave_bytes, bool residual) {
   const int nr = 16 * nb;
-  const int merge = (4 * nr * (d + 2) + 5 * nr) * 4;
+  const int merge = 4 * nr * (residual ? 2 * d + 2 : d + 2) * 4;  // every wave's records of every row
   const int tiles = 4 * wave_bytes;
   return merge > tiles ? merge : tiles;
 }
@@ -1010,7 +1007,7 @@ static void launch_mfma_dp(const DecodeArgs& a, dim3 grid, int lds, bool residua
 template <int D, int NB>
 static void launch_mfma_d(DecodeArgs a, dim3 grid, bool residual, hipStream_t stream) {
   a.lds_wave_bytes = decode_wave_lds_bytes(D, a.bits, residual ? a.n_loops_launch : 0);
-  const int lds = block_lds_bytes(D, NB, a.lds_wave_bytes);
+  const int lds = block_lds_bytes(D, NB, a.lds_wave_bytes, residual);
   if (a.block_table != nullptr) launch_mfma_dp<D, NB, true>(a, grid, lds, residual, stream);
   else launch_mfma_dp<D, NB, false>(a, grid, lds, residual, stream);
 }
