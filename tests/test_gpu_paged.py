@@ -291,3 +291,60 @@ def test_varlen_ignores_non_finite_bits_past_each_prefix():
                                 seq_lens=torch.from_numpy(lens).to(DEV)).cpu().numpy()
     assert np.all(np.isfinite(out))
     assert_attn_close(out, oracle.decode_attn_varlen(q, kh, vh, lens))
+
+
+def test_serving_step_full_size_sampled_rows():
+    """The launches the benchmark's serving legs time, at full size: the
+    l4_b16_s4k cache encoded on the GPU, prefix lengths drawn in [S/2, S) as
+    the benchmark draws them, one bf16 tail position per loop, decoded over the
+    dense cache and over a copy in 512 shuffled blocks of 128 positions;
+    sampled (batch, kv head) rows against the oracle."""
+    w = workloads.WORKLOADS["l4_b16_s4k"]
+    bits = [b for b in w.bits if b]
+    P, nbs = 128, w.seq_len // 128
+    kx = [to_dev(x) for x in workloads.kv_tensors(w, workloads.TENSOR_K)]
+    vx = [to_dev(x) for x in workloads.kv_tensors(w, workloads.TENSOR_V)]
+    kc, ks = rq.encode(kx[:-1], kx[-1], bits)
+    vc, vs = rq.encode(vx[:-1], vx[-1], bits)
+    views = [rq.LoopView(b, kc[i], ks[i], vc[i], vs[i]) for i, b in enumerate(bits)] + [rq.LoopView(0)]
+    lens = np.random.default_rng(w.seed).integers(w.seq_len // 2, w.seq_len, size=w.batch).astype(np.int32)
+    lens_d = torch.from_numpy(lens).to(DEV)
+    tk = [x[:, :, :1].contiguous() for x in kx]
+    tv = [x[:, :, :1].contiguous() for x in vx]
+    q_bits = workloads.q_tensor(w)
+    q = to_dev(q_bits)
+    dense = rq.decode_attn_varlen(q, kx[-1], vx[-1], views, seq_lens=lens_d, tail_k=tk, tail_v=tv).cpu().numpy()
+    perm = torch.from_numpy(np.random.default_rng(w.seed + 1).permutation(w.batch * nbs)).to(DEV)
+    table = perm.view(w.batch, nbs).to(torch.int32).contiguous()
+
+    def paged(t):
+        blocks = t.view(w.batch, w.n_kv_heads, nbs, P, t.shape[-1]).permute(0, 2, 1, 3, 4)
+        blocks = blocks.reshape(w.batch * nbs, w.n_kv_heads, P, t.shape[-1])
+        out = torch.empty_like(blocks)
+        out[perm] = blocks
+        return out
+
+    pviews = [rq.LoopView(b, paged(kc[i]), paged(ks[i]), paged(vc[i]), paged(vs[i])) for i, b in enumerate(bits)]
+    pviews.append(rq.LoopView(0))
+    pag = rq.decode_attn_paged(q, paged(kx[-1]), paged(vx[-1]), pviews, table, seq_lens=lens_d, tail_k=tk,
+                               tail_v=tv).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.array_equal(dense, pag)  # the same cache, dense or paged: identical results
+    g = w.group_size
+    for (b, h) in [(0, 0), (7, 3), (15, 7)]:
+        n = int(lens[b])
+        k_st = workloads.kv_rows_all_loops(w, b, h, workloads.TENSOR_K)
+        v_st = workloads.kv_rows_all_loops(w, b, h, workloads.TENSOR_V)
+        for l in range(w.n_loops):
+            if w.bits[l]:
+                # the residual loops are loops 0 .. L-2, in order
+                k = oracle.reconstruct(k_st[-1], to_host_words(kc[l][b, h]), to_host_u16(ks[l][b, h]), w.bits[l])
+                v = oracle.reconstruct(v_st[-1], to_host_words(vc[l][b, h]), to_host_u16(vs[l][b, h]), w.bits[l])
+            else:
+                k, v = oracle.bf16_to_f64(k_st[-1]), oracle.bf16_to_f64(v_st[-1])
+            k = np.concatenate([k[:n], oracle.bf16_to_f64(k_st[l][:1])])
+            v = np.concatenate([v[:n], oracle.bf16_to_f64(v_st[l][:1])])
+            qq = oracle.bf16_to_f64(q_bits[l, b, h * g:(h + 1) * g])
+            assert_attn_close(dense[l, b, h * g:(h + 1) * g], oracle.attention(qq, k, v, 1.0 / np.sqrt(w.head_dim)))
+    del kx, vx, kc, ks, vc, vs
+    torch.cuda.empty_cache()
