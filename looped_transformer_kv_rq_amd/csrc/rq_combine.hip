@@ -26,20 +26,49 @@ __global__ __launch_bounds__(256) void rq_combine_kernel(CombineArgs a) {
   const int lane = threadIdx.x & 63;
   if (row >= a.n_out) return;
   const float* src = a.ws + row * a.n_splits * REC;
-  float mm = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) mm = fmaxf(mm, src[s * REC]);
-  float lsum = 0.0f, o[DJ], r[DJ];
+  // Splits go in chunks of kChunk whose loads are all issued before any is
+  // used; the running maximum and the sums are rescaled chunk by chunk, in
+  // split order, so the result does not depend on scheduling.
+  constexpr int kChunk = 8;
+  float mm = -INFINITY, lsum = 0.0f, o[DJ], r[DJ];
 #pragma unroll
   for (int j = 0; j < DJ; ++j) o[j] = r[j] = 0.0f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float* p = src + s * REC;
-    const float w = (p[0] == -INFINITY) ? 0.0f : exp2f(p[0] - mm);
-    lsum = fmaf(w, p[1], lsum);
+  for (int s0 = 0; s0 < a.n_splits; s0 += kChunk) {
+    float pm[kChunk], pl[kChunk], po[kChunk][DJ], pr[kChunk][DJ];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const bool in = s0 + c < a.n_splits;
+      const float* p = src + (in ? s0 + c : s0) * REC;
+      pm[c] = in ? p[0] : -INFINITY;
+      pl[c] = p[1];
+#pragma unroll
+      for (int j = 0; j < DJ; ++j) {
+        po[c][j] = p[2 + lane + 64 * j];
+        pr[c][j] = a.residual ? p[2 + D + lane + 64 * j] : 0.0f;
+      }
+    }
+    float cm = mm;
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) cm = fmaxf(cm, pm[c]);
+    if (cm == -INFINITY) continue;  // no position yet
+    const float keep = mm == -INFINITY ? 0.0f : exp2f(mm - cm);
+    lsum *= keep;
 #pragma unroll
     for (int j = 0; j < DJ; ++j) {
-      o[j] = fmaf(w, p[2 + lane + 64 * j], o[j]);
-      if (a.residual) r[j] = fmaf(w, p[2 + D + lane + 64 * j], r[j]);
+      o[j] *= keep;
+      r[j] *= keep;
     }
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const float w = pm[c] == -INFINITY ? 0.0f : exp2f(pm[c] - cm);
+      lsum = fmaf(w, pl[c], lsum);
+#pragma unroll
+      for (int j = 0; j < DJ; ++j) {
+        o[j] = fmaf(w, po[c][j], o[j]);
+        r[j] = fmaf(w, pr[c][j], r[j]);
+      }
+    }
+    mm = cm;
   }
   if (a.residual) {
     // unnormalised transform: index bit 6 in the lane, bits 0..5 across lanes
