@@ -212,12 +212,27 @@ __global__ __launch_bounds__(256) void rq_query_prep(QueryPrepArgs a) {
       v[j] = upper ? p - v[j] : v[j] + p;
     }
   }
-  // fp16 of the normalised value; the offsets sum exactly these values
+  // fp16 of the normalised value; the offsets sum exactly these values, a
+  // group (32 coordinates: lane / 32 of value j) at a time across the half wave
+  const float off = bits > 0 ? (float)(1 << bits) + (float)(1 << (bits - 1)) - 0.5f : 0.0f;
+  float gsum[PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) buf[wave][lane + 64 * j] = (float)(_Float16)(v[j] * RsqrtD<D>::v);
+  for (int j = 0; j < PER; ++j) {
+    const float h = (float)(_Float16)(v[j] * RsqrtD<D>::v);
+    buf[wave][lane + 64 * j] = h;
+    float sum = h;
+#pragma unroll
+    for (int st = 1; st < 32; st <<= 1) sum += __shfl_xor(sum, st);
+    gsum[j] = sum;
+  }
   __syncthreads();
   if (!active) return;
   unsigned char* rec = a.out + row * MfmaGeom<D>::PREP_BYTES;
+  // qoff[ks] for ks = 2 j + lane / 32, written by lanes 0 and 32
+  if ((lane & 31) == 0) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) reinterpret_cast<float*>(rec + 2 * D)[2 * j + (lane >> 5)] = -off * gsum[j];
+  }
   // operand-ordered fp16 values: lane -> (ks, g) = (lane / 4, lane % 4) for lane < 4 NG
   if (lane < 4 * NG) {
     const int ks = lane >> 2, g = lane & 3;
@@ -229,13 +244,7 @@ __global__ __launch_bounds__(256) void rq_query_prep(QueryPrepArgs a) {
     }
     *reinterpret_cast<uint4*>(rec + 16 * (4 * ks + g)) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  if (lane < NG) {
-    float s = 0.0f;
-    for (int d = 0; d < 32; ++d) s += buf[wave][32 * lane + d];
-    // 2^b + 2^(b-1) - 1/2 (unused for a reference-only loop)
-    const float off = bits > 0 ? (float)(1 << bits) + (float)(1 << (bits - 1)) - 0.5f : 0.0f;
-    reinterpret_cast<float*>(rec + 2 * D)[lane] = -off * s;
-  }
+
 }
 
 // ---------------------------------------------------------------------------
