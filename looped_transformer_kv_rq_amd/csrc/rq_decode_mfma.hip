@@ -180,71 +180,103 @@ __host__ __device__ constexpr int rs_coord(int ks, int g, int e) {
   return 32 * ks + 16 * (g >> 1) + 4 * (g & 1) + (e >> 1) + 8 * (e & 1);
 }
 
-// One wave per query row (loop, b, hq): writes the fp16 normalised rotation
-// H q in operand order (16 bytes per (ks, g)) and
+// Four lanes per query row (loop, b, hq), sixteen rows per wave. Lane g of a
+// row loads the query in residual-score operand order: coordinates
+// rs_coord(ks, g, 2i + p) = base + i + 8p (base = 32 ks + 16 (g >> 1) + 4 (g & 1))
+// as x[ks][p][i]. The normalised Walsh-Hadamard transform runs over coordinate
+// bits 0, 1, 3 and the k-step bits in registers and over bits 2 and 4 (lane
+// bits 0 and 1) by DPP quad permutes. The record holds the fp16 rotated values
+// in operand order (16 bytes per (ks, g)) and
 // qoff[ks] = -(2^b + 2^(b-1) - 1/2) * (sum of the group's fp16 values).
 template <int D>
-__global__ __launch_bounds__(256) void rq_query_prep(QueryPrepArgs a) {
+__global__ __launch_bounds__(64) void rq_query_prep(QueryPrepArgs a) {
   constexpr int NG = D / 32;
-  constexpr int PER = D / 64;  // coordinates per lane: lane + 64 j
-  __shared__ float buf[4][D];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const int lane = threadIdx.x;
+  const int g = lane & 3;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (lane >> 2);
   const bool active = row < a.n_rows;
   const int64_t rr = active ? row : 0;
   const int loop = (int)(rr / ((int64_t)a.batch * a.n_q_heads));
   const int bits = a.bits[loop];
-  float v[PER];
+  const uint16_t* qr = a.q + rr * D + 16 * (g >> 1) + 4 * (g & 1);
+  float x[NG][2][4];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) v[j] = __uint_as_float((uint32_t)a.q[rr * D + lane + 64 * j] << 16);
-  // butterflies on bit 6 (in lane) and bits 0..5 (across lanes)
-  if constexpr (PER == 2) {
-    const float x = v[0], y = v[1];
-    v[0] = x + y;
-    v[1] = x - y;
-  }
+  for (int ks = 0; ks < NG; ++ks)
 #pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const bool upper = (lane & s) != 0;
+    for (int pp = 0; pp < 2; ++pp) {
+      const uint2 u = *reinterpret_cast<const uint2*>(qr + 32 * ks + 8 * pp);
+      x[ks][pp][0] = bf16_lo(u.x);
+      x[ks][pp][1] = bf16_hi(u.x);
+      x[ks][pp][2] = bf16_lo(u.y);
+      x[ks][pp][3] = bf16_hi(u.y);
+    }
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const float p = __shfl_xor(v[j], s);
-      v[j] = upper ? p - v[j] : v[j] + p;
+  for (int ks = 0; ks < NG; ++ks) {
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+      for (int st = 1; st < 4; st <<= 1)  // coordinate bits 0 and 1
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!(i & st)) {
+            const float u = x[ks][pp][i], w = x[ks][pp][i | st];
+            x[ks][pp][i] = u + w;
+            x[ks][pp][i | st] = u - w;
+          }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // coordinate bit 3
+      const float u = x[ks][0][i], w = x[ks][1][i];
+      x[ks][0][i] = u + w;
+      x[ks][1][i] = u - w;
     }
   }
-  // fp16 of the normalised value; the offsets sum exactly these values, a
-  // group (32 coordinates: lane / 32 of value j) at a time across the half wave
+#pragma unroll
+  for (int st = 1; st < NG; st <<= 1)  // coordinate bits 5 (and 6)
+#pragma unroll
+    for (int ks = 0; ks < NG; ++ks)
+      if (!(ks & st))
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float u = x[ks][pp][i], w = x[ks | st][pp][i];
+            x[ks][pp][i] = u + w;
+            x[ks | st][pp][i] = u - w;
+          }
+  // coordinate bit 2 (lane bit 0), then bit 4 (lane bit 1): the lower lane
+  // keeps own + partner, the upper lane partner - own
+  const float s1 = (g & 1) ? -1.0f : 1.0f, s2 = (g & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int ks = 0; ks < NG; ++ks)
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[ks][pp][i] = fmaf(s1, x[ks][pp][i], quad_xor<1>(x[ks][pp][i]));
+#pragma unroll
+  for (int ks = 0; ks < NG; ++ks)
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[ks][pp][i] = fmaf(s2, x[ks][pp][i], quad_xor<2>(x[ks][pp][i]));
   const float off = bits > 0 ? (float)(1 << bits) + (float)(1 << (bits - 1)) - 0.5f : 0.0f;
-  float gsum[PER];
+  unsigned char* rec = a.out + rr * MfmaGeom<D>::PREP_BYTES;
+  float qo = 0.0f;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const float h = (float)(_Float16)(v[j] * RsqrtD<D>::v);
-    buf[wave][lane + 64 * j] = h;
-    float sum = h;
-#pragma unroll
-    for (int st = 1; st < 32; st <<= 1) sum += __shfl_xor(sum, st);
-    gsum[j] = sum;
-  }
-  __syncthreads();
-  if (!active) return;
-  unsigned char* rec = a.out + row * MfmaGeom<D>::PREP_BYTES;
-  // qoff[ks] for ks = 2 j + lane / 32, written by lanes 0 and 32
-  if ((lane & 31) == 0) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) reinterpret_cast<float*>(rec + 2 * D)[2 * j + (lane >> 5)] = -off * gsum[j];
-  }
-  // operand-ordered fp16 values: lane -> (ks, g) = (lane / 4, lane % 4) for lane < 4 NG
-  if (lane < 4 * NG) {
-    const int ks = lane >> 2, g = lane & 3;
+  for (int ks = 0; ks < NG; ++ks) {
     uint32_t w[4];
+    float sum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f16x2_t h = {(_Float16)buf[wave][rs_coord(ks, g, 2 * i)], (_Float16)buf[wave][rs_coord(ks, g, 2 * i + 1)]};
-      w[i] = __builtin_bit_cast(uint32_t, h);
+      const _Float16 h0 = (_Float16)(x[ks][0][i] * RsqrtD<D>::v), h1 = (_Float16)(x[ks][1][i] * RsqrtD<D>::v);
+      w[i] = __builtin_bit_cast(uint32_t, f16x2_t{h0, h1});
+      sum += (float)h0 + (float)h1;
     }
-    *reinterpret_cast<uint4*>(rec + 16 * (4 * ks + g)) = make_uint4(w[0], w[1], w[2], w[3]);
+    sum += quad_xor<1>(sum);
+    sum += quad_xor<2>(sum);
+    if (ks % 4 == g) qo = -off * sum;
+    if (active) *reinterpret_cast<uint4*>(rec + 16 * (4 * ks + g)) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-
+  if (active && g < NG) reinterpret_cast<float*>(rec + 2 * D)[g] = qo;
 }
 
 // ---------------------------------------------------------------------------
@@ -1035,9 +1067,9 @@ hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, int n_z, boo
 }
 
 hipError_t launch_query_prep(const QueryPrepArgs& a, int head_dim, hipStream_t stream) {
-  const dim3 grid((unsigned)((a.n_rows + 3) / 4));
-  if (head_dim == 128) hipLaunchKernelGGL(rq_query_prep<128>, grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(rq_query_prep<64>, grid, dim3(256), 0, stream, a);
+  const dim3 grid((unsigned)((a.n_rows + 15) / 16));
+  if (head_dim == 128) hipLaunchKernelGGL(rq_query_prep<128>, grid, dim3(64), 0, stream, a);
+  else hipLaunchKernelGGL(rq_query_prep<64>, grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
