@@ -24,6 +24,10 @@ measured kernel):
 * the rotation-only baseline (rq_encode_rotonly of every loop of K with no
   reference): its encode rate, and its per-loop reconstruction error and
   cache bytes beside those of the residual codec.
+* first of all, the peak-batch workload (8 loops, 4 / 16 heads, 16K tokens):
+  the batch grows until the cache fills about 200 GB of HBM, for the residual
+  cache and for the bf16-KV baseline at its own largest batch; decode tokens/s
+  of both (one decode call = the next token of every sequence).
 
 `roofline` covers the kernel that takes the largest share of the step (the
 encoder). Its achieved rate is algorithmic bytes per launch divided by the
@@ -209,6 +213,88 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 5}))
 
 
+def peak_batch_leg(rq, torch, dev, reps):
+    """The peak-batch workload: the batch grows until the cache fills about
+    200 GB of HBM (less if the device has less free), for the residual cache
+    (INT4 loop 0, INT2 loops 1-6, bf16 reference) and for the bf16-KV baseline
+    at its own largest batch. One decode call produces the next token of every
+    sequence (all 8 loops), so tokens/s = batch / call time. The batch repeats
+    eight host-drawn entries (decode time does not depend on the values)."""
+    w8 = workloads.WORKLOADS["peak_batch"].with_batch(workloads.PEAK_TILE)
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    budget = min(workloads.PEAK_CACHE_BUDGET, free - 16 * 2**30)
+    b_rq = workloads.peak_batch(workloads.cache_bytes_per_sequence(w8, w8.bits), budget)
+    b_bf = workloads.peak_batch(workloads.bf16_cache_bytes_per_sequence(w8, w8.n_loops), budget)
+    if b_bf < workloads.PEAK_TILE:
+        return {"skipped": f"{free / 1e9:.0f} GB free on the device"}
+
+    def dev16(bits_u16, dtype=torch.bfloat16):
+        return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).to(dev).view(dtype)
+
+    def words(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(dev)
+
+    tile = workloads.tile_batch
+    kref8 = dev16(workloads.ref_tensor(w8, workloads.TENSOR_K))
+    vref8 = dev16(workloads.ref_tensor(w8, workloads.TENSOR_V))
+    q8 = workloads.q_tensor(w8)
+    stream = torch.cuda.current_stream(dev)
+    Ev = torch.cuda.Event
+
+    def timed(fn):
+        fn(); fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = Ev(enable_timing=True), Ev(enable_timing=True)
+            a.record(stream); fn(); b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return statistics.median(ts)
+
+    def q_for(batch):
+        return torch.stack([tile(dev16(q8[l]), batch) for l in range(w8.n_loops)])
+
+    out = {"workload": "peak_batch", "cache_budget_GB": budget / 1e9}
+    # residual cache
+    kref, vref = tile(kref8, b_rq), tile(vref8, b_rq)
+    views = []
+    for l in range(w8.n_loops):
+        if w8.bits[l]:
+            (kw, ksc), (vw, vsc) = workloads.packed_tensors(w8, 0, l), workloads.packed_tensors(w8, 1, l)
+            views.append(rq.LoopView(w8.bits[l], tile(words(kw), b_rq), tile(dev16(ksc, torch.float16), b_rq),
+                                     tile(words(vw), b_rq), tile(dev16(vsc, torch.float16), b_rq)))
+        else:
+            views.append(rq.LoopView(0))
+    q = q_for(b_rq)
+    o = torch.empty((w8.n_loops, b_rq, w8.n_q_heads, w8.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(rq.decode_workspace_bytes(b_rq, w8.n_kv_heads, w8.seq_len, w8.head_dim, w8.n_q_heads,
+                                               w8.n_loops), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: rq.decode_attn(q, kref, vref, views, out=o, workspace=ws, stream=stream))
+    wb = w8.with_batch(b_rq)
+    nbytes = decode_bytes(wb, list(w8.bits))
+    out["rq"] = {"batch": b_rq, "cache_GB": b_rq * workloads.cache_bytes_per_sequence(w8, w8.bits) / 1e9,
+                 "ms": ms, "tokens_per_s": b_rq / (ms * 1e-3), "GBps": nbytes / (ms * 1e-3) / 1e9,
+                 "frac_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    del kref, vref, views, q, o, ws
+    torch.cuda.empty_cache()
+    # bf16-KV baseline: every loop's K and V in its own allocation
+    ks = [tile(kref8, b_bf) for _ in range(w8.n_loops)]
+    vs = [tile(vref8, b_bf) for _ in range(w8.n_loops)]
+    q = q_for(b_bf)
+    o = torch.empty((w8.n_loops, b_bf, w8.n_q_heads, w8.head_dim), dtype=torch.float32, device=dev)
+    ms = timed(lambda: rq.decode_attn_bf16(q, ks, vs, out=o, stream=stream))
+    nbytes = bf16_decode_bytes(w8.with_batch(b_bf), w8.n_loops)
+    out["bf16"] = {"batch": b_bf, "cache_GB": b_bf * workloads.bf16_cache_bytes_per_sequence(w8, w8.n_loops) / 1e9,
+                   "ms": ms, "tokens_per_s": b_bf / (ms * 1e-3), "GBps": nbytes / (ms * 1e-3) / 1e9,
+                   "frac_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    del ks, vs, q, o
+    torch.cuda.empty_cache()
+    out["rq_over_bf16_tokens_per_s"] = out["rq"]["tokens_per_s"] / out["bf16"]["tokens_per_s"]
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +304,7 @@ def main():
     ap.add_argument("--reps", type=int, default=20, help="repetitions of each side measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-step", action="store_true", help="time the step only (for profiling runs)")
+    ap.add_argument("--no-peak-batch", action="store_true", help="skip the peak-batch leg (about 200 GB of HBM)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy, five times: the reference kernel "
                          "whose FETCH_SIZE / WRITE_SIZE readings calibrate the HBM byte counters")
@@ -246,6 +333,8 @@ def main():
     rq._load()  # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    # first, while nothing else holds device memory
+    peak = None if (args.only_step or args.no_peak_batch) else peak_batch_leg(rq, torch, dev, 5)
 
     def up(bits_u16):
         return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -600,6 +689,8 @@ def main():
             "what": "serving_step over a block-paged cache (shuffled blocks of 128 positions)",
         }
         del kref_p, vref_p, kc_p, ks_p, vc_p, vs_p
+    if peak is not None:
+        result["peak_batch"] = peak
     if cpu is not None:
         result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)

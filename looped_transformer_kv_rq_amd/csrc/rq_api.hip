@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "rq.h"
 #include "rq_internal.h"
 
@@ -396,45 +398,74 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
       ++nl;
     }
     if (nl == 0) nl = 1;  // G == 32: one loop per launch
-    DecodeArgs a{};
-    fill_common(a, shape, n_q_heads, q, softmax_scale, plan, workspace);
-    a.rec_splits = rec_splits;
-    a.seq_lens = seq_lens;
-    a.qprep = prep;
-    a.k[0] = k_ref;
-    a.v[0] = v_ref;
-    if (pages != nullptr) {
-      a.block_table = pages->block_table;
-      a.max_blocks = pages->max_blocks;
-      a.log2_block = log2_of(pages->block_size);
-      a.n_blocks = pages->n_blocks;
-    }
-    a.n_loops_launch = nl;
-    a.n_rows = nl * G;
-    bool residual = false;
-    // slots in the order INT8, INT4, INT3, INT2, reference-only: the kernel
-    // runs one branch-free loop per width
-    int li = 0;
-    for (const int want : {8, 4, 3, 2, 0}) {
+    // More than 16 rows whose loops each fit 16: two argument sets of at most
+    // 16 / G loops (one 16-row MFMA block each), the loops dealt to balance
+    // the LDS each set stages per tile. Otherwise one set.
+    int members[kMaxSets][kMaxLoops];
+    int n_members[kMaxSets] = {0, 0};
+    int n_sets = 1;
+    if (nl * G > 16 && G <= 16) {
+      n_sets = 2;
+      const int cap = 16 / G;
+      int order[kMaxLoops];
+      for (int j = 0; j < nl; ++j) order[j] = base + j;
+      std::stable_sort(order, order + nl, [&](int x, int y) {
+        return decode_loop_lds_bytes(shape->head_dim, loops[x].bits) > decode_loop_lds_bytes(shape->head_dim, loops[y].bits);
+      });
+      int bytes[kMaxSets] = {0, 0};
       for (int j = 0; j < nl; ++j) {
-        const rq_loop_view& lv = loops[base + j];
-        if (lv.bits != want) continue;
-        a.loop_id[li] = base + j;
-        a.bits[li] = lv.bits;
-        a.kc[li] = lv.k_codes;
-        a.ks[li] = lv.k_scales;
-        a.vc[li] = lv.v_codes;
-        a.vs[li] = lv.v_scales;
-        if (want == 8) ++a.n8;
-        if (want == 4) ++a.n4;
-        if (want == 3) ++a.n3;
-        if (want == 2) ++a.n2;
-        residual = residual || lv.bits != 0;
-        ++li;
+        const int t = (n_members[0] < cap && (n_members[1] >= cap || bytes[0] <= bytes[1])) ? 0 : 1;
+        members[t][n_members[t]++] = order[j];
+        bytes[t] += decode_loop_lds_bytes(shape->head_dim, loops[order[j]].bits);
+      }
+    } else {
+      for (int j = 0; j < nl; ++j) members[0][j] = base + j;
+      n_members[0] = nl;
+    }
+    DecodeArgs sets[kMaxSets];
+    bool residual = false;
+    for (int si = 0; si < n_sets; ++si) {
+      DecodeArgs& a = sets[si];
+      a = DecodeArgs{};
+      fill_common(a, shape, n_q_heads, q, softmax_scale, plan, workspace);
+      a.rec_splits = rec_splits;
+      a.seq_lens = seq_lens;
+      a.qprep = prep;
+      a.k[0] = k_ref;
+      a.v[0] = v_ref;
+      if (pages != nullptr) {
+        a.block_table = pages->block_table;
+        a.max_blocks = pages->max_blocks;
+        a.log2_block = log2_of(pages->block_size);
+        a.n_blocks = pages->n_blocks;
+      }
+      a.n_loops_launch = n_members[si];
+      a.n_rows = n_members[si] * G;
+      // slots in the order INT8, INT4, INT3, INT2, reference-only: the kernel
+      // runs one branch-free loop per width
+      int li = 0;
+      for (const int want : {8, 4, 3, 2, 0}) {
+        for (int j = 0; j < n_members[si]; ++j) {
+          const int l = members[si][j];
+          const rq_loop_view& lv = loops[l];
+          if (lv.bits != want) continue;
+          a.loop_id[li] = l;
+          a.bits[li] = lv.bits;
+          a.kc[li] = lv.k_codes;
+          a.ks[li] = lv.k_scales;
+          a.vc[li] = lv.v_codes;
+          a.vs[li] = lv.v_scales;
+          if (want == 8) ++a.n8;
+          if (want == 4) ++a.n4;
+          if (want == 3) ++a.n3;
+          if (want == 2) ++a.n2;
+          residual = residual || lv.bits != 0;
+          ++li;
+        }
       }
     }
-    a.zero_residual = any_residual && !residual;
-    st = hip_status(launch_decode_partial(a, shape->head_dim, 1, residual, s));
+    for (int si = 0; si < n_sets; ++si) sets[si].zero_residual = any_residual && !residual;
+    st = hip_status(launch_decode_partial(sets, n_sets, shape->head_dim, 1, residual, s));
     if (st != RQ_OK) return st;
     base += nl;
   }
@@ -455,7 +486,7 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
     a.n_loops_launch = 1;
     a.n_rows = G;
     a.zero_residual = any_residual;
-    st = hip_status(launch_decode_partial(a, shape->head_dim, n_loops, false, s));
+    st = hip_status(launch_decode_partial(&a, 1, shape->head_dim, n_loops, false, s));
     if (st != RQ_OK) return st;
   }
   return run_combine(shape, n_q_heads, n_loops, rec_splits, static_cast<const float*>(workspace), out,
@@ -533,7 +564,7 @@ int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loop
   a.loop_id[0] = 0;  // blockIdx.y selects the loop
   a.n_loops_launch = 1;
   a.n_rows = G;
-  st = hip_status(launch_decode_partial(a, shape->head_dim, n_loops, false, s));
+  st = hip_status(launch_decode_partial(&a, 1, shape->head_dim, n_loops, false, s));
   if (st != RQ_OK) return st;
   return run_combine(shape, n_q_heads, n_loops, plan.n_splits, static_cast<const float*>(workspace), out, false, s);
 }

@@ -47,6 +47,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "rq_device.h"
 #include "rq_internal.h"
 
@@ -815,10 +817,11 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
 
 // WIDE instantiations also take INT8 and INT3 loops; the others carry no code
 // for them.
-template <int D, int NB, bool RESID, bool WIDE, bool PAGED>
+// SETS: the launch's argument sets (1 or 2); blocks alternate between them.
+template <int D, int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RESID && NB == 2 ? 1 : 2,
                                                                      RESID && NB == 1 ? 2 : 4)))
-void rq_decode_partial_mfma(DecodeArgs a) {
+void rq_decode_partial_mfma(DecodeLaunch launch) {
   using Gm = MfmaGeom<D>;
   constexpr int NG = Gm::NG, NH = Gm::NH;
   constexpr int NR = 16 * NB;
@@ -828,8 +831,10 @@ void rq_decode_partial_mfma(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: tile bases stay scalar
   const int m = lane & 15, g = lane >> 4;
-  const int split = blockIdx.x % a.n_splits;
-  const int bh = blockIdx.x / a.n_splits;
+  const DecodeArgs& a = launch.set[SETS == 1 ? 0 : blockIdx.x % SETS];
+  const int work = blockIdx.x / SETS;
+  const int split = work % a.n_splits;
+  const int bh = work / a.n_splits;
   const int z = blockIdx.y;
   const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
   const int G = a.group, R = a.n_rows, S = a.seq_len;
@@ -1015,6 +1020,8 @@ int decode_wave_lds_bytes(int head_dim, const int32_t* bits, int n_loops) {
   return bytes;
 }
 
+int decode_loop_lds_bytes(int head_dim, int bits) { return loop_lds_bytes(head_dim, bits); }
+
 int query_prep_bytes(int head_dim) {
   return head_dim == 128 ? MfmaGeom<128>::PREP_BYTES : MfmaGeom<64>::PREP_BYTES;
 }
@@ -1027,41 +1034,63 @@ static int block_lds_bytes(int d, int nb, int wave_bytes, bool residual) {
   return merge > tiles ? merge : tiles;
 }
 
-template <int D, int NB, bool RESID, bool WIDE, bool PAGED>
-static void launch_mfma_kernel(const DecodeArgs& a, dim3 grid, int lds, hipStream_t stream) {
+template <int D, int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
+static void launch_mfma_kernel(const DecodeLaunch& l, dim3 grid, int lds, hipStream_t stream) {
   static bool attr_set = false;  // lift the default dynamic-LDS cap once per instantiation
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED, SETS>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxBlockLds);
     attr_set = true;
   }
-  hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED>), grid, dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED, SETS>), grid, dim3(256), lds, stream, l);
 }
 
-template <int D, int NB, bool PAGED>
-static void launch_mfma_dp(const DecodeArgs& a, dim3 grid, int lds, bool residual, hipStream_t stream) {
-  if (!residual) launch_mfma_kernel<D, NB, false, false, PAGED>(a, grid, lds, stream);
-  else if (a.n8 + a.n3 > 0) launch_mfma_kernel<D, NB, true, true, PAGED>(a, grid, lds, stream);
-  else launch_mfma_kernel<D, NB, true, false, PAGED>(a, grid, lds, stream);
+template <int D, int NB, bool PAGED, int SETS>
+static void launch_mfma_dp(const DecodeLaunch& l, dim3 grid, int lds, bool residual, bool wide, hipStream_t stream) {
+  if (!residual) launch_mfma_kernel<D, NB, false, false, PAGED, SETS>(l, grid, lds, stream);
+  else if (wide) launch_mfma_kernel<D, NB, true, true, PAGED, SETS>(l, grid, lds, stream);
+  else launch_mfma_kernel<D, NB, true, false, PAGED, SETS>(l, grid, lds, stream);
 }
 
 template <int D, int NB>
-static void launch_mfma_d(DecodeArgs a, dim3 grid, bool residual, hipStream_t stream) {
-  a.lds_wave_bytes = decode_wave_lds_bytes(D, a.bits, residual ? a.n_loops_launch : 0);
-  const int lds = block_lds_bytes(D, NB, a.lds_wave_bytes, residual);
-  if (a.block_table != nullptr) launch_mfma_dp<D, NB, true>(a, grid, lds, residual, stream);
-  else launch_mfma_dp<D, NB, false>(a, grid, lds, residual, stream);
+static void launch_mfma_d(DecodeLaunch& l, dim3 grid, bool residual, hipStream_t stream) {
+  int lds = 0;
+  bool wide = false;
+  for (int i = 0; i < l.n_sets; ++i) {
+    DecodeArgs& a = l.set[i];
+    a.lds_wave_bytes = decode_wave_lds_bytes(D, a.bits, residual ? a.n_loops_launch : 0);
+    lds = std::max(lds, block_lds_bytes(D, NB, a.lds_wave_bytes, residual));
+    wide = wide || a.n8 + a.n3 > 0;
+  }
+  const bool paged = l.set[0].block_table != nullptr;
+  if (l.n_sets == 2) {  // two sets of at most 16 rows
+    if (paged) launch_mfma_dp<D, 1, true, 2>(l, grid, lds, residual, wide, stream);
+    else launch_mfma_dp<D, 1, false, 2>(l, grid, lds, residual, wide, stream);
+  } else {
+    if (paged) launch_mfma_dp<D, NB, true, 1>(l, grid, lds, residual, wide, stream);
+    else launch_mfma_dp<D, NB, false, 1>(l, grid, lds, residual, wide, stream);
+  }
 }
 
-hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, int n_z, bool residual, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)a.n_splits * a.batch * a.n_kv_heads), n_z);
-  const bool two = a.n_rows > 16;
+hipError_t launch_decode_partial(const DecodeArgs* sets, int n_sets, int head_dim, int n_z, bool residual,
+                                 hipStream_t stream) {
+  if (n_sets < 1 || n_sets > kMaxSets) return hipErrorInvalidValue;
+  DecodeLaunch l{};
+  l.n_sets = n_sets;
+  int rows = 0;
+  for (int i = 0; i < n_sets; ++i) {
+    l.set[i] = sets[i];
+    rows = std::max(rows, sets[i].n_rows);
+  }
+  const DecodeArgs& a = sets[0];
+  const dim3 grid((unsigned)((int64_t)a.n_splits * a.batch * a.n_kv_heads * n_sets), n_z);
+  const bool two = rows > 16;
   if (head_dim == 128) {
-    if (two) launch_mfma_d<128, 2>(a, grid, residual, stream);
-    else launch_mfma_d<128, 1>(a, grid, residual, stream);
+    if (two) launch_mfma_d<128, 2>(l, grid, residual, stream);
+    else launch_mfma_d<128, 1>(l, grid, residual, stream);
   } else {
-    if (two) launch_mfma_d<64, 2>(a, grid, residual, stream);
-    else launch_mfma_d<64, 1>(a, grid, residual, stream);
+    if (two) launch_mfma_d<64, 2>(l, grid, residual, stream);
+    else launch_mfma_d<64, 1>(l, grid, residual, stream);
   }
   return hipGetLastError();
 }

@@ -77,6 +77,17 @@ struct DecodeArgs {
   int32_t zero_residual;                // write a zero residual accumulator (reference-only launch)
 };
 
+// One partial launch holds up to kMaxSets argument sets over the same cache
+// rows, each with its own query rows (at most 16 when there are two) and
+// residual loops. Block x works on set x % n_sets, so the blocks of all sets of
+// one (batch, kv head, split) run side by side and the reference tiles they
+// all stream are read from HBM about once.
+constexpr int kMaxSets = 2;
+struct DecodeLaunch {
+  DecodeArgs set[kMaxSets];
+  int32_t n_sets;
+};
+
 struct CombineArgs {
   const float* ws;
   float* out;
@@ -99,7 +110,10 @@ struct QueryPrepArgs {
 
 hipError_t launch_encode(const EncodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_reconstruct(const ReconstructArgs& a, int head_dim, int bits, int out_bf16, hipStream_t stream);
-hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, int n_z, bool residual, hipStream_t stream);
+// sets[0 .. n_sets): argument sets of one launch (the same shape, splits,
+// cache and paging; their own rows and loops)
+hipError_t launch_decode_partial(const DecodeArgs* sets, int n_sets, int head_dim, int n_z, bool residual,
+                                 hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_query_prep(const QueryPrepArgs& a, int head_dim, hipStream_t stream);
 
@@ -114,5 +128,7 @@ constexpr int kMaxBlockLds = 160 * 1024;
 
 // LDS bytes one decode wave stages per token tile for the given residual loops
 int decode_wave_lds_bytes(int head_dim, const int32_t* bits, int n_loops);
+// LDS bytes one residual loop of the given width adds to that (0 for bits 0)
+int decode_loop_lds_bytes(int head_dim, int bits);
 
 }  // namespace rq

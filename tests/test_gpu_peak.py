@@ -1,0 +1,103 @@
+"""The peak-batch workload at its largest batch, against the oracle on sampled
+rows: the residual cache of 8 loops (INT4 loop 0, INT2 loops 1-6, bf16
+reference) filling about 200 GB of HBM, and the bf16-KV baseline at its own
+largest batch. These are the largest launches the library runs here (row
+offsets past 2^31 elements). The batch is built on the device by repeating
+eight host-drawn entries, so row (b, h) holds the generator's row (b % 8, h)."""
+import numpy as np
+import pytest
+import torch
+
+import looped_transformer_kv_rq_amd as rq
+import oracle
+import workloads
+from rq_parity import assert_attn_close, to_dev, words_to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _budget():
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    return min(workloads.PEAK_CACHE_BUDGET, free - 16 * 2**30)
+
+
+def _rows(batch):
+    return [(0, 0), (batch - 1, 3), (batch // 2 + 3, 1), (1029 % batch, 2)]
+
+
+def _q(q8, batch):
+    return torch.stack([workloads.tile_batch(to_dev(q8[l]), batch) for l in range(q8.shape[0])])
+
+
+def test_peak_batch_rq_decode_sampled_rows():
+    w8 = workloads.WORKLOADS["peak_batch"].with_batch(workloads.PEAK_TILE)
+    batch = workloads.peak_batch(workloads.cache_bytes_per_sequence(w8, w8.bits), _budget())
+    print(f"peak batch rq: B = {batch}", flush=True)
+    assert batch >= 8 * workloads.PEAK_TILE
+    kref8 = workloads.ref_tensor(w8, workloads.TENSOR_K)
+    vref8 = workloads.ref_tensor(w8, workloads.TENSOR_V)
+    res8 = {l: (workloads.packed_tensors(w8, 0, l), workloads.packed_tensors(w8, 1, l))
+            for l in range(w8.n_loops) if w8.bits[l]}
+    q8 = workloads.q_tensor(w8)
+    tile = workloads.tile_batch
+    kref, vref = tile(to_dev(kref8), batch), tile(to_dev(vref8), batch)
+    views = []
+    for l in range(w8.n_loops):
+        if w8.bits[l]:
+            (kw, ks), (vw, vs) = res8[l]
+            views.append(rq.LoopView(w8.bits[l], tile(words_to_dev(kw), batch), tile(to_dev(ks, torch.float16), batch),
+                                     tile(words_to_dev(vw), batch), tile(to_dev(vs, torch.float16), batch)))
+        else:
+            views.append(rq.LoopView(0))
+    out = rq.decode_attn(_q(q8, batch), kref, vref, views)
+    torch.cuda.synchronize()
+    g = w8.group_size
+    rows = _rows(batch)
+    got = np.stack([np.stack([out[l, b, h * g:(h + 1) * g].cpu().numpy() for (b, h) in rows])
+                    for l in range(w8.n_loops)])
+    del out, views, kref, vref
+    torch.cuda.empty_cache()
+    want = np.empty_like(got, dtype=np.float64)
+    scale = 1.0 / np.sqrt(w8.head_dim)
+    for j, (b, h) in enumerate(rows):
+        t = b % workloads.PEAK_TILE
+        for l in range(w8.n_loops):
+            if w8.bits[l]:
+                (kw, ks), (vw, vs) = res8[l]
+                k = oracle.reconstruct(kref8[t, h], kw[t, h], ks[t, h], w8.bits[l])
+                v = oracle.reconstruct(vref8[t, h], vw[t, h], vs[t, h], w8.bits[l])
+            else:
+                k, v = oracle.bf16_to_f64(kref8[t, h]), oracle.bf16_to_f64(vref8[t, h])
+            want[l, j] = oracle.attention(oracle.bf16_to_f64(q8[l, t, h * g:(h + 1) * g]), k, v, scale)
+    assert_attn_close(got, want)
+
+
+def test_peak_batch_bf16_baseline_sampled_rows():
+    """Every loop's K_l / V_l is its own allocation holding the reference's values."""
+    w8 = workloads.WORKLOADS["peak_batch"].with_batch(workloads.PEAK_TILE)
+    batch = workloads.peak_batch(workloads.bf16_cache_bytes_per_sequence(w8, w8.n_loops), _budget())
+    print(f"peak batch bf16: B = {batch}", flush=True)
+    assert batch >= 8 * workloads.PEAK_TILE
+    kref8 = workloads.ref_tensor(w8, workloads.TENSOR_K)
+    vref8 = workloads.ref_tensor(w8, workloads.TENSOR_V)
+    q8 = workloads.q_tensor(w8)
+    kd, vd = to_dev(kref8), to_dev(vref8)
+    ks = [workloads.tile_batch(kd, batch) for _ in range(w8.n_loops)]
+    vs = [workloads.tile_batch(vd, batch) for _ in range(w8.n_loops)]
+    out = rq.decode_attn_bf16(_q(q8, batch), ks, vs)
+    torch.cuda.synchronize()
+    g = w8.group_size
+    rows = _rows(batch)
+    got = np.stack([np.stack([out[l, b, h * g:(h + 1) * g].cpu().numpy() for (b, h) in rows])
+                    for l in range(w8.n_loops)])
+    del out, ks, vs
+    torch.cuda.empty_cache()
+    want = np.empty_like(got, dtype=np.float64)
+    scale = 1.0 / np.sqrt(w8.head_dim)
+    for j, (b, h) in enumerate(rows):
+        t = b % workloads.PEAK_TILE
+        k, v = oracle.bf16_to_f64(kref8[t, h]), oracle.bf16_to_f64(vref8[t, h])
+        for l in range(w8.n_loops):
+            want[l, j] = oracle.attention(oracle.bf16_to_f64(q8[l, t, h * g:(h + 1) * g]), k, v, scale)
+    assert_attn_close(got, want)

@@ -244,3 +244,42 @@ def ref_tensor(w: Workload, tensor: int) -> np.ndarray:
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(fill, rows))
     return out
+
+
+# ---------------------------------------------------------------------------
+# the peak-batch sweep: the batch grows until the cache fills about 200 GB
+# ---------------------------------------------------------------------------
+
+PEAK_CACHE_BUDGET = 200 * 10**9
+PEAK_TILE = 8  # batch entries drawn on the host; a larger batch repeats them in order
+
+
+def cache_bytes_per_sequence(w: Workload, bits_per_loop, with_reference: bool = True) -> int:
+    """K and V cache bytes of one sequence (every KV head and position): the
+    bf16 reference plus, per residual loop of width b, D*b/8 bytes of codes and
+    2*D/32 bytes of scales per vector. A bf16-KV cache passes its loops as
+    zero widths and counts 2*D bytes per loop instead."""
+    d = w.head_dim
+    per = sum(d * b // 8 + 2 * d // GROUP for b in bits_per_loop if b)
+    return 2 * w.n_kv_heads * w.seq_len * ((2 * d if with_reference else 0) + per)
+
+
+def bf16_cache_bytes_per_sequence(w: Workload, n_loops: int) -> int:
+    return 2 * w.n_kv_heads * w.seq_len * 2 * w.head_dim * n_loops
+
+
+def peak_batch(bytes_per_sequence: int, budget: int = PEAK_CACHE_BUDGET, multiple: int = PEAK_TILE) -> int:
+    """The largest batch, a multiple of ``multiple``, whose cache fits ``budget`` bytes."""
+    return int(budget // bytes_per_sequence // multiple * multiple)
+
+
+def tile_batch(src, batch: int):
+    """A [batch, ...] copy of the tensor src [T, ...] on src's device whose
+    entry b is src[b % T] (batch a multiple of T)."""
+    t = src.shape[0]
+    if batch % t:
+        raise ValueError("batch must be a multiple of the tile")
+    rest = tuple(src.shape[1:])
+    out = src.new_empty((batch,) + rest)
+    out.view((batch // t, t) + rest).copy_(src.unsqueeze(0).expand((batch // t, t) + rest))
+    return out
