@@ -817,7 +817,10 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
 
 // WIDE instantiations also take INT8 and INT3 loops; the others carry no code
 // for them.
-// SETS: the launch's argument sets (1 or 2); blocks alternate between them.
+// SETS: the launch's argument sets (1 or 2). With two, the block of set s for
+// work item w is 16 (w / 8) + 8 s + w % 8, so the two blocks of a work item go
+// to the same XCD under the round-robin dispatch and are dispatched close
+// together.
 template <int D, int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RESID && NB == 2 ? 1 : 2,
                                                                      RESID && NB == 1 ? 2 : 4)))
@@ -831,8 +834,12 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: tile bases stay scalar
   const int m = lane & 15, g = lane >> 4;
-  const DecodeArgs& a = launch.set[SETS == 1 ? 0 : blockIdx.x % SETS];
-  const int work = blockIdx.x / SETS;
+  // Two sets: the twin blocks of one work item are 8 apart, so with the
+  // round-robin dispatch over the 8 XCDs they share an XCD and its L2.
+  const int bx = blockIdx.x;
+  const DecodeArgs& a = launch.set[SETS == 1 ? 0 : (bx >> 3) & 1];
+  const int work = SETS == 1 ? bx : ((bx >> 4) << 3) | (bx & 7);
+  if (SETS == 2 && work >= a.n_splits * a.batch * a.n_kv_heads) return;
   const int split = work % a.n_splits;
   const int bh = work / a.n_splits;
   const int z = blockIdx.y;
@@ -1083,7 +1090,8 @@ hipError_t launch_decode_partial(const DecodeArgs* sets, int n_sets, int head_di
     rows = std::max(rows, sets[i].n_rows);
   }
   const DecodeArgs& a = sets[0];
-  const dim3 grid((unsigned)((int64_t)a.n_splits * a.batch * a.n_kv_heads * n_sets), n_z);
+  const int64_t n_work = (int64_t)a.n_splits * a.batch * a.n_kv_heads;
+  const dim3 grid((unsigned)(n_sets == 1 ? n_work : (n_work + 7) / 8 * 16), n_z);
   const bool two = rows > 16;
   if (head_dim == 128) {
     if (two) launch_mfma_d<128, 2>(l, grid, residual, stream);

@@ -79,9 +79,8 @@ struct DecodeArgs {
 
 // One partial launch holds up to kMaxSets argument sets over the same cache
 // rows, each with its own query rows (at most 16 when there are two) and
-// residual loops. Block x works on set x % n_sets, so the blocks of all sets of
-// one (batch, kv head, split) run side by side and the reference tiles they
-// all stream are read from HBM about once.
+// residual loops. The two blocks of one (batch, kv head, split) run side by
+// side on one XCD.
 constexpr int kMaxSets = 2;
 struct DecodeLaunch {
   DecodeArgs set[kMaxSets];
