@@ -146,7 +146,7 @@ def _oracle_row(args):
     return 1
 
 
-def cpu_baseline(w, rows_per_worker=4):
+def cpu_baseline(w, rows_per_worker=8):
     try:
         avail = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
