@@ -73,12 +73,15 @@ def _hat(kref, vref, res, bits_per_loop):
     return kh, vh
 
 
-@pytest.mark.parametrize("d,P,bits_per_loop,tail", [
-    (128, 64, (2, 4, 0), 0), (128, 128, (2, 2, 0), 1), (64, 64, (8, 3, 0), 2), (128, 256, (4, 2, 2, 0), 1)])
-def test_paged_decode_matches_oracle(d, P, bits_per_loop, tail):
-    print(f"paged d={d} P={P} bits={bits_per_loop} tail={tail}", flush=True)
-    rng = np.random.default_rng(d + P + tail)
-    L, B, H, hq, max_blocks = len(bits_per_loop), 6, 2, 8, 4
+# hq = 8 (G = 4) with 8 loops and hq = 16 (G = 8) with 4 loops: 32 query rows
+# per kv head, so the launch runs two 16-row argument sets
+@pytest.mark.parametrize("d,P,bits_per_loop,tail,hq", [
+    (128, 64, (2, 4, 0), 0, 8), (128, 128, (2, 2, 0), 1, 8), (64, 64, (8, 3, 0), 2, 8), (128, 256, (4, 2, 2, 0), 1, 8),
+    (128, 64, (2, 4, 2, 2, 2, 2, 2, 0), 1, 8), (64, 128, (8, 3, 2, 0), 0, 16)])
+def test_paged_decode_matches_oracle(d, P, bits_per_loop, tail, hq):
+    print(f"paged d={d} P={P} bits={bits_per_loop} tail={tail} hq={hq}", flush=True)
+    rng = np.random.default_rng(d + P + tail + hq)
+    L, B, H, max_blocks = len(bits_per_loop), 6, 2, 4
     S = max_blocks * P
     lens = np.array([0, 1, P - 1, P, P + 1, S], dtype=np.int32)
     kref, vref, res = _dense_cache(rng, B, H, S, d, bits_per_loop)
@@ -116,16 +119,17 @@ def test_paged_decode_matches_oracle(d, P, bits_per_loop, tail):
         assert_attn_close(out, expect)
 
 
-def test_paged_equals_contiguous_varlen():
-    """The same cache, dense or scattered into shuffled blocks: identical results."""
+@pytest.mark.parametrize("bits_per_loop,hq", [((2, 2, 0), 8), ((4, 2, 2, 2, 2, 2, 2, 0), 8)])
+def test_paged_equals_contiguous_varlen(bits_per_loop, hq):
+    """The same cache, dense or scattered into shuffled blocks: identical results
+    (the 8-loop case runs two argument sets)."""
     rng = np.random.default_rng(5)
-    bits_per_loop = (2, 2, 0)
     B, H, d, P, max_blocks = 3, 2, 128, 128, 3
     S = P * max_blocks
     lens = np.array([S, 200, 77], dtype=np.int32)
     kref, vref, res = _dense_cache(rng, B, H, S, d, bits_per_loop)
     table, n_blocks = _table(rng, B, max_blocks, np.full(B, S), P, spare=1)
-    q = to_dev(_bf16(rng, (3, B, 8, d)))
+    q = to_dev(_bf16(rng, (len(bits_per_loop), B, hq, d)))
     dense_views, paged_views = [], []
     for l, bl in enumerate(bits_per_loop):
         if bl:
