@@ -181,6 +181,19 @@ def test_bf16_baseline(name):
     assert_attn_close(out, expect)
 
 
+@pytest.mark.parametrize("hq,hkv,d,n_loops", [(4, 4, 128, 2), (16, 2, 64, 3), (32, 1, 128, 2), (24, 8, 64, 1)])
+def test_bf16_baseline_head_groupings(hq, hkv, d, n_loops):
+    """G = 1, 8, 32 (two 16-row MFMA blocks) and 3, both head sizes, a ragged length."""
+    bits = tuple([2] * (n_loops - 1) + [0])
+    sig = tuple([0.1] * (n_loops - 1) + [0.0])
+    w = workloads.Workload("bf16_groups", 94, n_loops, 2, hkv, hq, d, 257, bits, sig)
+    ks, vs = workloads.kv_tensors(w, 0), workloads.kv_tensors(w, 1)
+    q_bits = workloads.q_tensor(w)
+    out = rq.decode_attn_bf16(to_dev(q_bits), [to_dev(x) for x in ks], [to_dev(x) for x in vs]).cpu().numpy()
+    expect = oracle.decode_attn(q_bits, [oracle.bf16_to_f64(x) for x in ks], [oracle.bf16_to_f64(x) for x in vs])
+    assert_attn_close(out, expect)
+
+
 def test_final_loop_rq_equals_bf16_on_reference():
     w = workloads.Workload("final", 95, 1, 2, 2, 8, 128, 333, (0,), (0.0,))
     kref, vref = workloads.ref_tensor(w, 0), workloads.ref_tensor(w, 1)
