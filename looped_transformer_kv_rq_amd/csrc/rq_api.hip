@@ -385,9 +385,10 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
     st = hip_status(launch_query_prep(qa, shape->head_dim, s));
     if (st != RQ_OK) return st;
   }
-  // A launch holds at most 32 query rows per kv head and what its waves stage
-  // per tile must fit the block's LDS; further loops go to further launches
-  // (each streams the reference again).
+  // A launch holds at most 32 query rows per kv head, and what its waves stage
+  // per tile must fit the block's LDS. Past 16 rows (G <= 16) it runs as two
+  // argument sets of at most 16 / G loops each. Further loops go to further
+  // launches (each streams the reference again).
   int base = 0;
   while (base < n_loops) {
     int nl = 0;
@@ -395,6 +396,7 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
     while (base + nl < n_loops && (nl + 1) * G <= 32) {
       bits[nl] = loops[base + nl].bits;
       if (nl > 0 && 4 * decode_wave_lds_bytes(shape->head_dim, bits, nl + 1) > kMaxBlockLds) break;
+      if ((nl + 1) * G > 16 && G <= 16 && nl + 1 > 2 * (16 / G)) break;
       ++nl;
     }
     if (nl == 0) nl = 1;  // G == 32: one loop per launch

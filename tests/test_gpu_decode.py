@@ -92,9 +92,11 @@ def test_decode_ragged_lengths(d, s):
     _run_case(w, range(3), _all_rows(w))
 
 
-@pytest.mark.parametrize("hq,hkv,n_loops", [(4, 4, 4), (16, 2, 4), (32, 1, 2), (12, 4, 8)])
+@pytest.mark.parametrize("hq,hkv,n_loops", [(4, 4, 4), (16, 2, 4), (32, 1, 2), (12, 4, 8), (12, 2, 5), (20, 2, 3)])
 def test_decode_head_groupings(hq, hkv, n_loops):
-    """G = 1, 8, 32 and 3; more than 32 rows per kv head splits the launch over loops."""
+    """G = 1, 8, 32, 3, 6 and 10; more than 32 rows per kv head splits the launch over loops.
+    G = 6 with 5 loops and G = 10 with 3 loops fit 32 rows but not two sets of at most 16
+    (2 and 1 loops per set), so those launches split over loops."""
     bits = tuple([4] + [2] * (n_loops - 2) + [0])
     sig = tuple([0.1] * (n_loops - 1) + [0.0])
     w = workloads.Workload("groups", 91, n_loops, 2, hkv, hq, 128, 300, bits, sig)
