@@ -374,17 +374,13 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
   unsigned char* prep = static_cast<unsigned char*>(workspace) + partial_bytes(shape, n_q_heads, n_loops, rec_splits);
   bool any_residual = false;
   for (int i = 0; i < n_loops; ++i) any_residual = any_residual || loops[i].bits != 0;
-  if (any_residual) {
-    QueryPrepArgs qa{};
-    qa.q = q;
-    qa.out = prep;
-    for (int i = 0; i < n_loops; ++i) qa.bits[i] = loops[i].bits;
-    qa.n_rows = (int64_t)n_loops * shape->batch * n_q_heads;
-    qa.batch = shape->batch;
-    qa.n_q_heads = n_q_heads;
-    st = hip_status(launch_query_prep(qa, shape->head_dim, s));
-    if (st != RQ_OK) return st;
-  }
+  struct Launch {
+    DecodeArgs sets[kMaxSets];
+    int n_sets;
+    bool residual;
+  };
+  Launch launches[kMaxLoops];
+  int n_launches = 0;
   // A launch holds at most 32 query rows per kv head, and what its waves stage
   // per tile must fit the block's LDS. Past 16 rows (G <= 16) it runs as two
   // argument sets of at most 16 / G loops each. Further loops go to further
@@ -467,9 +463,45 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
       }
     }
     for (int si = 0; si < n_sets; ++si) sets[si].zero_residual = any_residual && !residual;
-    st = hip_status(launch_decode_partial(sets, n_sets, shape->head_dim, 1, residual, s));
-    if (st != RQ_OK) return st;
+    Launch& ln = launches[n_launches++];
+    for (int si = 0; si < n_sets; ++si) ln.sets[si] = sets[si];
+    ln.n_sets = n_sets;
+    ln.residual = residual;
     base += nl;
+  }
+  // The residual launches rotate the queries themselves when every one of
+  // them can (one 16-row block per set, a dense cache, INT2 / INT4 loops) and
+  // the rotated operands fit their blocks' LDS without costing a block per
+  // CU; otherwise one prep kernel writes every query row's record first.
+  bool rotate = pages == nullptr;
+  for (int i = 0; i < n_launches; ++i) {
+    const Launch& ln = launches[i];
+    if (!ln.residual) continue;
+    int rows = 0;
+    for (int si = 0; si < ln.n_sets; ++si) {
+      rows = std::max(rows, ln.sets[si].n_rows);
+      if (ln.sets[si].n8 + ln.sets[si].n3 > 0) rotate = false;
+    }
+    const int with = decode_launch_lds_bytes(ln.sets, ln.n_sets, shape->head_dim, true, true);
+    const int without = decode_launch_lds_bytes(ln.sets, ln.n_sets, shape->head_dim, true, false);
+    if (rows > 16 || with > kMaxBlockLds || kMaxBlockLds / with < kMaxBlockLds / without) rotate = false;
+  }
+  if (any_residual && !rotate) {
+    QueryPrepArgs qa{};
+    qa.q = q;
+    qa.out = prep;
+    for (int i = 0; i < n_loops; ++i) qa.bits[i] = loops[i].bits;
+    qa.n_rows = (int64_t)n_loops * shape->batch * n_q_heads;
+    qa.batch = shape->batch;
+    qa.n_q_heads = n_q_heads;
+    st = hip_status(launch_query_prep(qa, shape->head_dim, s));
+    if (st != RQ_OK) return st;
+  }
+  for (int i = 0; i < n_launches; ++i) {
+    Launch& ln = launches[i];
+    for (int si = 0; si < ln.n_sets; ++si) ln.sets[si].qprep = rotate ? nullptr : prep;
+    st = hip_status(launch_decode_partial(ln.sets, ln.n_sets, shape->head_dim, 1, ln.residual, s));
+    if (st != RQ_OK) return st;
   }
   if (tail_len > 0) {
     // the tail: plain bf16 positions of every loop, one more split per row

@@ -182,6 +182,18 @@ __host__ __device__ constexpr int rs_coord(int ks, int g, int e) {
   return 32 * ks + 16 * (g >> 1) + 4 * (g & 1) + (e >> 1) + 8 * (e & 1);
 }
 
+// fp16 of x / sqrt(D), rounded twice as written (the fp32 product, then fp16).
+// The code generator fuses a product and its fp16 conversion into one
+// mixed-precision fma (a single rounding) at some sites and not at others, so
+// two kernels computing the same operand could disagree by one fp16 ulp. The
+// empty asm statement hands the conversion a finished fp32 value.
+template <int D>
+__device__ __forceinline__ _Float16 scaled_f16(float x) {
+  float y = x * RsqrtD<D>::v;
+  asm volatile("" : "+v"(y));
+  return (_Float16)y;
+}
+
 // Four lanes per query row (loop, b, hq), sixteen rows per wave. Lane g of a
 // row loads the query in residual-score operand order: coordinates
 // rs_coord(ks, g, 2i + p) = base + i + 8p (base = 32 ks + 16 (g >> 1) + 4 (g & 1))
@@ -269,7 +281,7 @@ __global__ __launch_bounds__(64) void rq_query_prep(QueryPrepArgs a) {
     float sum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const _Float16 h0 = (_Float16)(x[ks][0][i] * RsqrtD<D>::v), h1 = (_Float16)(x[ks][1][i] * RsqrtD<D>::v);
+      const _Float16 h0 = scaled_f16<D>(x[ks][0][i]), h1 = scaled_f16<D>(x[ks][1][i]);
       w[i] = __builtin_bit_cast(uint32_t, f16x2_t{h0, h1});
       sum += (float)h0 + (float)h1;
     }
@@ -675,6 +687,41 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* b
   }
 }
 
+// Paged cache: whether the table entry of the tile at token t is a valid block
+// (a tile without one takes no weight).
+template <bool PAGED>
+__device__ __forceinline__ bool tile_valid(const DecodeArgs& a, int b, int t) {
+  if constexpr (PAGED) {
+    const int blk = a.block_table[(int64_t)b * a.max_blocks + (t >> a.log2_block)];
+    return blk >= 0 && blk < a.n_blocks;
+  } else {
+    return true;
+  }
+}
+
+// Issue the tile at token t of sequence b, kv head kvh (blockIdx.y = z), dense
+// or paged. Unclamped loads only when every token of the tile is one of this
+// call's positions: positions past a sequence's length may hold any bits.
+template <int D, bool RESID, bool WIDE, bool PAGED>
+__device__ __forceinline__ void issue_at(const DecodeArgs& a, unsigned char* buf, const uint16_t* kbase,
+                                         const uint16_t* vbase, int64_t row_base, int b, int kvh, int z, int t,
+                                         int t_end, int lane, int m, int g, uint4 (&ka)[2][D / 32]) {
+  const bool full = t + kTile <= t_end;
+  const int tlast = t_end - 1;
+  if constexpr (PAGED) {
+    const int blk = a.block_table[(int64_t)b * a.max_blocks + (t >> a.log2_block)];
+    // vector index of token t; the tile's tokens follow it
+    const int64_t tv = (((int64_t)blk * a.n_kv_heads + kvh) << a.log2_block) + (t & ((1 << a.log2_block) - 1));
+    const uint16_t* kt = a.k[z] + tv * D;
+    const uint16_t* vt = a.v[z] + tv * D;
+    if (full) issue_tile<D, RESID, WIDE, true>(a, buf, kt, vt, tv, 0, tlast - t, lane, m, g, ka);
+    else issue_tile<D, RESID, WIDE, false>(a, buf, kt, vt, tv, 0, tlast - t, lane, m, g, ka);
+  } else {
+    if (full) issue_tile<D, RESID, WIDE, true>(a, buf, kbase, vbase, row_base, t, tlast, lane, m, g, ka);
+    else issue_tile<D, RESID, WIDE, false>(a, buf, kbase, vbase, row_base, t, tlast, lane, m, g, ka);
+  }
+}
+
 // Scores, online softmax and PV of one staged tile.
 template <int D, int NB, bool RESID, bool WIDE>
 __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned char* buf, int t0, int t_end,
@@ -817,6 +864,12 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
 
 // WIDE instantiations also take INT8 and INT3 loops; the others carry no code
 // for them.
+// Instantiations that can rotate the queries themselves (DecodeArgs::qprep
+// NULL): one 16-row block of a residual launch over a dense cache with INT2 /
+// INT4 loops.
+template <int NB, bool RESID, bool WIDE, bool PAGED>
+constexpr bool kRotatesQueries = NB == 1 && RESID && !WIDE && !PAGED;
+
 // SETS: the launch's argument sets (1 or 2). With two, the block of set s for
 // work item w is 16 (w / 8) + 8 s + w % 8, so the two blocks of a work item go
 // to the same XCD under the round-robin dispatch and are dispatched close
@@ -870,7 +923,7 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
       qoff[nb][ks] = 0.0f;
     }
     if constexpr (RESID) {
-      if (qrow >= 0 && lb != 0) {
+      if (qrow >= 0 && lb != 0 && a.qprep != nullptr) {
         const unsigned char* rec = a.qprep + qrow * Gm::PREP_BYTES;
 #pragma unroll
         for (int ks = 0; ks < NG; ++ks) {
@@ -911,23 +964,99 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
 
   const Consts kc = make_consts<WIDE>();
   uint4 ka[2][NG];
-  for (int t0 = t_begin + wave * kTile; t0 < t_end; t0 += kStep) {
-    // Unclamped loads only when every token of the tile is one of this call's
-    // positions: positions past a sequence's length may hold any bits.
-    const bool full = t0 + kTile <= t_end;
-    if constexpr (PAGED) {
-      const int blk = a.block_table[(int64_t)b * a.max_blocks + (t0 >> a.log2_block)];
-      if (blk < 0 || blk >= a.n_blocks) continue;  // no valid page: the tile takes no weight
-      // vector index of token t0; the tile's tokens follow it
-      const int64_t tv = (((int64_t)blk * a.n_kv_heads + kvh) << a.log2_block) + (t0 & ((1 << a.log2_block) - 1));
-      const uint16_t* kt = a.k[z] + tv * D;
-      const uint16_t* vt = a.v[z] + tv * D;
-      if (full) issue_tile<D, RESID, WIDE, true>(a, buf, kt, vt, tv, 0, tlast - t0, lane, m, g, ka);
-      else issue_tile<D, RESID, WIDE, false>(a, buf, kt, vt, tv, 0, tlast - t0, lane, m, g, ka);
-    } else {
-      if (full) issue_tile<D, RESID, WIDE, true>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
-      else issue_tile<D, RESID, WIDE, false>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, ka);
+  int t0 = t_begin + wave * kTile;
+  // (only where the extra copy of the tile body adds no register spills)
+  if constexpr (kRotatesQueries<NB, RESID, WIDE, PAGED>) {
+    if (a.qprep == nullptr) {
+      // The residual-score operand is computed here rather than read from
+      // prepared records: the block's 16 rows go 16 / NG to a wave, 4 NG lanes
+      // per row with one 8-coordinate operand chunk (ks, g) each, and the
+      // block shares them through LDS after the tiles. The query loads go out
+      // with the wave's first tile.
+      constexpr int kLanesRow = 4 * NG, kRowsWave = 64 / kLanesRow;
+      constexpr int QS = 2 * D + 16;  // LDS bytes per row: operand chunks, then 4 NG offsets
+      unsigned char* qreg = smem + 4 * a.lds_wave_bytes;
+      const int rr = kRowsWave * wave + lane / kLanesRow;  // block row this lane rotates
+      const int c = lane % kLanesRow, cks = c >> 2, cg = c & 3;
+      const int lbr = rr < R ? a.bits[rr / G] : 0;
+      int64_t qr = -1;
+      if (rr < R && lbr != 0) qr = ((int64_t)(a.loop_id[rr / G] + z) * a.batch + b) * a.n_q_heads + kvh * G + rr % G;
+      const uint16_t* qs = a.q + (qr >= 0 ? qr : 0) * D + 32 * cks + 16 * (cg >> 1) + 4 * (cg & 1);
+      const uint2 q0 = qr >= 0 ? *reinterpret_cast<const uint2*>(qs) : make_uint2(0, 0);
+      const uint2 q1 = qr >= 0 ? *reinterpret_cast<const uint2*>(qs + 8) : make_uint2(0, 0);
+      if (t0 < t_end) issue_at<D, RESID, WIDE, PAGED>(a, buf, kbase, vbase, row_base, b, kvh, z, t0, t_end, lane, m, g, ka);
+      wait_vmem();
+      // x[p][i]: coordinate base + i + 8p. Butterflies on coordinate bits 0, 1
+      // and 3 in the lane, then across the row's lanes: the k-step bits (lane
+      // bits 2 and up), coordinate bit 2 (lane bit 0) and bit 4 (lane bit 1).
+      // The lower lane keeps own + partner, the upper one partner - own. This
+      // is the prep kernel's stage order, so both give identical values.
+      float x[2][4] = {{bf16_lo(q0.x), bf16_hi(q0.x), bf16_lo(q0.y), bf16_hi(q0.y)},
+                       {bf16_lo(q1.x), bf16_hi(q1.x), bf16_lo(q1.y), bf16_hi(q1.y)}};
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int st = 1; st < 4; st <<= 1)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!(i & st)) {
+              const float u = x[pp][i], w = x[pp][i | st];
+              x[pp][i] = u + w;
+              x[pp][i | st] = u - w;
+            }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float u = x[0][i], w = x[1][i];
+        x[0][i] = u + w;
+        x[1][i] = u - w;
+      }
+#pragma unroll
+      for (int k = 2; k < 2 + NG / 2 + 2; ++k) {  // lane bits 2 (, 3), then 0 and 1
+        const int st = 1 << (k < 2 + NG / 2 ? k : k - 2 - NG / 2);
+        const float sg = (c & st) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[pp][i] = fmaf(sg, x[pp][i], __shfl_xor(x[pp][i], st));
+      }
+      uint32_t w4[4];
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const _Float16 h0 = scaled_f16<D>(x[0][i]), h1 = scaled_f16<D>(x[1][i]);
+        w4[i] = __builtin_bit_cast(uint32_t, f16x2_t{h0, h1});
+        sum += (float)h0 + (float)h1;
+      }
+      sum += quad_xor<1>(sum);  // the group's four chunks (same k-step)
+      sum += quad_xor<2>(sum);
+      if (rr < 16) {
+        *reinterpret_cast<uint4*>(qreg + rr * QS + 16 * c) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        if (cg == 0) {
+          const float off = lbr > 0 ? (float)(1 << lbr) + (float)(1 << (lbr - 1)) - 0.5f : 0.0f;
+          *reinterpret_cast<float*>(qreg + rr * QS + 2 * D + 4 * cks) = -off * sum;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) {
+        qtB[0][ks] = *reinterpret_cast<const uint4*>(qreg + m * QS + 16 * (4 * ks + g));
+        qoff[0][ks] = *reinterpret_cast<const float*>(qreg + m * QS + 2 * D + 4 * ks);
+      }
+      wave_sync_lds();
+      // the first tile, already staged (its own copy of the tile body, so the
+      // K registers are not live across the loop below)
+      if (t0 < t_end) {
+        compute_tile<D, NB, RESID, WIDE>(a, buf, t0, t_end, m, g, ka, qB, qtB, qoff, qmul, my_loop, o_ref, o_res, m_run,
+                                         l_run, kc);
+        wait_lds();
+        wave_sync_lds();
+        t0 += kStep;
+      }
     }
+  }
+  for (; t0 < t_end; t0 += kStep) {
+    if (!tile_valid<PAGED>(a, b, t0)) continue;  // no valid page: the tile takes no weight
+    issue_at<D, RESID, WIDE, PAGED>(a, buf, kbase, vbase, row_base, b, kvh, z, t0, t_end, lane, m, g, ka);
     wait_vmem();
     wave_sync_lds();
     compute_tile<D, NB, RESID, WIDE>(a, buf, t0, t_end, m, g, ka, qB, qtB, qoff, qmul, my_loop, o_ref, o_res, m_run, l_run,
@@ -1034,11 +1163,23 @@ int query_prep_bytes(int head_dim) {
 }
 
 // LDS bytes of one block: the larger of the merge slots and 4 wave tiles
-static int block_lds_bytes(int d, int nb, int wave_bytes, bool residual) {
+// (rotate: plus the 16 rows' rotated-query operands after the wave tiles)
+static int block_lds_bytes(int d, int nb, int wave_bytes, bool residual, bool rotate) {
   const int nr = 16 * nb;
   const int merge = 4 * nr * (residual ? 2 * d + 2 : d + 2) * 4;  // every wave's records of every row
-  const int tiles = 4 * wave_bytes;
+  const int tiles = 4 * wave_bytes + (rotate ? 16 * (2 * d + 16) : 0);
   return merge > tiles ? merge : tiles;
+}
+
+int decode_launch_lds_bytes(const DecodeArgs* sets, int n_sets, int head_dim, bool residual, bool rotate) {
+  int rows = 0, lds = 0;
+  for (int i = 0; i < n_sets; ++i) rows = std::max(rows, sets[i].n_rows);
+  const int nb = rows > 16 ? 2 : 1;
+  for (int i = 0; i < n_sets; ++i) {
+    const int wave = decode_wave_lds_bytes(head_dim, sets[i].bits, residual ? sets[i].n_loops_launch : 0);
+    lds = std::max(lds, block_lds_bytes(head_dim, nb, wave, residual, rotate && residual && nb == 1));
+  }
+  return lds;
 }
 
 template <int D, int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
@@ -1053,30 +1194,35 @@ static void launch_mfma_kernel(const DecodeLaunch& l, dim3 grid, int lds, hipStr
 }
 
 template <int D, int NB, bool PAGED, int SETS>
-static void launch_mfma_dp(const DecodeLaunch& l, dim3 grid, int lds, bool residual, bool wide, hipStream_t stream) {
+static hipError_t launch_mfma_dp(const DecodeLaunch& l, dim3 grid, int lds, bool residual, bool wide,
+                                 hipStream_t stream) {
+  // a residual launch without prepared records must be one that rotates the queries itself
+  if (residual && l.set[0].qprep == nullptr &&
+      (wide ? !kRotatesQueries<NB, true, true, PAGED> : !kRotatesQueries<NB, true, false, PAGED>))
+    return hipErrorInvalidValue;
   if (!residual) launch_mfma_kernel<D, NB, false, false, PAGED, SETS>(l, grid, lds, stream);
   else if (wide) launch_mfma_kernel<D, NB, true, true, PAGED, SETS>(l, grid, lds, stream);
   else launch_mfma_kernel<D, NB, true, false, PAGED, SETS>(l, grid, lds, stream);
+  return hipSuccess;
 }
 
 template <int D, int NB>
-static void launch_mfma_d(DecodeLaunch& l, dim3 grid, bool residual, hipStream_t stream) {
+static hipError_t launch_mfma_d(DecodeLaunch& l, dim3 grid, bool residual, hipStream_t stream) {
   int lds = 0;
   bool wide = false;
   for (int i = 0; i < l.n_sets; ++i) {
     DecodeArgs& a = l.set[i];
     a.lds_wave_bytes = decode_wave_lds_bytes(D, a.bits, residual ? a.n_loops_launch : 0);
-    lds = std::max(lds, block_lds_bytes(D, NB, a.lds_wave_bytes, residual));
+    lds = std::max(lds, block_lds_bytes(D, NB, a.lds_wave_bytes, residual, residual && NB == 1 && a.qprep == nullptr));
     wide = wide || a.n8 + a.n3 > 0;
   }
   const bool paged = l.set[0].block_table != nullptr;
   if (l.n_sets == 2) {  // two sets of at most 16 rows
-    if (paged) launch_mfma_dp<D, 1, true, 2>(l, grid, lds, residual, wide, stream);
-    else launch_mfma_dp<D, 1, false, 2>(l, grid, lds, residual, wide, stream);
-  } else {
-    if (paged) launch_mfma_dp<D, NB, true, 1>(l, grid, lds, residual, wide, stream);
-    else launch_mfma_dp<D, NB, false, 1>(l, grid, lds, residual, wide, stream);
+    if (paged) return launch_mfma_dp<D, 1, true, 2>(l, grid, lds, residual, wide, stream);
+    return launch_mfma_dp<D, 1, false, 2>(l, grid, lds, residual, wide, stream);
   }
+  if (paged) return launch_mfma_dp<D, NB, true, 1>(l, grid, lds, residual, wide, stream);
+  return launch_mfma_dp<D, NB, false, 1>(l, grid, lds, residual, wide, stream);
 }
 
 hipError_t launch_decode_partial(const DecodeArgs* sets, int n_sets, int head_dim, int n_z, bool residual,
@@ -1093,13 +1239,10 @@ hipError_t launch_decode_partial(const DecodeArgs* sets, int n_sets, int head_di
   const int64_t n_work = (int64_t)a.n_splits * a.batch * a.n_kv_heads;
   const dim3 grid((unsigned)(n_sets == 1 ? n_work : (n_work + 7) / 8 * 16), n_z);
   const bool two = rows > 16;
-  if (head_dim == 128) {
-    if (two) launch_mfma_d<128, 2>(l, grid, residual, stream);
-    else launch_mfma_d<128, 1>(l, grid, residual, stream);
-  } else {
-    if (two) launch_mfma_d<64, 2>(l, grid, residual, stream);
-    else launch_mfma_d<64, 1>(l, grid, residual, stream);
-  }
+  hipError_t e;
+  if (head_dim == 128) e = two ? launch_mfma_d<128, 2>(l, grid, residual, stream) : launch_mfma_d<128, 1>(l, grid, residual, stream);
+  else e = two ? launch_mfma_d<64, 2>(l, grid, residual, stream) : launch_mfma_d<64, 1>(l, grid, residual, stream);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

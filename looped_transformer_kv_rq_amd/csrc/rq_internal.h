@@ -58,7 +58,8 @@ struct DecodeArgs {
   const uint32_t* vc[kMaxLoops];
   const uint16_t* vs[kMaxLoops];
   float* ws;                            // partials [n_loops_total][B][Hq][n_splits][2D + 2]
-  const unsigned char* qprep;           // rotated-query records [n_loops_total][B][Hq] (residual launches)
+  const unsigned char* qprep;           // rotated-query records [n_loops_total][B][Hq], or NULL: a
+                                        // residual launch at NB = 1 rotates the queries itself
   int32_t loop_id[kMaxLoops];           // per slot: the call's loop index of its rows (+ blockIdx.y)
   int32_t n8, n4, n3, n2;               // slot counts per width, in slot order; the rest bits 0
   int32_t n_loops_launch;               // slots (loops) whose rows this launch holds
@@ -129,5 +130,9 @@ constexpr int kMaxBlockLds = 160 * 1024;
 int decode_wave_lds_bytes(int head_dim, const int32_t* bits, int n_loops);
 // LDS bytes one residual loop of the given width adds to that (0 for bits 0)
 int decode_loop_lds_bytes(int head_dim, int bits);
+
+// LDS bytes one block of a partial launch takes (the largest over its sets);
+// rotate: its residual blocks rotate the queries themselves (no prepared records)
+int decode_launch_lds_bytes(const DecodeArgs* sets, int n_sets, int head_dim, bool residual, bool rotate);
 
 }  // namespace rq
