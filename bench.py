@@ -3,8 +3,9 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
 One step is one pass of the hot path over one batch of synthetic input:
-rq_encode of K and of V (every non-final loop against the bf16 final-loop
-reference), then rq_decode_attn for every loop over the just-encoded cache.
+rq_encode_kv, the encode of K and of V in one launch (every non-final loop
+against the bf16 final-loop reference), then rq_decode_attn for every loop
+over the just-encoded cache.
 K steps are timed between two device synchronisations. `value` is KV tokens
 through the hot path per second: batch * seq_len * n_loops / step time.
 
@@ -30,7 +31,7 @@ measured kernel):
   of both (one decode call = the next token of every sequence).
 
 `roofline` covers the kernel that takes the largest share of the step (the
-encoder). Its achieved rate is algorithmic bytes per launch divided by the
+encoder, one launch for K and V). Its achieved rate is algorithmic bytes per launch divided by the
 launch's average duration, timed with HIP events on the stream the kernel
 runs on over a run of back-to-back launches (no event marker between two
 launches). `traffic` comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary
@@ -365,14 +366,15 @@ def main():
     def enc_k():
         rq.encode_into([kx[l] for l in res_loops], kref, bits, kc, ks, stream=stream)
 
-    def enc_v():
-        rq.encode_into([vx[l] for l in res_loops], vref, bits, vc, vs, stream=stream)
+    def enc_kv():  # K and V in one launch (the step's encode)
+        rq.encode_kv_into([kx[l] for l in res_loops], [vx[l] for l in res_loops], kref, vref, bits, kc, ks, vc, vs,
+                          stream=stream)
 
     def dec():
         rq.decode_attn(q, kref, vref, views, out=out, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
-        enc_k(); enc_v(); dec()
+        enc_kv(); dec()
     torch.cuda.synchronize()
 
     # The timed steps: one pair of events around all of them and nothing
@@ -383,7 +385,7 @@ def main():
     t_wall = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        enc_k(); enc_v(); dec()
+        enc_kv(); dec()
     stop.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
@@ -391,34 +393,33 @@ def main():
 
     # Per-kernel split of a step, from a separate pass with an event between
     # every two launches (each marker adds a drain, so this pass runs slower).
-    marks = [[Ev(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    marks = [[Ev(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for k in range(args.steps):
         m = marks[k]
-        m[0].record(stream); enc_k()
-        m[1].record(stream); enc_v()
-        m[2].record(stream); dec()
-        m[3].record(stream)
+        m[0].record(stream); enc_kv()
+        m[1].record(stream); dec()
+        m[2].record(stream)
     torch.cuda.synchronize()
-    enc_in_step_ms = statistics.mean([m[0].elapsed_time(m[1]) for m in marks] +
-                                     [m[1].elapsed_time(m[2]) for m in marks])
-    dec_in_step_ms = statistics.mean([m[2].elapsed_time(m[3]) for m in marks])
-    marked_step_ms = statistics.mean([m[0].elapsed_time(m[3]) for m in marks])
+    enc_in_step_ms = statistics.mean([m[0].elapsed_time(m[1]) for m in marks])
+    dec_in_step_ms = statistics.mean([m[1].elapsed_time(m[2]) for m in marks])
+    marked_step_ms = statistics.mean([m[0].elapsed_time(m[2]) for m in marks])
 
-    # The encoder's roofline figure: back-to-back launches (K, V, K, V, ...)
-    # bracketed by one pair of events, so no event marker sits between two
-    # launches (a marker between kernels adds its own drain to the interval).
+    # The encoder's roofline figure: back-to-back K+V launches bracketed by
+    # one pair of events, so no event marker sits between two launches (a
+    # marker between kernels adds its own drain to the interval).
     enc_reps = max(10, args.steps // 2)
     e0, e1 = Ev(enable_timing=True), Ev(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(enc_reps):
-        enc_k(); enc_v()
+        enc_kv()
     e1.record(stream)
     torch.cuda.synchronize()
-    enc_ms = e0.elapsed_time(e1) / (2 * enc_reps)
+    enc_ms = e0.elapsed_time(e1) / enc_reps
 
     kv_tokens = w.batch * w.seq_len * w.n_loops
-    enc_b = encode_bytes(w, bits)
+    enc_b = encode_bytes(w, bits)  # one tensor
+    enc_kv_b = 2 * enc_b
     dec_b = decode_bytes(w, list(w.bits))
     result = {
         "metric": METRIC,
@@ -436,16 +437,16 @@ def main():
         "config": {
             "workload": w.name, "n_loops": w.n_loops, "batch": w.batch, "n_kv_heads": w.n_kv_heads,
             "n_q_heads": w.n_q_heads, "head_dim": w.head_dim, "seq_len": w.seq_len, "bits": list(w.bits),
-            "step": "rq_encode(K) + rq_encode(V) + rq_decode_attn(all loops)",
+            "step": "rq_encode_kv (K and V, one launch) + rq_decode_attn (all loops)",
             "storage": "bf16 reference, int2/int4 residual codes, fp16 scales per 32",
         },
     }
-    enc_gbps = enc_b / (enc_ms * 1e-3) / 1e9
+    enc_gbps = enc_kv_b / (enc_ms * 1e-3) / 1e9
     result["roofline"] = {
-        "kernel": f"rq_encode_kernel<{w.head_dim}> ({len(bits)} loops per launch)",
+        "kernel": f"rq_encode_kernel<{w.head_dim}> (K and V, {len(bits)} loops each, one launch)",
         "bound": "hbm", "achieved": enc_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": enc_gbps / HBM_PEAK_GBPS, "traffic": _traffic("encode", w.name),
-        "algorithmic_bytes_per_launch": enc_b, "launch_ms": enc_ms, "launches_timed": 2 * enc_reps,
+        "algorithmic_bytes_per_launch": enc_kv_b, "launch_ms": enc_ms, "launches_timed": enc_reps,
     }
     result["wall_s_timed"] = wall_s
 
@@ -501,8 +502,8 @@ def main():
             "frac_peak": dec_gbps / HBM_PEAK_GBPS, "ms_in_step": dec_in_step_ms,
         }
         result["encode"] = {"GBps": enc_gbps, "ms_per_launch": enc_ms, "ms_per_launch_in_step": enc_in_step_ms,
-                            "launches_per_step": 2}
-        result["step_split"] = {"encode_ms": 2 * enc_in_step_ms, "decode_ms": dec_in_step_ms,
+                            "launches_per_step": 1, "tensors_per_launch": 2}
+        result["step_split"] = {"encode_ms": enc_in_step_ms, "decode_ms": dec_in_step_ms,
                                 "step_ms_with_markers": marked_step_ms,
                                 "what": "a separate pass with an event between launches"}
         result["bf16_baseline"] = {
@@ -639,8 +640,8 @@ def main():
         def serve():
             rq.decode_attn_varlen(q, kref, vref, views, seq_lens=lens_d, tail_k=tk, tail_v=tv, out=out,
                                   workspace=ws_v, stream=stream)
-            rq.encode_append([tk[l] for l in res_loops], tk[-1], bits, lens_d, kref, kc, ks, stream=stream)
-            rq.encode_append([tv[l] for l in res_loops], tv[-1], bits, lens_d, vref, vc, vs, stream=stream)
+            rq.encode_append_kv([tk[l] for l in res_loops], [tv[l] for l in res_loops], tk[-1], tv[-1], bits, lens_d,
+                                kref, vref, kc, ks, vc, vs, stream=stream)
 
         sv_ms = timed(serve, args.reps)
         per_tok = decode_bytes(w, list(w.bits)) / (w.batch * w.seq_len)  # cache bytes per (b, position)
@@ -649,7 +650,7 @@ def main():
             "ms": sv_ms, "prefix_tokens": int(lens.sum()), "tail_positions_per_loop": 1,
             "decode_GBps": sv_bytes / (sv_ms * 1e-3) / 1e9,
             "kv_tokens_per_s": float(lens.sum() + w.batch) * w.n_loops / (sv_ms * 1e-3),
-            "what": "rq_decode_attn_varlen (ragged prefixes + 1 tail position) + rq_encode_append of K and V",
+            "what": "rq_decode_attn_varlen (ragged prefixes + 1 tail position) + rq_encode_append_kv (K and V)",
         }
 
         # The same serving step over a block-paged copy of the cache: blocks of
@@ -676,10 +677,8 @@ def main():
         def serve_paged():
             rq.decode_attn_paged(q, kref_p, vref_p, views_p, table, seq_lens=lens_d, tail_k=tk, tail_v=tv, out=out,
                                  workspace=ws_v, stream=stream)
-            rq.encode_append_paged([tk[l] for l in res_loops], tk[-1], bits, lens_d, table, kref_p, kc_p, ks_p,
-                                   stream=stream)
-            rq.encode_append_paged([tv[l] for l in res_loops], tv[-1], bits, lens_d, table, vref_p, vc_p, vs_p,
-                                   stream=stream)
+            rq.encode_append_paged_kv([tk[l] for l in res_loops], [tv[l] for l in res_loops], tk[-1], tv[-1], bits,
+                                      lens_d, table, kref_p, vref_p, kc_p, ks_p, vc_p, vs_p, stream=stream)
 
         svp_ms = timed(serve_paged, args.reps)
         result["serving_step_paged"] = {

@@ -13,6 +13,8 @@
  * this custom format. This library provides exactly those operations:
  *
  *   rq_encode          rotate + quantize + pack the residuals of one tensor
+ *   rq_encode_kv, rq_encode_append_kv, rq_encode_append_paged_kv  the same
+ *                        for K and V together, in one launch
  *   rq_reconstruct     materialise one loop's K or V from ref + residual
  *   rq_decode_attn     fused reconstruct + single-query decode attention
  *   rq_decode_attn_bf16  the same decode attention over plain bf16 K/V per
@@ -139,6 +141,17 @@ typedef struct rq_loop_view {
 int rq_encode(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
               const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, void* stream);
 
+/* rq_encode of K and V together, in one launch: the same as rq_encode(kx,
+ * k_ref, k_codes, k_scales) followed by rq_encode(vx, v_ref, v_codes,
+ * v_scales) with the same bits, and bit-identical to it. A layer's K and V
+ * share the loop table; one launch saves the second launch's ramp and the
+ * first one's tail. Arguments as in rq_encode, once per tensor; the checks are
+ * those of two rq_encode calls and nothing is enqueued if either fails.
+ */
+int rq_encode_kv(const rq_shape* shape, int32_t n_loops, const uint16_t* const* kx, const uint16_t* const* vx,
+                 const int32_t* bits, const uint16_t* k_ref, const uint16_t* v_ref, uint32_t* const* k_codes,
+                 uint16_t* const* k_scales, uint32_t* const* v_codes, uint16_t* const* v_scales, void* stream);
+
 /* rq_encode with `refits` extra alternations of the two least-squares
  * half-steps after the first fit (ResidualQuant, newx.sg page, AI Summary:
  * the scale is a least-squares fit; the alternation applies that fit in turn
@@ -186,6 +199,28 @@ int rq_encode_append_paged(const rq_shape* cache, const rq_pages* pages, int32_t
                            const uint16_t* const* x, const int32_t* bits, const uint16_t* ref_new,
                            const int32_t* pos, uint16_t* ref_pages, uint32_t* const* codes,
                            uint16_t* const* scales, void* stream);
+
+/* rq_encode_append of K and V together, in one launch (bit-identical to the
+ * two calls with the same pos and bits). A serving step appends both tensors
+ * of every layer; these launches are small enough that the second launch's
+ * latency is most of its cost. Arguments as in rq_encode_append, once per
+ * tensor.
+ */
+int rq_encode_append_kv(const rq_shape* cache, int32_t n_loops, int32_t t_new, const uint16_t* const* kx,
+                        const uint16_t* const* vx, const int32_t* bits, const uint16_t* k_ref_new,
+                        const uint16_t* v_ref_new, const int32_t* pos, uint16_t* k_ref_cache, uint16_t* v_ref_cache,
+                        uint32_t* const* k_codes, uint16_t* const* k_scales, uint32_t* const* v_codes,
+                        uint16_t* const* v_scales, void* stream);
+
+/* rq_encode_append_paged of K and V together, in one launch (bit-identical to
+ * the two calls). Arguments as in rq_encode_append_paged, once per tensor.
+ */
+int rq_encode_append_paged_kv(const rq_shape* cache, const rq_pages* pages, int32_t n_loops, int32_t t_new,
+                              const uint16_t* const* kx, const uint16_t* const* vx, const int32_t* bits,
+                              const uint16_t* k_ref_new, const uint16_t* v_ref_new, const int32_t* pos,
+                              uint16_t* k_ref_pages, uint16_t* v_ref_pages, uint32_t* const* k_codes,
+                              uint16_t* const* k_scales, uint32_t* const* v_codes, uint16_t* const* v_scales,
+                              void* stream);
 
 /* Materialise one loop: out = ref + H (s * q) (ResidualQuant, newx.sg page,
  * Abstract: the residual format keeps reconstruction cheap).

@@ -103,6 +103,12 @@ def _load():
         "rq_decode_attn": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, P, P, ctypes.POINTER(_LoopView),
                                           F, I32, P, P, SZ, P]),
         "rq_decode_attn_bf16": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, PP, PP, F, I32, P, P, SZ, P]),
+        "rq_encode_kv": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, PP, ctypes.POINTER(I32), P, P, PP, PP, PP,
+                                        PP, P]),
+        "rq_encode_append_kv": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, PP, PP, ctypes.POINTER(I32), P, P,
+                                               P, P, P, PP, PP, PP, PP, P]),
+        "rq_encode_append_paged_kv": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.POINTER(_Pages), I32, I32, PP,
+                                                     PP, ctypes.POINTER(I32), P, P, P, P, P, PP, PP, PP, PP, P]),
         "rq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "rq_format_version": (I32, []),
     }
@@ -190,6 +196,36 @@ def encode_into(xs: Sequence[torch.Tensor], ref: torch.Tensor, bits: Sequence[in
         st = lib.rq_encode(ctypes.byref(shp), n, _ptr_array(xs), bits_arr, _ptr(ref), _ptr_array(codes),
                            _ptr_array(scales), _stream(ref.device, stream))
         _check(st, "rq_encode")
+
+
+def _check_loop_outputs(xs, ref, bits, codes, scales, rows, what):
+    """Shapes of one tensor's loop states and outputs: rows = the leading [B, Hkv, S] of codes / scales."""
+    b, h, s, d = ref.shape
+    n = len(xs)
+    if not (len(bits) == len(codes) == len(scales) == n):
+        raise ValueError(f"{what}: xs, bits, codes and scales must have one entry per loop")
+    for i in range(n):
+        _need(xs[i], f"{what} xs[{i}]", torch.bfloat16, ref.shape, ref.device)
+        _need(codes[i], f"{what} codes[{i}]", torch.int32, rows + (d * int(bits[i]) // 32,), ref.device)
+        _need(scales[i], f"{what} scales[{i}]", torch.float16, rows + (d // GROUP,), ref.device)
+
+
+def encode_kv_into(kx: Sequence[torch.Tensor], vx: Sequence[torch.Tensor], k_ref: torch.Tensor, v_ref: torch.Tensor,
+                   bits: Sequence[int], k_codes: Sequence[torch.Tensor], k_scales: Sequence[torch.Tensor],
+                   v_codes: Sequence[torch.Tensor], v_scales: Sequence[torch.Tensor], stream=None) -> None:
+    """rq_encode_kv: encode_into for K and V in one launch (bit-identical to two encode_into calls)."""
+    lib = _load()
+    _need(k_ref, "k_ref", torch.bfloat16, k_ref.shape)
+    _need(v_ref, "v_ref", torch.bfloat16, k_ref.shape, k_ref.device)
+    rows = tuple(k_ref.shape[:3])
+    _check_loop_outputs(kx, k_ref, bits, k_codes, k_scales, rows, "K")
+    _check_loop_outputs(vx, v_ref, bits, v_codes, v_scales, rows, "V")
+    n = len(kx)
+    bits_arr = (ctypes.c_int32 * n)(*[int(x) for x in bits])
+    st = lib.rq_encode_kv(ctypes.byref(_shape_of(k_ref)), n, _ptr_array(kx), _ptr_array(vx), bits_arr, _ptr(k_ref),
+                          _ptr(v_ref), _ptr_array(k_codes), _ptr_array(k_scales), _ptr_array(v_codes),
+                          _ptr_array(v_scales), _stream(k_ref.device, stream))
+    _check(st, "rq_encode_kv")
 
 
 def encode(xs: Sequence[torch.Tensor], ref: torch.Tensor, bits: Sequence[int], stream=None, refits: int = 0):
@@ -478,6 +514,58 @@ def encode_append(xs: Sequence[torch.Tensor], ref_new: torch.Tensor, bits: Seque
     st = lib.rq_encode_append(ctypes.byref(shp), n, t, _ptr_array(xs), bits_arr, _ptr(ref_new), _ptr(pos),
                               _ptr(ref_cache), _ptr_array(codes), _ptr_array(scales), _stream(ref_new.device, stream))
     _check(st, "rq_encode_append")
+
+
+def encode_append_kv(kx: Sequence[torch.Tensor], vx: Sequence[torch.Tensor], k_ref_new: torch.Tensor,
+                     v_ref_new: torch.Tensor, bits: Sequence[int], pos: torch.Tensor, k_ref_cache: torch.Tensor,
+                     v_ref_cache: torch.Tensor, k_codes: Sequence[torch.Tensor], k_scales: Sequence[torch.Tensor],
+                     v_codes: Sequence[torch.Tensor], v_scales: Sequence[torch.Tensor], stream=None) -> None:
+    """rq_encode_append_kv: encode_append for K and V in one launch (bit-identical to two calls)."""
+    lib = _load()
+    b, h, t, d = k_ref_new.shape
+    _need(k_ref_new, "k_ref_new", torch.bfloat16, k_ref_new.shape)
+    _need(v_ref_new, "v_ref_new", torch.bfloat16, k_ref_new.shape, k_ref_new.device)
+    s_cap = k_ref_cache.shape[2]
+    _need(k_ref_cache, "k_ref_cache", torch.bfloat16, (b, h, s_cap, d), k_ref_new.device)
+    _need(v_ref_cache, "v_ref_cache", torch.bfloat16, (b, h, s_cap, d), k_ref_new.device)
+    _need(pos, "pos", torch.int32, (b,), k_ref_new.device)
+    _check_loop_outputs(kx, k_ref_new, bits, k_codes, k_scales, (b, h, s_cap), "K")
+    _check_loop_outputs(vx, v_ref_new, bits, v_codes, v_scales, (b, h, s_cap), "V")
+    n = len(kx)
+    shp = _Shape(b, h, s_cap, d)
+    bits_arr = (ctypes.c_int32 * n)(*[int(x) for x in bits])
+    st = lib.rq_encode_append_kv(ctypes.byref(shp), n, t, _ptr_array(kx), _ptr_array(vx), bits_arr, _ptr(k_ref_new),
+                                 _ptr(v_ref_new), _ptr(pos), _ptr(k_ref_cache), _ptr(v_ref_cache),
+                                 _ptr_array(k_codes), _ptr_array(k_scales), _ptr_array(v_codes), _ptr_array(v_scales),
+                                 _stream(k_ref_new.device, stream))
+    _check(st, "rq_encode_append_kv")
+
+
+def encode_append_paged_kv(kx: Sequence[torch.Tensor], vx: Sequence[torch.Tensor], k_ref_new: torch.Tensor,
+                           v_ref_new: torch.Tensor, bits: Sequence[int], pos: torch.Tensor, block_table: torch.Tensor,
+                           k_ref_pages: torch.Tensor, v_ref_pages: torch.Tensor, k_codes: Sequence[torch.Tensor],
+                           k_scales: Sequence[torch.Tensor], v_codes: Sequence[torch.Tensor],
+                           v_scales: Sequence[torch.Tensor], stream=None) -> None:
+    """rq_encode_append_paged_kv: encode_append_paged for K and V in one launch (bit-identical to two calls)."""
+    lib = _load()
+    b, h, t, d = k_ref_new.shape
+    n_blocks, _, p, _ = k_ref_pages.shape
+    _need(k_ref_new, "k_ref_new", torch.bfloat16, k_ref_new.shape)
+    _need(v_ref_new, "v_ref_new", torch.bfloat16, k_ref_new.shape, k_ref_new.device)
+    _need(k_ref_pages, "k_ref_pages", torch.bfloat16, (n_blocks, h, p, d), k_ref_new.device)
+    _need(v_ref_pages, "v_ref_pages", torch.bfloat16, (n_blocks, h, p, d), k_ref_new.device)
+    _need(pos, "pos", torch.int32, (b,), k_ref_new.device)
+    pages = _pages_of(block_table, p, n_blocks, b, k_ref_new.device)
+    _check_loop_outputs(kx, k_ref_new, bits, k_codes, k_scales, (n_blocks, h, p), "K")
+    _check_loop_outputs(vx, v_ref_new, bits, v_codes, v_scales, (n_blocks, h, p), "V")
+    n = len(kx)
+    shp = _Shape(b, h, pages.max_blocks * p, d)
+    bits_arr = (ctypes.c_int32 * n)(*[int(x) for x in bits])
+    st = lib.rq_encode_append_paged_kv(ctypes.byref(shp), ctypes.byref(pages), n, t, _ptr_array(kx), _ptr_array(vx),
+                                       bits_arr, _ptr(k_ref_new), _ptr(v_ref_new), _ptr(pos), _ptr(k_ref_pages),
+                                       _ptr(v_ref_pages), _ptr_array(k_codes), _ptr_array(k_scales),
+                                       _ptr_array(v_codes), _ptr_array(v_scales), _stream(k_ref_new.device, stream))
+    _check(st, "rq_encode_append_paged_kv")
 
 
 def encode_layers(xs: Sequence[Sequence[torch.Tensor]], refs: Sequence[torch.Tensor],

@@ -126,12 +126,13 @@ int encode_check(const rq_shape* shape, int32_t n_loops, const uint16_t* const* 
 
 // Shared by rq_encode (ref = the final loop) and rq_encode_rotonly (ref = NULL:
 // a zero reference, so each state is quantized directly after the rotation).
-int encode_common(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
-                  const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, int32_t refits,
-                  void* stream) {
+// Checks one tensor's encode and fills its launch arguments (no HIP call).
+int encode_fill(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
+                const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, int32_t refits,
+                EncodeArgs& a) {
   const int st = encode_check(shape, n_loops, x, bits, ref, codes, scales, refits);
   if (st != RQ_OK) return st;
-  EncodeArgs a{};
+  a = EncodeArgs{};
   for (int i = 0; i < n_loops; ++i) {
     a.x[i] = x[i];
     a.codes[i] = codes[i];
@@ -142,7 +143,16 @@ int encode_common(const rq_shape* shape, int32_t n_loops, const uint16_t* const*
   a.n_loops = n_loops;
   a.refits = refits;
   a.n_vec = n_vectors(shape);
-  return hip_status(launch_encode(a, shape->head_dim, static_cast<hipStream_t>(stream)));
+  return RQ_OK;
+}
+
+int encode_common(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
+                  const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, int32_t refits,
+                  void* stream) {
+  EncodeArgs a;
+  const int st = encode_fill(shape, n_loops, x, bits, ref, codes, scales, refits, a);
+  if (st != RQ_OK) return st;
+  return hip_status(launch_encode(&a, 1, shape->head_dim, static_cast<hipStream_t>(stream)));
 }
 
 int reconstruct_common(const rq_shape* shape, int32_t bits, const uint16_t* ref, const uint32_t* codes,
@@ -173,6 +183,18 @@ int rq_encode(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, 
               const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, void* stream) {
   if (ref == nullptr) return RQ_EINVAL;
   return encode_common(shape, n_loops, x, bits, ref, codes, scales, 0, stream);
+}
+
+int rq_encode_kv(const rq_shape* shape, int32_t n_loops, const uint16_t* const* kx, const uint16_t* const* vx,
+                 const int32_t* bits, const uint16_t* k_ref, const uint16_t* v_ref, uint32_t* const* k_codes,
+                 uint16_t* const* k_scales, uint32_t* const* v_codes, uint16_t* const* v_scales, void* stream) {
+  if (k_ref == nullptr || v_ref == nullptr) return RQ_EINVAL;
+  EncodeArgs a[2];
+  int st = encode_fill(shape, n_loops, kx, bits, k_ref, k_codes, k_scales, 0, a[0]);
+  if (st != RQ_OK) return st;
+  st = encode_fill(shape, n_loops, vx, bits, v_ref, v_codes, v_scales, 0, a[1]);
+  if (st != RQ_OK) return st;
+  return hip_status(launch_encode(a, 2, shape->head_dim, static_cast<hipStream_t>(stream)));
 }
 
 int rq_encode_refit(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
@@ -209,9 +231,10 @@ int log2_of(int32_t p) {
   return l;
 }
 
-int append_impl(const rq_shape* cache, const rq_pages* pages, int32_t n_loops, int32_t t_new,
+// Checks one tensor's append and fills its launch arguments (no HIP call).
+int append_fill(const rq_shape* cache, const rq_pages* pages, int32_t n_loops, int32_t t_new,
                 const uint16_t* const* x, const int32_t* bits, const uint16_t* ref_new, const int32_t* pos,
-                uint16_t* ref_cache, uint32_t* const* codes, uint16_t* const* scales, void* stream) {
+                uint16_t* ref_cache, uint32_t* const* codes, uint16_t* const* scales, EncodeArgs& a) {
   int st = check_shape(cache);
   if (st != RQ_OK) return st;
   if (pages != nullptr) {
@@ -232,7 +255,7 @@ int append_impl(const rq_shape* cache, const rq_pages* pages, int32_t n_loops, i
   for (int i = 0; i < n_loops; ++i) {
     if (!aligned16(x[i]) || !aligned16(codes[i]) || !aligned16(scales[i])) return RQ_EALIGN;
   }
-  EncodeArgs a{};
+  a = EncodeArgs{};
   for (int i = 0; i < n_loops; ++i) {
     a.x[i] = x[i];
     a.codes[i] = codes[i];
@@ -253,7 +276,30 @@ int append_impl(const rq_shape* cache, const rq_pages* pages, int32_t n_loops, i
     a.n_blocks = pages->n_blocks;
   }
   a.n_vec = (int64_t)cache->batch * cache->n_kv_heads * t_new;
-  return hip_status(launch_encode(a, cache->head_dim, static_cast<hipStream_t>(stream)));
+  return RQ_OK;
+}
+
+int append_impl(const rq_shape* cache, const rq_pages* pages, int32_t n_loops, int32_t t_new,
+                const uint16_t* const* x, const int32_t* bits, const uint16_t* ref_new, const int32_t* pos,
+                uint16_t* ref_cache, uint32_t* const* codes, uint16_t* const* scales, void* stream) {
+  EncodeArgs a;
+  const int st = append_fill(cache, pages, n_loops, t_new, x, bits, ref_new, pos, ref_cache, codes, scales, a);
+  if (st != RQ_OK) return st;
+  return hip_status(launch_encode(&a, 1, cache->head_dim, static_cast<hipStream_t>(stream)));
+}
+
+// K and V of one append in one launch
+int append_kv_impl(const rq_shape* cache, const rq_pages* pages, int32_t n_loops, int32_t t_new,
+                   const uint16_t* const* kx, const uint16_t* const* vx, const int32_t* bits,
+                   const uint16_t* k_ref_new, const uint16_t* v_ref_new, const int32_t* pos, uint16_t* k_ref_cache,
+                   uint16_t* v_ref_cache, uint32_t* const* k_codes, uint16_t* const* k_scales,
+                   uint32_t* const* v_codes, uint16_t* const* v_scales, void* stream) {
+  EncodeArgs a[2];
+  int st = append_fill(cache, pages, n_loops, t_new, kx, bits, k_ref_new, pos, k_ref_cache, k_codes, k_scales, a[0]);
+  if (st != RQ_OK) return st;
+  st = append_fill(cache, pages, n_loops, t_new, vx, bits, v_ref_new, pos, v_ref_cache, v_codes, v_scales, a[1]);
+  if (st != RQ_OK) return st;
+  return hip_status(launch_encode(a, 2, cache->head_dim, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -274,6 +320,26 @@ int rq_encode_append_paged(const rq_shape* cache, const rq_pages* pages, int32_t
   return append_impl(cache, pages, n_loops, t_new, x, bits, ref_new, pos, ref_pages, codes, scales, stream);
 }
 
+int rq_encode_append_kv(const rq_shape* cache, int32_t n_loops, int32_t t_new, const uint16_t* const* kx,
+                        const uint16_t* const* vx, const int32_t* bits, const uint16_t* k_ref_new,
+                        const uint16_t* v_ref_new, const int32_t* pos, uint16_t* k_ref_cache, uint16_t* v_ref_cache,
+                        uint32_t* const* k_codes, uint16_t* const* k_scales, uint32_t* const* v_codes,
+                        uint16_t* const* v_scales, void* stream) {
+  return append_kv_impl(cache, nullptr, n_loops, t_new, kx, vx, bits, k_ref_new, v_ref_new, pos, k_ref_cache,
+                        v_ref_cache, k_codes, k_scales, v_codes, v_scales, stream);
+}
+
+int rq_encode_append_paged_kv(const rq_shape* cache, const rq_pages* pages, int32_t n_loops, int32_t t_new,
+                              const uint16_t* const* kx, const uint16_t* const* vx, const int32_t* bits,
+                              const uint16_t* k_ref_new, const uint16_t* v_ref_new, const int32_t* pos,
+                              uint16_t* k_ref_pages, uint16_t* v_ref_pages, uint32_t* const* k_codes,
+                              uint16_t* const* k_scales, uint32_t* const* v_codes, uint16_t* const* v_scales,
+                              void* stream) {
+  if (pages == nullptr) return RQ_EINVAL;
+  return append_kv_impl(cache, pages, n_loops, t_new, kx, vx, bits, k_ref_new, v_ref_new, pos, k_ref_pages,
+                        v_ref_pages, k_codes, k_scales, v_codes, v_scales, stream);
+}
+
 int rq_encode_layers(const rq_shape* shape, int32_t n_layers, int32_t n_loops, const uint16_t* const* x,
                      const int32_t* bits_table, const uint16_t* const* ref, uint32_t* const* codes,
                      uint16_t* const* scales, void* stream) {
@@ -286,9 +352,16 @@ int rq_encode_layers(const rq_shape* shape, int32_t n_layers, int32_t n_loops, c
     const int st = encode_check(shape, n_loops, x + o, bits_table + o, ref[l], codes + o, scales + o, 0);
     if (st != RQ_OK) return st;
   }
-  for (int l = 0; l < n_layers; ++l) {
-    const int64_t o = (int64_t)l * n_loops;
-    const int st = encode_common(shape, n_loops, x + o, bits_table + o, ref[l], codes + o, scales + o, 0, stream);
+  // layers go two to a launch
+  for (int l = 0; l < n_layers; l += 2) {
+    const int n = n_layers - l < 2 ? n_layers - l : 2;
+    EncodeArgs a[2];
+    for (int j = 0; j < n; ++j) {
+      const int64_t o = (int64_t)(l + j) * n_loops;
+      const int st = encode_fill(shape, n_loops, x + o, bits_table + o, ref[l + j], codes + o, scales + o, 0, a[j]);
+      if (st != RQ_OK) return st;
+    }
+    const int st = hip_status(launch_encode(a, n, shape->head_dim, static_cast<hipStream_t>(stream)));
     if (st != RQ_OK) return st;
   }
   return RQ_OK;

@@ -136,8 +136,11 @@ __device__ __forceinline__ float quantize_group(const float* y, int refits, uint
 //    on the lane bits go across lanes inside a quad (DPP).
 //  * WIDE instantiations also take INT3 and INT8 loops; the INT2/INT4-only
 //    ones carry no code for them.
-template <int D, int PER, bool REFIT, bool APPEND, bool WIDE>
-__global__ __launch_bounds__(256) void rq_encode_kernel(EncodeArgs a) {
+// SETS: tensors of the launch (1, or 2 for K and V together); blockIdx.y
+// picks the tensor.
+template <int D, int PER, bool REFIT, bool APPEND, bool WIDE, int SETS>
+__global__ __launch_bounds__(256) void rq_encode_kernel(EncodeLaunch launch) {
+  const EncodeArgs& a = launch.set[SETS == 1 ? 0 : blockIdx.y];
   constexpr int kLanes = D / PER;  // lanes per vector
   constexpr int kVecPerBlock = 256 / kLanes;
   constexpr int NGL = PER / 32;    // scale groups per lane
@@ -376,29 +379,44 @@ static unsigned grid_for(int64_t n_vec, int vec_per_block) {
 // registers) and runs slower.
 constexpr int kEncodePer = 32;
 
-template <int D, bool WIDE>
-static void launch_encode_dw(const EncodeArgs& a, hipStream_t stream) {
+template <int D, bool WIDE, int SETS>
+static void launch_encode_dw(const EncodeLaunch& l, hipStream_t stream) {
   constexpr int per = kEncodePer;
-  const dim3 grid(grid_for(a.n_vec, 256 / (D / per)));
+  const EncodeArgs& a = l.set[0];
+  const dim3 grid(grid_for(a.n_vec, 256 / (D / per)), SETS);
   if (a.pos != nullptr)
-    hipLaunchKernelGGL((rq_encode_kernel<D, per, false, true, WIDE>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((rq_encode_kernel<D, per, false, true, WIDE, SETS>), grid, dim3(256), 0, stream, l);
   else if (a.refits > 0)
-    hipLaunchKernelGGL((rq_encode_kernel<D, per, true, false, WIDE>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((rq_encode_kernel<D, per, true, false, WIDE, SETS>), grid, dim3(256), 0, stream, l);
   else
-    hipLaunchKernelGGL((rq_encode_kernel<D, per, false, false, WIDE>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((rq_encode_kernel<D, per, false, false, WIDE, SETS>), grid, dim3(256), 0, stream, l);
 }
 
 template <int D>
-static void launch_encode_d(const EncodeArgs& a, hipStream_t stream) {
+static void launch_encode_d(const EncodeLaunch& l, int n_sets, hipStream_t stream) {
   bool wide = false;
-  for (int l = 0; l < a.n_loops; ++l) wide = wide || a.bits[l] == 3 || a.bits[l] == 8;
-  if (wide) launch_encode_dw<D, true>(a, stream);
-  else launch_encode_dw<D, false>(a, stream);
+  for (int s = 0; s < n_sets; ++s)
+    for (int i = 0; i < l.set[s].n_loops; ++i) wide = wide || l.set[s].bits[i] == 3 || l.set[s].bits[i] == 8;
+  if (n_sets == 2) {
+    if (wide) launch_encode_dw<D, true, 2>(l, stream);
+    else launch_encode_dw<D, false, 2>(l, stream);
+  } else {
+    if (wide) launch_encode_dw<D, true, 1>(l, stream);
+    else launch_encode_dw<D, false, 1>(l, stream);
+  }
 }
 
-hipError_t launch_encode(const EncodeArgs& a, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) launch_encode_d<128>(a, stream);
-  else launch_encode_d<64>(a, stream);
+hipError_t launch_encode(const EncodeArgs* sets, int n_sets, int head_dim, hipStream_t stream) {
+  if (n_sets < 1 || n_sets > kMaxEncodeSets) return hipErrorInvalidValue;
+  for (int s = 1; s < n_sets; ++s) {  // one grid: the sets share the shape and the kind of launch
+    if (sets[s].n_vec != sets[0].n_vec || (sets[s].pos == nullptr) != (sets[0].pos == nullptr) ||
+        sets[s].refits != sets[0].refits)
+      return hipErrorInvalidValue;
+  }
+  EncodeLaunch l{};
+  for (int s = 0; s < n_sets; ++s) l.set[s] = sets[s];
+  if (head_dim == 128) launch_encode_d<128>(l, n_sets, stream);
+  else launch_encode_d<64>(l, n_sets, stream);
   return hipGetLastError();
 }
 

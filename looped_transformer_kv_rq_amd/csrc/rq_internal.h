@@ -35,6 +35,13 @@ struct EncodeArgs {
   int64_t n_vec;  // batch * n_kv_heads * seq_len
 };
 
+// One encode launch holds up to kMaxEncodeSets tensors of the same shape (K
+// and V): blockIdx.y picks the tensor.
+constexpr int kMaxEncodeSets = 2;
+struct EncodeLaunch {
+  EncodeArgs set[kMaxEncodeSets];
+};
+
 struct ReconstructArgs {
   const uint16_t* ref;  // NULL: zero reference (rotation-only baseline)
   const uint32_t* codes;
@@ -108,7 +115,7 @@ struct QueryPrepArgs {
 // launchers (defined in the .hip files); return hipGetLastError()
 // ---------------------------------------------------------------------------
 
-hipError_t launch_encode(const EncodeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_encode(const EncodeArgs* sets, int n_sets, int head_dim, hipStream_t stream);
 hipError_t launch_reconstruct(const ReconstructArgs& a, int head_dim, int bits, int out_bf16, hipStream_t stream);
 // sets[0 .. n_sets): argument sets of one launch (the same shape, splits,
 // cache and paging; their own rows and loops)

@@ -259,3 +259,46 @@ def test_paged_argument_checks():
     assert app(t_new=0) == rq.RQ_EINVAL
     assert app(pages=rq._Pages(FAKE, max_blocks, 100, 16)) == rq.RQ_EUNSUPPORTED
     assert app(pages=rq._Pages(FAKE, 3, P, 16)) == rq.RQ_EINVAL
+
+
+def test_kv_entry_points_check_both_tensors():
+    """rq_encode_kv and the K+V appends reject a bad argument on either tensor
+    before any HIP call (each returns the status the single-tensor call gives)."""
+    lib = rq._load()
+    bits = (ctypes.c_int32 * 1)(2)
+    good = dict(kx=_ptrs(FAKE), vx=_ptrs(FAKE), kref=FAKE, vref=FAKE, kc=_ptrs(FAKE), ks=_ptrs(FAKE), vc=_ptrs(FAKE),
+                vs=_ptrs(FAKE))
+
+    def enc(shape=_shape(), **kw):
+        a = {**good, **kw}
+        return lib.rq_encode_kv(ctypes.byref(shape), 1, a["kx"], a["vx"], bits, a["kref"], a["vref"], a["kc"],
+                                a["ks"], a["vc"], a["vs"], None)
+
+    assert enc(kref=None) == rq.RQ_EINVAL
+    assert enc(vref=None) == rq.RQ_EINVAL
+    assert enc(vx=_ptrs(0)) == rq.RQ_EINVAL
+    assert enc(vs=_ptrs(FAKE + 2)) == rq.RQ_EALIGN
+    assert enc(kc=_ptrs(FAKE + 4)) == rq.RQ_EALIGN
+    assert enc(shape=_shape(d=96)) == rq.RQ_EUNSUPPORTED
+
+    sh = _shape(b=2, h=2, s=256, d=64)
+
+    def app(**kw):
+        a = {**good, **kw}
+        return lib.rq_encode_append_kv(ctypes.byref(sh), 1, 1, a["kx"], a["vx"], bits, a["kref"], a["vref"], FAKE,
+                                       FAKE, a.get("vcache", FAKE), a["kc"], a["ks"], a["vc"], a["vs"], None)
+
+    assert app(vref=None) == rq.RQ_EINVAL
+    assert app(vcache=FAKE + 8) == rq.RQ_EALIGN
+    assert app(vc=_ptrs(0)) == rq.RQ_EINVAL
+    pages = rq._Pages(FAKE, 4, 64, 16)
+
+    def papp(pg=pages, **kw):
+        a = {**good, **kw}
+        p = None if pg is None else ctypes.byref(pg)
+        return lib.rq_encode_append_paged_kv(ctypes.byref(sh), p, 1, 1, a["kx"], a["vx"], bits, a["kref"], a["vref"],
+                                             FAKE, FAKE, FAKE, a["kc"], a["ks"], a["vc"], a["vs"], None)
+
+    assert papp(pg=None) == rq.RQ_EINVAL
+    assert papp(pg=rq._Pages(FAKE, 4, 96, 16)) == rq.RQ_EUNSUPPORTED
+    assert papp(vs=_ptrs(FAKE + 2)) == rq.RQ_EALIGN
