@@ -62,7 +62,8 @@ SplitPlan plan_splits(const rq_shape* s, int32_t requested) {
 }
 
 // Workspace: split partials [n_loops][B][Hq][n_splits][2D + 2] floats, padded
-// to 256 bytes, then one rotated-query record per query row.
+// to 256 bytes, then one rotated-query record per query row (written only by
+// the calls that run the prep kernel).
 size_t partial_bytes(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int32_t n_splits) {
   const size_t b = (size_t)n_loops * s->batch * n_q_heads * n_splits * (2 * s->head_dim + 2) * sizeof(float);
   return (b + 255) / 256 * 256;
@@ -124,9 +125,9 @@ int encode_check(const rq_shape* shape, int32_t n_loops, const uint16_t* const* 
   return RQ_OK;
 }
 
-// Shared by rq_encode (ref = the final loop) and rq_encode_rotonly (ref = NULL:
-// a zero reference, so each state is quantized directly after the rotation).
 // Checks one tensor's encode and fills its launch arguments (no HIP call).
+// ref = the final loop, or NULL for the rotation-only baseline (a zero
+// reference, so each state is quantized directly after the rotation).
 int encode_fill(const rq_shape* shape, int32_t n_loops, const uint16_t* const* x, const int32_t* bits,
                 const uint16_t* ref, uint32_t* const* codes, uint16_t* const* scales, int32_t refits,
                 EncodeArgs& a) {

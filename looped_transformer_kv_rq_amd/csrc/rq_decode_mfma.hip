@@ -8,14 +8,17 @@
 // (normalised Walsh-Hadamard) is symmetric, so
 //   score  = q . k_ref + (H q) . (s * lev)
 //   output = sum_t p_t v_ref,t + H sum_t p_t (s * lev)_t.
-// rq_query_prep rotates each query once. The partial kernel keeps the residual
-// terms in the rotated domain, and the combine kernel applies H to the merged
-// residual accumulator of each query row once.
+// The query is rotated once per block by the partial kernel itself (or, for the
+// launches that cannot, once per call by rq_query_prep). The partial kernel
+// keeps the residual terms in the rotated domain, and the combine kernel
+// applies H to the merged residual accumulator of each query row once.
 //
 // Partial kernel: one block is four independent waves over one split of one
 // (batch, kv head) row. A wave takes 32-token tiles (tiles w, w+4, ...). Every
 // query row of the kv head (loops x G query heads, at most 32 = two 16-row
-// blocks) is one MFMA column. All products run on v_mfma_f32_16x16x32:
+// blocks) is one MFMA column; a launch with more than 16 rows whose loops fit
+// 16 each runs as two argument sets of one 16-row block. All products run on
+// v_mfma_f32_16x16x32:
 //  * reference scores S^T = K_ref Q^T (bf16; exact products, fp32 sums). The
 //    K tile is loaded straight into the A operand;
 //  * residual scores per loop and scale group (fp16). A code becomes the fp16
