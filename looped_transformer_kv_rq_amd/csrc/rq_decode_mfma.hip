@@ -51,6 +51,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "rq_device.h"
 #include "rq_internal.h"
@@ -1187,11 +1188,16 @@ int decode_launch_lds_bytes(const DecodeArgs* sets, int n_sets, int head_dim, bo
 
 template <int D, int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
 static void launch_mfma_kernel(const DecodeLaunch& l, dim3 grid, int lds, hipStream_t stream) {
-  static bool attr_set = false;  // lift the default dynamic-LDS cap once per instantiation
-  if (!attr_set) {
+  // Lift the default dynamic-LDS cap once per instantiation and device (the
+  // attribute belongs to the current device; devices past 63 set it every time).
+  static std::atomic<uint64_t> lifted{0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
+  if ((lifted.load(std::memory_order_relaxed) & bit) == 0) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED, SETS>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxBlockLds);
-    attr_set = true;
+    lifted.fetch_or(bit, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED, SETS>), grid, dim3(256), lds, stream, l);
 }
