@@ -136,6 +136,13 @@ constexpr uint32_t kLutInt3Hi = 0x43413E38u;  // fp16 high bytes of 0.5, 1.5, 2.
 constexpr int kTile = 32;
 constexpr int kTile16 = 16;  // tokens per MFMA row block
 
+// Residual accumulator blocks per 16-row block: 2 D/32 output blocks, and at
+// NB = 1 one more per scale group for the weight sums of the INT2 / INT4
+// decode (residual_pv). At NB = 2 those would push the kernel into spills, so
+// it decodes every width through the byte table.
+template <int D, int NB>
+constexpr int kResBlocks = 2 * (D / 32) + (NB == 1 ? D / 32 : 0);
+
 template <int D>
 struct MfmaGeom {
   static constexpr int NG = D / 32;    // scale groups = k-steps of the score products
@@ -527,9 +534,12 @@ __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, con
 template <int D, int NB, int BITS>
 __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const unsigned char* base,
                                             const float (&p)[NB][8], const int (&my_loop)[NB],
-                                            f32x4_t (&o_res)[NB][2 * (D / 32)], int m, int g, const Consts& k) {
+                                            f32x4_t (&o_res)[NB][kResBlocks<D, NB>], int m, int g, const Consts& k) {
   constexpr int NG = D / 32;
   constexpr int W = D * BITS / 32;
+  // INT2 / INT4 at NB = 1: codes decoded through the fp16 mantissa (see the
+  // correction after the token loop); other widths through byte tables
+  constexpr bool kMant = (BITS == 2 || BITS == 4) && NB == 1;
   const unsigned char* vc_l = base + 128 * W + 64 * NG;
   const unsigned char* vs_l = vc_l + 128 * W;
   const int G = a.group;
@@ -586,6 +596,12 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
       bop.y = mul_f16x2(p16[1], vperm(vsw[3][grp >> 1], vsw[2][grp >> 1], hsel));
       bop.z = mul_f16x2(p16[2], vperm(vsw[5][grp >> 1], vsw[4][grp >> 1], hsel));
       bop.w = mul_f16x2(p16[3], vperm(vsw[7][grp >> 1], vsw[6][grp >> 1], hsel));
+      if constexpr (kMant) {
+        // the group's weight sum (P s summed over the tile's tokens), in every
+        // element of the block: an A operand of fp16 ones
+        const uint4 ones = make_uint4(k.one, k.one, k.one, k.one);
+        o_res[nb][2 * NG + grp] = mma_f16(ones, bop, o_res[nb][2 * NG + grp]);
+      }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         if constexpr (BITS == 8) {
@@ -621,6 +637,18 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
           alo.y = vperm(kLutInt3Hi, kLutInt3Lo, and_or(vperm(ha.w, ha.z, hsel) << hsh, k.m3s, and_or(y1, k.m2, k.sel0)));
           alo.z = vperm(kLutInt3Hi, kLutInt3Lo, and_or(vperm(hb.y, hb.x, hsel) << hsh, k.m3s, and_or(y2, k.m2, k.sel0)));
           alo.w = vperm(kLutInt3Hi, kLutInt3Lo, and_or(vperm(hb.w, hb.z, hsel) << hsh, k.m3s, and_or(y3, k.m2, k.sel0)));
+        } else if constexpr (kMant && BITS == 2) {
+          // the code in the top mantissa bits of 1.0: fp16 1 + c/4
+          alo.x = and_or(y0, k.m2, k.one);
+          alo.y = and_or(y1, k.m2, k.one);
+          alo.z = and_or(y2, k.m2, k.one);
+          alo.w = and_or(y3, k.m2, k.one);
+        } else if constexpr (kMant) {
+          // the nibble at mantissa bits 6..9: fp16 1 + c/16
+          alo.x = and_or(y0 >> 2, k.m4, k.one);
+          alo.y = and_or(y1 >> 2, k.m4, k.one);
+          alo.z = and_or(y2 >> 2, k.m4, k.one);
+          alo.w = and_or(y3 >> 2, k.m4, k.one);
         } else {
           alo.x = vperm(0u, kLutInt2, and_or(y0, k.m2, k.sel0));
           alo.y = vperm(0u, kLutInt2, and_or(y1, k.m2, k.sel0));
@@ -628,7 +656,7 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
           alo.w = vperm(0u, kLutInt2, and_or(y3, k.m2, k.sel0));
         }
         o_res[nb][2 * grp + hf] = mma_f16(alo, bop, o_res[nb][2 * grp + hf]);
-        if constexpr (BITS == 4) {
+        if constexpr (BITS == 4 && !kMant) {
           uint4 ahi;
           ahi.x = vperm(0u, kLutInt4Hi, and_or(y0 >> 2, k.m2, k.sel0));
           ahi.y = vperm(0u, kLutInt4Hi, and_or(y1 >> 2, k.m2, k.sel0));
@@ -739,7 +767,7 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
                                              int m, int g, const uint4 (&ka)[2][D / 32], const uint4 (&qB)[NB][D / 32],
                                              const uint4 (&qtB)[NB][D / 32], const float (&qoff)[NB][D / 32],
                                              const float (&qmul)[NB], const int (&my_loop)[NB],
-                                             f32x4_t (&o_ref)[NB][D / 64][4], f32x4_t (&o_res)[NB][2 * (D / 32)],
+                                             f32x4_t (&o_ref)[NB][D / 64][4], f32x4_t (&o_res)[NB][kResBlocks<D, NB>],
                                              float (&m_run)[NB], float (&l_run)[NB], const Consts& k) {
   using Gm = MfmaGeom<D>;
   constexpr int NG = Gm::NG, NH = Gm::NH;
@@ -807,7 +835,7 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
         for (int r = 0; r < 4; ++r) o_ref[nb][hh][r] *= alpha;
       if constexpr (RESID) {
 #pragma unroll
-        for (int k = 0; k < 2 * NG; ++k) o_res[nb][k] *= alpha;
+        for (int k = 0; k < kResBlocks<D, NB>; ++k) o_res[nb][k] *= alpha;
       }
     }
   }
@@ -951,7 +979,7 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   // wave (prefetching the next tile) costs more occupancy than it hides.
   unsigned char* buf = smem + wave * a.lds_wave_bytes;
   f32x4_t o_ref[NB][NH][4];
-  f32x4_t o_res[NB][2 * NG];
+  f32x4_t o_res[NB][kResBlocks<D, NB>];
   float m_run[NB], l_run[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -962,7 +990,7 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) o_ref[nb][hh][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 2 * NG; ++k) o_res[nb][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < kResBlocks<D, NB>; ++k) o_res[nb][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   const int t_begin = split * a.tokens_per_split;
@@ -1074,6 +1102,24 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
                                kc);
     wait_lds();
     wave_sync_lds();  // the buffer is free for the next tile's DMA
+  }
+
+  // At NB = 1 the INT2 / INT4 rows accumulated sum P s (1 + c/2^b). The level
+  // c - (2^(b-1) - 1/2) is 2^b (1 + c/2^b) - (2^b + 2^(b-1) - 1/2), so the
+  // level sum is 2^b times the accumulator minus that constant times the
+  // group's weight sum. Rows of INT3 / INT8 loops hold level sums already.
+  if constexpr (RESID && NB == 1) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int lb = my_loop[nb] >= 0 ? a.bits[my_loop[nb]] : 0;
+      const bool mant = lb == 2 || lb == 4;
+      const float mulc = mant ? qmul[nb] : 1.0f;
+      const float offc = mant ? 1.5f * qmul[nb] - 0.5f : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 2 * NG; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o_res[nb][k][i] = fmaf(mulc, o_res[nb][k][i], -offc * o_res[nb][2 * NG + k / 2][i]);
+    }
   }
 
   // ------------------------------------------------ merge the four waves
