@@ -103,6 +103,41 @@ def test_decode_head_groupings(hq, hkv, n_loops):
     _run_case(w, range(n_loops), _all_rows(w))
 
 
+def _constant_words(shape, d, bits, c):
+    """Code words [..., d*bits/32] holding code c at every coordinate (the
+    layouts of oracle.pack_codes, written out for a constant)."""
+    if bits == 3:
+        lo = sum((c & 3) << (2 * j) for j in range(16))
+        hi = 0xFFFFFFFF if c & 4 else 0
+        words = np.empty(shape + (3 * d // 32,), dtype=np.uint32)
+        words[..., : d // 16] = lo
+        words[..., d // 16:] = hi
+        return words
+    return np.full(shape + (d * bits // 32,), sum(c << (bits * j) for j in range(32 // bits)), dtype=np.uint32)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("hq", [8, 40])
+def test_decode_constant_v_codes(bits, hq):
+    """Every V code of the residual loop set to one value: the lowest, the
+    highest and the first positive level. The residual part of each output is
+    then that level times the scale-weighted softmax sum of each group, which a
+    decode that forms levels as 2^b (1 + c/2^b) minus an offset must cancel
+    exactly. G = 4 runs one 16-row block; G = 20 two (the byte-table levels)."""
+    w = workloads.Workload("constv", 98, 2, 1, 2, hq, 128, 150, (bits, 0), (0.2, 0.0))
+    kref, vref, res = _packed_cache(w, [0, 1])
+    (kw, ks), (vw, vs) = res[0]
+    q_bits = workloads.q_tensor(w)
+    rows = _all_rows(w)
+    for c in (0, (1 << bits) - 1, 1 << (bits - 1)):
+        print(f"constant V codes bits={bits} hq={hq} c={c}", flush=True)
+        cres = {0: ((kw, ks), (_constant_words(vw.shape[:-1], w.head_dim, bits, c), vs))}
+        out = rq.decode_attn(to_dev(q_bits), to_dev(kref), to_dev(vref), _views(w, [0, 1], cres))
+        torch.cuda.synchronize()
+        got = _gpu_rows(out.cpu().numpy(), rows, w.group_size)
+        assert_attn_close(got, _oracle_rows(w, [0, 1], q_bits, kref, vref, cres, rows))
+
+
 def test_decode_split_counts_agree():
     w = workloads.Workload("splits", 92, 2, 1, 2, 8, 128, 1000, (2, 0), (0.1, 0.0))
     for n in (1, 3, 16):
