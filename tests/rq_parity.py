@@ -17,6 +17,7 @@ import numpy as np
 import torch
 
 import oracle
+import workloads
 
 BOUNDARY_EPS = 1e-5
 ATTN_TOL = 2e-3
@@ -40,6 +41,34 @@ def to_host_words(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy().view(np.uint32)
 
 
+def unpack_words(words: np.ndarray, bits: int) -> np.ndarray:
+    """Codes [..., D] of packed words, for words read back from the device, so
+    that no oracle function takes the GPU's output. The layout is the library
+    header's: for b in {2, 4, 8} word w holds coordinates [(32/b) w, (32/b)(w+1)),
+    coordinate j of the word at bits [b j, b j + b); for b = 3 the INT2 words of
+    the low two bits come first, then one word of bit 2 per 32 coordinates."""
+    w = np.asarray(words).astype(np.uint32)
+    if bits == 3:
+        d = w.shape[-1] // 3 * 32
+        lo = unpack_words(w[..., : d // 16], 2)
+        hi = (w[..., d // 16:, None] >> np.arange(32, dtype=np.uint32)) & np.uint32(1)
+        return lo | (hi.reshape(w.shape[:-1] + (d,)) << np.uint32(2))
+    per = 32 // bits
+    c = (w[..., :, None] >> (bits * np.arange(per, dtype=np.uint32))) & np.uint32((1 << bits) - 1)
+    return c.reshape(w.shape[:-1] + (w.shape[-1] * per,))
+
+
+def host_f64(bits_u16: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns read back from the device, as float64."""
+    return workloads.bf16_bits_to_f32(bits_u16).astype(np.float64)
+
+
+def recon_error(x_hat: np.ndarray, x_bits: np.ndarray, ref_bits: np.ndarray) -> float:
+    """|X_hat - X|_F / |X - X_ref|_F of a reconstruction read back from the device."""
+    x, xr = host_f64(x_bits), host_f64(ref_bits)
+    return float(np.linalg.norm(x_hat - x) / np.linalg.norm(x - xr))
+
+
 def exempt_mask(x_bits: np.ndarray, ref_bits: np.ndarray, bits: int) -> np.ndarray:
     """Coordinates within BOUNDARY_EPS of a code decision threshold (fp64)."""
     r = oracle.bf16_to_f64(x_bits) - oracle.bf16_to_f64(ref_bits)
@@ -56,8 +85,8 @@ def compare_codes(gpu_words, gpu_scales, orc_words, orc_scales, x_bits, ref_bits
     """Assert parity of one encoded tensor (any leading shape, [..., D] coords).
     Returns the number of exempt coordinates that differed."""
     d = x_bits.shape[-1]
-    cg = oracle.unpack_codes(gpu_words, bits)
-    co = oracle.unpack_codes(orc_words, bits)
+    cg = unpack_words(gpu_words, bits)
+    co = unpack_words(orc_words, bits)
     diff = cg != co
     n_diff = int(diff.sum())
     bad_groups = np.zeros(gpu_scales.shape, dtype=bool)
@@ -113,8 +142,8 @@ def compare_codes_refit(gpu_words, gpu_scales, orc_words, orc_scales, x_bits, re
     not exempt (refit_exempt_groups) match the oracle (codes bit-exact, scales
     within one fp16 ulp). Returns the number of exempt groups that differ."""
     d = x_bits.shape[-1]
-    cg = oracle.unpack_codes(gpu_words, bits)
-    co = oracle.unpack_codes(orc_words, bits)
+    cg = unpack_words(gpu_words, bits)
+    co = unpack_words(orc_words, bits)
     gdiff = (cg != co).reshape(cg.shape[:-1] + (d // 32, 32)).any(axis=-1)
     ulp = np.abs(gpu_scales.astype(np.int32) - orc_scales.astype(np.int32))
     gdiff |= ulp > 1

@@ -6,7 +6,7 @@ import torch
 import looped_transformer_kv_rq_amd as rq
 import oracle
 import workloads
-from rq_parity import (RECON_TOL, compare_codes, to_dev, to_host_u16, to_host_words)
+from rq_parity import (RECON_TOL, compare_codes, recon_error, to_dev, to_host_u16, to_host_words)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -161,7 +161,7 @@ def test_reconstruction_error_end_to_end(name):
         codes, scales = rq.encode(xd[:-1], xd[-1], bits)
         for l, bl in enumerate(bits):
             xh = rq.reconstruct(xd[-1], codes[l], scales[l], bl).cpu().numpy().astype(np.float64)
-            e_gpu = oracle.reconstruction_error(xh, xs[l], xs[-1])
+            e_gpu = recon_error(xh, xs[l], xs[-1])
             ow, os_ = oracle.encode(xs[l], xs[-1], bl)
             e_orc = oracle.reconstruction_error(oracle.reconstruct(xs[-1], ow, os_, bl), xs[l], xs[-1])
             assert abs(e_gpu - e_orc) <= RECON_TOL, (name, tensor, l, e_gpu, e_orc)

@@ -50,6 +50,17 @@ def _table(rng, B, max_blocks, lens, P, spare):
     return table, len(perm)
 
 
+def _dense_from_pages(pages, table, P, S):
+    """Dense [B, H, S, ...] copy of a paged cache read back from the device:
+    position t of sequence b from block table[b, t // P]; unmapped blocks stay zero."""
+    out = np.zeros((table.shape[0], pages.shape[1], S) + pages.shape[3:], dtype=pages.dtype)
+    for b in range(table.shape[0]):
+        for j in range(S // P):
+            if 0 <= table[b, j] < pages.shape[0]:
+                out[b, :, j * P:(j + 1) * P] = pages[table[b, j]]
+    return out
+
+
 def _scatter(dense, table, lens, P, n_blocks, fill):
     """Paged copy of dense [B, H, S, row]: positions below lens[b] only; the rest is `fill`."""
     B, H, S = dense.shape[:3]
@@ -228,6 +239,11 @@ def test_paged_serving_steps_append_then_decode():
         rq.encode_append_paged([to_dev(x[:, :, :n0]) for x in src[:-1]], to_dev(src[-1][:, :, :n0]), bits, zero,
                                table, refp, codes, scales)
     views = [rq.LoopView(b, kc[i], ks[i], vc[i], vs[i]) for i, b in enumerate(bits)] + [rq.LoopView(0)]
+    # the oracle's cache: its own encode of every loop's whole history, dense
+    khat = [oracle.reconstruct(kl[-1], *oracle.encode(kl[i], kl[-1], bl), bl) for i, bl in enumerate(bits)]
+    vhat = [oracle.reconstruct(vl[-1], *oracle.encode(vl[i], vl[-1], bl), bl) for i, bl in enumerate(bits)]
+    khat.append(oracle.bf16_to_f64(kl[-1]))
+    vhat.append(oracle.bf16_to_f64(vl[-1]))
     lens_now = lens.copy()
     for step in range(3):
         q = _bf16(rng, (L, B, hq, d))
@@ -236,17 +252,6 @@ def test_paged_serving_steps_append_then_decode():
         out = rq.decode_attn_paged(to_dev(q), kref_p, vref_p, views, table,
                                    seq_lens=torch.from_numpy(lens_now).to(DEV),
                                    tail_k=[to_dev(x) for x in tail_k], tail_v=[to_dev(x) for x in tail_v])
-        # oracle: the dense cache the table describes, read back from the device pages
-        kr = oracle.gather_pages(to_host_u16(kref_p), table_np, P, S)
-        vr = oracle.gather_pages(to_host_u16(vref_p), table_np, P, S)
-        khat, vhat = [], []
-        for i, bl in enumerate(bits):
-            khat.append(oracle.reconstruct(kr, oracle.gather_pages(to_host_words(kc[i]), table_np, P, S),
-                                           oracle.gather_pages(to_host_u16(ks[i]), table_np, P, S), bl))
-            vhat.append(oracle.reconstruct(vr, oracle.gather_pages(to_host_words(vc[i]), table_np, P, S),
-                                           oracle.gather_pages(to_host_u16(vs[i]), table_np, P, S), bl))
-        khat.append(oracle.bf16_to_f64(kr))
-        vhat.append(oracle.bf16_to_f64(vr))
         expect = oracle.decode_attn_varlen(q, khat, vhat, lens_now, tail_k, tail_v)
         assert_attn_close(out.cpu().numpy(), expect)
         pos = torch.from_numpy(lens_now).to(DEV)
@@ -255,13 +260,13 @@ def test_paged_serving_steps_append_then_decode():
                                    refp, codes, scales)
         lens_now = lens_now + 1
     torch.cuda.synchronize()
-    kr = oracle.gather_pages(to_host_u16(kref_p), table_np, P, S)
+    kr = _dense_from_pages(to_host_u16(kref_p), table_np, P, S)
     for b in range(B):
         n = int(lens_now[b])
         np.testing.assert_array_equal(kr[b, :, :n], kl[-1][b, :, :n])
         for i, bl in enumerate(bits):
-            cw = oracle.gather_pages(to_host_words(kc[i]), table_np, P, S)
-            cs = oracle.gather_pages(to_host_u16(ks[i]), table_np, P, S)
+            cw = _dense_from_pages(to_host_words(kc[i]), table_np, P, S)
+            cs = _dense_from_pages(to_host_u16(ks[i]), table_np, P, S)
             ow, os_ = oracle.encode(kl[i][b, :, :n], kl[-1][b, :, :n], bl)
             compare_codes(cw[b, :, :n], cs[b, :, :n], ow, os_, kl[i][b, :, :n], kl[-1][b, :, :n], bl)
 
@@ -302,7 +307,8 @@ def test_serving_step_full_size_sampled_rows():
     l4_b16_s4k cache encoded on the GPU, prefix lengths drawn in [S/2, S) as
     the benchmark draws them, one bf16 tail position per loop, decoded over the
     dense cache and over a copy in 512 shuffled blocks of 128 positions;
-    sampled (batch, kv head) rows against the oracle."""
+    sampled (batch, kv head) rows against the oracle: their codes, then their
+    decode over the oracle's codes."""
     w = workloads.WORKLOADS["l4_b16_s4k"]
     bits = [b for b in w.bits if b]
     P, nbs = 128, w.seq_len // 128
@@ -310,6 +316,26 @@ def test_serving_step_full_size_sampled_rows():
     vx = [to_dev(x) for x in workloads.kv_tensors(w, workloads.TENSOR_V)]
     kc, ks = rq.encode(kx[:-1], kx[-1], bits)
     vc, vs = rq.encode(vx[:-1], vx[-1], bits)
+    torch.cuda.synchronize()
+    rows = [(0, 0), (7, 3), (15, 7)]
+    # The GPU's codes of the sampled rows against the oracle's own encode. Then
+    # those rows take the oracle's codes, so the decodes below run on exactly the
+    # oracle's inputs there: a code the two round to opposite sides of a decision
+    # boundary (allowed above) moves that token's score by up to s/sqrt(D).
+    orc = {}
+    for (b, h) in rows:
+        k_st = workloads.kv_rows_all_loops(w, b, h, workloads.TENSOR_K)
+        v_st = workloads.kv_rows_all_loops(w, b, h, workloads.TENSOR_V)
+        for l, bl in enumerate(bits):  # the residual loops are loops 0 .. L-2, in order
+            okw, oks = oracle.encode(k_st[l], k_st[-1], bl)
+            ovw, ovs = oracle.encode(v_st[l], v_st[-1], bl)
+            compare_codes(to_host_words(kc[l][b, h]), to_host_u16(ks[l][b, h]), okw, oks, k_st[l], k_st[-1], bl)
+            compare_codes(to_host_words(vc[l][b, h]), to_host_u16(vs[l][b, h]), ovw, ovs, v_st[l], v_st[-1], bl)
+            kc[l][b, h] = words_to_dev(okw)
+            ks[l][b, h] = to_dev(oks, torch.float16)
+            vc[l][b, h] = words_to_dev(ovw)
+            vs[l][b, h] = to_dev(ovs, torch.float16)
+            orc[(b, h, l)] = (okw, oks, ovw, ovs)
     views = [rq.LoopView(b, kc[i], ks[i], vc[i], vs[i]) for i, b in enumerate(bits)] + [rq.LoopView(0)]
     lens = np.random.default_rng(w.seed).integers(w.seq_len // 2, w.seq_len, size=w.batch).astype(np.int32)
     lens_d = torch.from_numpy(lens).to(DEV)
@@ -335,15 +361,15 @@ def test_serving_step_full_size_sampled_rows():
     torch.cuda.synchronize()
     assert np.array_equal(dense, pag)  # the same cache, dense or paged: identical results
     g = w.group_size
-    for (b, h) in [(0, 0), (7, 3), (15, 7)]:
+    for (b, h) in rows:
         n = int(lens[b])
         k_st = workloads.kv_rows_all_loops(w, b, h, workloads.TENSOR_K)
         v_st = workloads.kv_rows_all_loops(w, b, h, workloads.TENSOR_V)
         for l in range(w.n_loops):
             if w.bits[l]:
-                # the residual loops are loops 0 .. L-2, in order
-                k = oracle.reconstruct(k_st[-1], to_host_words(kc[l][b, h]), to_host_u16(ks[l][b, h]), w.bits[l])
-                v = oracle.reconstruct(v_st[-1], to_host_words(vc[l][b, h]), to_host_u16(vs[l][b, h]), w.bits[l])
+                okw, oks, ovw, ovs = orc[(b, h, l)]
+                k = oracle.reconstruct(k_st[-1], okw, oks, w.bits[l])
+                v = oracle.reconstruct(v_st[-1], ovw, ovs, w.bits[l])
             else:
                 k, v = oracle.bf16_to_f64(k_st[-1]), oracle.bf16_to_f64(v_st[-1])
             k = np.concatenate([k[:n], oracle.bf16_to_f64(k_st[l][:1])])

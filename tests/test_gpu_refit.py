@@ -9,7 +9,7 @@ import torch
 import looped_transformer_kv_rq_amd as rq
 import oracle
 import workloads
-from rq_parity import RECON_TOL, compare_codes_refit, to_dev, to_host_u16, to_host_words
+from rq_parity import RECON_TOL, compare_codes_refit, recon_error, to_dev, to_host_u16, to_host_words
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +61,7 @@ def test_refit_lowers_the_reconstruction_error():
             for k in (0, 2):
                 c, s = rq.encode([xd[l]], xd[-1], [bl], refits=k)
                 xh = rq.reconstruct(xd[-1], c[0], s[0], bl).cpu().numpy().astype(np.float64)
-                e[k] = oracle.reconstruction_error(xh, xs[l], xs[-1])
+                e[k] = recon_error(xh, xs[l], xs[-1])
                 ow, os_ = oracle.encode(xs[l], xs[-1], bl, refits=k)
                 e_orc = oracle.reconstruction_error(oracle.reconstruct(xs[-1], ow, os_, bl), xs[l], xs[-1])
                 assert abs(e[k] - e_orc) <= RECON_TOL

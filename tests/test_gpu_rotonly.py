@@ -8,7 +8,7 @@ import torch
 import looped_transformer_kv_rq_amd as rq
 import oracle
 import workloads
-from rq_parity import compare_codes, to_dev, to_host_u16, to_host_words
+from rq_parity import compare_codes, host_f64, to_dev, to_host_u16, to_host_words
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -57,7 +57,7 @@ def test_rotonly_reconstruct_matches_oracle(d, bits):
     np.testing.assert_allclose(got, expect, rtol=0, atol=2e-6 * max(1.0, np.abs(expect).max()))
     # bf16 output: the RNE rounding of the fp32 value, within one bf16 ulp of the
     # oracle's rounding (values near zero may round across it, so compare values)
-    gotb = oracle.bf16_to_f64(to_host_u16(rq.reconstruct_rotonly(codes, scales, bits, out_dtype=torch.bfloat16)))
+    gotb = host_f64(to_host_u16(rq.reconstruct_rotonly(codes, scales, bits, out_dtype=torch.bfloat16)))
     expb = oracle.bf16_to_f64(oracle.f64_to_bf16(expect))
     tol = 2.0 ** -7 * np.abs(expect) + 2e-6 * max(1.0, np.abs(expect).max())  # one bf16 ulp
     assert np.all(np.abs(gotb - expb) <= tol)

@@ -167,6 +167,12 @@ def test_serving_steps_append_then_decode():
         rq.encode_append([to_dev(x[:, :, :n0]) for x in src[:-1]], to_dev(src[-1][:, :, :n0]), bits, zero, refc,
                          codes, scales)
     views = [rq.LoopView(b, kc[i], ks[i], vc[i], vs[i]) for i, b in enumerate(bits)] + [rq.LoopView(0)]
+    # the oracle's cache: its own encode of every loop's whole history (each step
+    # attends over the prefix of it that the GPU cache holds by then)
+    khat = [oracle.reconstruct(kl[-1], *oracle.encode(kl[i], kl[-1], bl), bl) for i, bl in enumerate(bits)]
+    vhat = [oracle.reconstruct(vl[-1], *oracle.encode(vl[i], vl[-1], bl), bl) for i, bl in enumerate(bits)]
+    khat.append(oracle.bf16_to_f64(kl[-1]))
+    vhat.append(oracle.bf16_to_f64(vl[-1]))
     lens_now = lens.copy()
     for step in range(3):
         q = _bf16(rng, (L, B, hq, d))
@@ -174,14 +180,6 @@ def test_serving_steps_append_then_decode():
         tail_v = [np.stack([vl[l][b, :, lens_now[b]:lens_now[b] + 1] for b in range(B)]) for l in range(L)]
         out = rq.decode_attn_varlen(to_dev(q), kref_c, vref_c, views, seq_lens=torch.from_numpy(lens_now).to(DEV),
                                     tail_k=[to_dev(x) for x in tail_k], tail_v=[to_dev(x) for x in tail_v])
-        # oracle: the same cache contents (codes read back from the device) over the same positions
-        khat, vhat = [], []
-        kr_h, vr_h = to_host_u16(kref_c), to_host_u16(vref_c)
-        for i, bl in enumerate(bits):
-            khat.append(oracle.reconstruct(kr_h, to_host_words(kc[i]), to_host_u16(ks[i]), bl))
-            vhat.append(oracle.reconstruct(vr_h, to_host_words(vc[i]), to_host_u16(vs[i]), bl))
-        khat.append(oracle.bf16_to_f64(kr_h))
-        vhat.append(oracle.bf16_to_f64(vr_h))
         expect = oracle.decode_attn_varlen(q, khat, vhat, lens_now, tail_k, tail_v)
         assert_attn_close(out.cpu().numpy(), expect)
         # the step's position is now complete: encode it into the cache

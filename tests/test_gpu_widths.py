@@ -121,6 +121,7 @@ def test_layer_table_full_size_sampled_rows():
     q_bits = workloads.q_tensor(w)
     qd = to_dev(q_bits)
     enc = {}
+    oenc = {}  # the oracle's own codes of the sampled rows
     for tensor in (workloads.TENSOR_K, workloads.TENSOR_V):
         xs = workloads.kv_tensors(w, tensor)
         xd = [to_dev(x) for x in xs]
@@ -132,8 +133,14 @@ def test_layer_table_full_size_sampled_rows():
             for l, row in enumerate(table):
                 for i, bl in enumerate(row[:-1]):
                     ow, os_ = oracle.encode(st[i], st[-1], bl)
+                    oenc[(tensor, l, i, b, h)] = (ow, os_)
                     compare_codes(to_host_words(codes[l][i][b, h]), to_host_u16(scales[l][i][b, h]), ow, os_,
                                   st[i], st[-1], bl)
+                    # the decode below runs on the oracle's codes for this row: a code
+                    # rounded to the other side of a decision boundary (allowed above)
+                    # would move that token's score
+                    codes[l][i][b, h] = words_to_dev(ow)
+                    scales[l][i][b, h] = to_dev(os_, torch.float16)
         enc[tensor] = (xd[-1], codes, scales)
         del xd
     kref, kc, ksc = enc[workloads.TENSOR_K]
@@ -148,8 +155,8 @@ def test_layer_table_full_size_sampled_rows():
             scale = 1.0 / np.sqrt(w.head_dim)
             for i, bl in enumerate(row):
                 if bl:
-                    k = oracle.reconstruct(k_st[-1], to_host_words(kc[l][i][b, h]), to_host_u16(ksc[l][i][b, h]), bl)
-                    v = oracle.reconstruct(v_st[-1], to_host_words(vc[l][i][b, h]), to_host_u16(vsc[l][i][b, h]), bl)
+                    k = oracle.reconstruct(k_st[-1], *oenc[(workloads.TENSOR_K, l, i, b, h)], bl)
+                    v = oracle.reconstruct(v_st[-1], *oenc[(workloads.TENSOR_V, l, i, b, h)], bl)
                 else:
                     k, v = oracle.bf16_to_f64(k_st[-1]), oracle.bf16_to_f64(v_st[-1])
                 q = oracle.bf16_to_f64(q_bits[i, b, h * g:(h + 1) * g])
