@@ -21,6 +21,7 @@ from .rq_oracle import (  # noqa: F401
     level_offset,
     ls_scale,
     pack_codes,
+    pages_present,
     quantize_groups,
     reconstruct,
     reconstruction_error,

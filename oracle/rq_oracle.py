@@ -298,7 +298,7 @@ def decode_attn(q_bits, k_hat: list, v_hat: list, scale: float | None = None) ->
 
 
 def decode_attn_varlen(q_bits, k_hat: list, v_hat: list, seq_lens, tail_k_bits=None, tail_v_bits=None,
-                       scale: float | None = None) -> np.ndarray:
+                       scale: float | None = None, present=None) -> np.ndarray:
     """Decode attention over a partly filled cache plus bf16 positions not
     yet encoded (the serving step around the hot path; paperaft JSON page,
     `summary`).
@@ -306,8 +306,12 @@ def decode_attn_varlen(q_bits, k_hat: list, v_hat: list, seq_lens, tail_k_bits=N
     q_bits: bf16 [n_loops, B, Hq, D]; k_hat, v_hat: per loop float64
     [B, Hkv, S_cap, D]; seq_lens: [B], the positions of sequence b are
     0 .. seq_lens[b]-1; tail_k_bits, tail_v_bits: per loop bf16 [B, Hkv, T, D]
-    or None. Row (l, b, h) attends to its sequence's cached positions followed
-    by its tail. A row with no position at all is zero.
+    or None. present: bool [B, S_cap] or None (every position is there); a
+    position with present[b, t] false is not part of sequence b's cache and
+    takes no part in the softmax (a paged cache's missing block, see
+    pages_present). Row (l, b, h) attends to its sequence's cached positions
+    that are present, followed by its tail. A row with no position at all is
+    zero.
     """
     q = bf16_to_f64(q_bits)
     n_loops, batch, hq, d = q.shape
@@ -319,9 +323,10 @@ def decode_attn_varlen(q_bits, k_hat: list, v_hat: list, seq_lens, tail_k_bits=N
     for l in range(n_loops):
         for b in range(batch):
             n = int(seq_lens[b])
+            keep = np.arange(n) if present is None else np.flatnonzero(np.asarray(present[b])[:n])
             for kv in range(hkv):
-                k = k_hat[l][b, kv, :n]
-                v = v_hat[l][b, kv, :n]
+                k = k_hat[l][b, kv, keep]
+                v = v_hat[l][b, kv, keep]
                 if tail_k_bits is not None:
                     k = np.concatenate([k, bf16_to_f64(tail_k_bits[l][b, kv])], axis=0)
                     v = np.concatenate([v, bf16_to_f64(tail_v_bits[l][b, kv])], axis=0)
@@ -354,3 +359,16 @@ def gather_pages(pages, block_table, block_size: int, seq_len: int) -> np.ndarra
             if 0 <= blk < n_blocks:
                 out[b, :, t] = pages[blk, :, t % block_size]
     return out
+
+
+def pages_present(block_table, block_size: int, n_blocks: int, seq_len: int) -> np.ndarray:
+    """Which positions a block table maps to a block: bool [B, seq_len],
+    true where the entry of position t of sequence b, block_table[b, t // P],
+    lies in [0, n_blocks). Reading of a table entry that is not a block: the
+    positions it covers are not part of the sequence's cache, so decode
+    attention leaves them out of the softmax (decode_attn_varlen's `present`)
+    rather than attending to a filler value."""
+    table = np.asarray(block_table)
+    t = np.arange(seq_len)
+    blk = table[:, t // block_size]
+    return (blk >= 0) & (blk < n_blocks)

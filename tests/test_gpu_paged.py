@@ -130,6 +130,71 @@ def test_paged_decode_matches_oracle(d, P, bits_per_loop, tail, hq):
         assert_attn_close(out, expect)
 
 
+@pytest.mark.parametrize("d,P,bits_per_loop,tail,hq", [
+    (128, 64, (2, 4, 0), 0, 8), (128, 128, (4, 2, 2, 0), 1, 8), (64, 64, (8, 3, 0), 1, 8),
+    (128, 64, (2, 4, 2, 2, 2, 2, 2, 0), 0, 8)])
+def test_paged_decode_missing_block_inside_prefix(d, P, bits_per_loop, tail, hq):
+    """Table entries that are not blocks (-1, and one past n_blocks) inside
+    [0, seq_lens[b]): their positions take no weight, as the oracle's
+    pages_present reading says; sequence 2's every block is missing."""
+    print(f"paged holes d={d} P={P} bits={bits_per_loop} tail={tail} hq={hq}", flush=True)
+    rng = np.random.default_rng(7 * d + P + tail)
+    L, B, H, max_blocks = len(bits_per_loop), 4, 2, 4
+    S = max_blocks * P
+    lens = np.array([S, 3 * P - 5, 2 * P, P + 40], dtype=np.int32)
+    kref, vref, res = _dense_cache(rng, B, H, S, d, bits_per_loop)
+    table, n_blocks = _table(rng, B, max_blocks, np.full(B, S), P, spare=1)
+    table[0, 1] = -1
+    table[1, 0] = -1
+    table[1, 2] = n_blocks + 3  # not a block either
+    table[2, :] = -1
+    table[3, 1] = -1  # the block holding the last, partial tile
+    present = oracle.pages_present(table, P, n_blocks, S)
+    assert not present[0, P] and present[0, 2 * P] and not present[1, 0] and not present[3, P]
+    views = []
+    for l, bl in enumerate(bits_per_loop):
+        if bl:
+            (kw, ks), (vw, vs) = res[l]
+            pk = [_scatter_present(kw, table, lens, P, n_blocks, 0xFFFFFFFF),
+                  _scatter_present(ks, table, lens, P, n_blocks, F16_INF)]
+            pv = [_scatter_present(vw, table, lens, P, n_blocks, 0xFFFFFFFF),
+                  _scatter_present(vs, table, lens, P, n_blocks, F16_INF)]
+            views.append(rq.LoopView(bl, words_to_dev(pk[0]), to_dev(pk[1], torch.float16), words_to_dev(pv[0]),
+                                     to_dev(pv[1], torch.float16)))
+        else:
+            views.append(rq.LoopView(0))
+    kp = _scatter_present(kref, table, lens, P, n_blocks, BF16_NAN)
+    vp = _scatter_present(vref, table, lens, P, n_blocks, BF16_NAN)
+    q = _bf16(rng, (L, B, hq, d))
+    tk = tv = None
+    if tail:
+        tk = [_bf16(rng, (B, H, tail, d)) for _ in range(L)]
+        tv = [_bf16(rng, (B, H, tail, d)) for _ in range(L)]
+    out = rq.decode_attn_paged(to_dev(q), to_dev(kp), to_dev(vp), views, torch.from_numpy(table).to(DEV),
+                               seq_lens=torch.from_numpy(lens).to(DEV),
+                               tail_k=None if tk is None else [to_dev(x) for x in tk],
+                               tail_v=None if tv is None else [to_dev(x) for x in tv]).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    kh, vh = _hat(kref, vref, res, bits_per_loop)
+    expect = oracle.decode_attn_varlen(q, kh, vh, lens, tk, tv, present=present)
+    if not tail:
+        assert np.all(out[:, 2] == 0)  # sequence 2 has no position at all
+    assert_attn_close(out, expect)
+
+
+def _scatter_present(dense, table, lens, P, n_blocks, fill):
+    """Paged copy of dense [B, H, S, row] for positions below lens[b] whose
+    table entry is a block; everything else is `fill`."""
+    B, H, S = dense.shape[:3]
+    pages = np.full((n_blocks, H, P) + dense.shape[3:], fill, dtype=dense.dtype)
+    for b in range(B):
+        for t in range(int(lens[b])):
+            blk = int(table[b, t // P])
+            if 0 <= blk < n_blocks:
+                pages[blk, :, t % P] = dense[b, :, t]
+    return pages
+
+
 @pytest.mark.parametrize("bits_per_loop,hq", [((2, 2, 0), 8), ((4, 2, 2, 2, 2, 2, 2, 0), 8)])
 def test_paged_equals_contiguous_varlen(bits_per_loop, hq):
     """The same cache, dense or scattered into shuffled blocks: identical results

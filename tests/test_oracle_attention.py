@@ -142,3 +142,55 @@ def test_gather_pages_inverts_a_scatter():
         for j in range(S // P):
             pages[table[b, j]] = dense[b, :, j * P:(j + 1) * P]
     np.testing.assert_array_equal(oracle.gather_pages(pages, table, P, S), dense)
+
+
+def test_missing_block_takes_no_weight_worked_example():
+    """A table entry that is not a block removes its positions from the
+    softmax. Blocks of one position, D = 2, scale 1: q = (1, 0); keys
+    (0, 0), (ln 3, 0) and (100, 0); values (1, 0), (0, 1) and (5, 5). The third
+    position's block is missing (-1), so the weights are 1 : 3 and the output
+    is (1/4, 3/4). Attending to a zero-filled third position would give
+    weights 1 : 3 : 1 and (1/5, 3/5) instead."""
+    table = np.array([[0, 1, -1]])
+    present = oracle.pages_present(table, 1, 2, 3)
+    np.testing.assert_array_equal(present, [[True, True, False]])
+    k = [np.array([[[[0.0, 0.0], [math.log(3.0), 0.0], [100.0, 0.0]]]])]
+    v = [np.array([[[[1.0, 0.0], [0.0, 1.0], [5.0, 5.0]]]])]
+    q = np.array([[[[0x3F80, 0x0000]]]], dtype=np.uint16)  # bf16 (1, 0)
+    out = oracle.decode_attn_varlen(q, k, v, np.array([3]), scale=1.0, present=present)
+    np.testing.assert_allclose(out[0, 0, 0], [0.25, 0.75], rtol=1e-14)
+    # the zero-filled cache gather_pages builds is not what the decode attends to
+    pages = np.stack([k[0][0, :, 0], k[0][0, :, 1]])  # [2 blocks, Hkv = 1, D] -> one position per block
+    kz = [oracle.gather_pages(pages[:, :, None, :], table, 1, 3)]
+    vz = [oracle.gather_pages(np.stack([v[0][0, :, 0], v[0][0, :, 1]])[:, :, None, :], table, 1, 3)]
+    zero_filled = oracle.decode_attn_varlen(q, kz, vz, np.array([3]), scale=1.0)
+    np.testing.assert_allclose(zero_filled[0, 0, 0], [0.2, 0.6], rtol=1e-14)
+
+
+def test_missing_blocks_equal_a_compacted_cache():
+    """Leaving positions out equals attending over the cache with them deleted;
+    a sequence whose every position is missing and has no tail is zero; with
+    a tail it is the tail alone."""
+    rng = np.random.default_rng(23)
+    L, B, Hkv, Hq, S, D, P = 2, 3, 2, 4, 12, 8, 2
+    q = _bf16(rng, (L, B, Hq, D))
+    kh = [oracle.bf16_to_f64(_bf16(rng, (B, Hkv, S, D))) for _ in range(L)]
+    vh = [oracle.bf16_to_f64(_bf16(rng, (B, Hkv, S, D))) for _ in range(L)]
+    table = np.array([[0, -1, 2, 3, 7, 5], [-1, -1, -1, -1, -1, -1], [4, 6, 99, 1, 8, 9]])
+    present = oracle.pages_present(table, P, 10, S)
+    lens = np.array([11, 12, 9])
+    got = oracle.decode_attn_varlen(q, kh, vh, lens, present=present)
+    for b in range(B):
+        keep = [t for t in range(lens[b]) if present[b, t]]
+        kc = [x[b:b + 1, :, keep] for x in kh]
+        vc = [x[b:b + 1, :, keep] for x in vh]
+        want = oracle.decode_attn_varlen(q[:, b:b + 1], kc, vc, np.array([len(keep)]))
+        np.testing.assert_allclose(got[:, b:b + 1], want, rtol=1e-12, atol=1e-14)
+    assert np.all(got[:, 1] == 0)
+    tk = [_bf16(rng, (B, Hkv, 1, D)) for _ in range(L)]
+    tv = [_bf16(rng, (B, Hkv, 1, D)) for _ in range(L)]
+    with_tail = oracle.decode_attn_varlen(q, kh, vh, lens, tk, tv, present=present)
+    for l in range(L):
+        for h in range(Hq):
+            np.testing.assert_allclose(with_tail[l, 1, h], oracle.bf16_to_f64(tv[l][1, h // (Hq // Hkv), 0]),
+                                       rtol=1e-15)
