@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -46,6 +47,21 @@ def _run(cmd):
     return out
 
 
+def scratch_users(log: str) -> list:
+    """(kernel, bytes per lane) of every kernel whose resource-usage remark in
+    a compile log reports private (scratch) memory, i.e. register spills."""
+    out, name = [], None
+    for line in log.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
@@ -54,10 +70,18 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(pair):
         src, obj = pair
-        return _run([cc, *CXXFLAGS, "-c", src, "-o", obj])
+        return _run([cc, *CXXFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj])
 
     with ThreadPoolExecutor(max(1, min(8, len(sources)))) as ex:
         logs = list(ex.map(compile_one, zip(sources, objs)))
+    # No kernel may spill registers to scratch: builds of the 128-coordinate
+    # INT3 / INT8 decode kernel whose register allocation spilled gave wrong
+    # attention rows on MI355X (every spill-free build of the same source was
+    # correct), so a spill fails the build instead of shipping.
+    spills = [u for log in logs for u in scratch_users(log)]
+    if spills:
+        raise RuntimeError("kernels spill registers to scratch: " + ", ".join(f"{k} ({n} B/lane)" for k, n in spills))
+    logs = ["\n".join(x for x in log.splitlines() if "remark:" not in x) for log in logs]
     tmp = LIB + ".tmp"
     logs.append(_run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
                       "-Wl,-rpath,/opt/rocm/lib"]))

@@ -558,7 +558,8 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
     }
     const int with = decode_launch_lds_bytes(ln.sets, ln.n_sets, shape->head_dim, true, true);
     const int without = decode_launch_lds_bytes(ln.sets, ln.n_sets, shape->head_dim, true, false);
-    if (rows > 16 || with > kMaxBlockLds || kMaxBlockLds / with < kMaxBlockLds / without) rotate = false;
+    if (ln.n_sets == 2 || rows > 16 || with > kMaxBlockLds || kMaxBlockLds / with < kMaxBlockLds / without)
+      rotate = false;
   }
   if (any_residual && !rotate) {
     QueryPrepArgs qa{};

@@ -27,7 +27,8 @@
 //    q . (c - o) = 2^b (q . val) - (2^b + o) sum(q);
 //  * reference PV, O_ref^T += V^T P^T (bf16). P is split into bf16 hi + lo
 //    halves (error ~2^-16), and V^T is read from the LDS tile;
-//  * residual PV, O_res^T += lev^T (P s)^T (fp16). Levels decode exactly
+//  * residual PV, O_res^T += lev^T (P s)^T (fp16; each weight P s is the
+//    fp32 P times the fp16 scale, rounded once to nearest). Levels decode exactly
 //    through a v_perm byte table (INT2: {-1.5,-0.5,0.5,1.5}; INT4 as
 //    4 lev_hi + lev_lo; INT3 from an eight-entry table). INT8 levels are
 //    formed as 2 lev = (1024 + 2c) - 1279 in fp16 against P s / 2. Rows of
@@ -76,11 +77,20 @@ __device__ __forceinline__ f32x4_t mma_f16(uint4 a, uint4 b, f32x4_t c) {
 __device__ __forceinline__ uint32_t vperm(uint32_t s0, uint32_t s1, uint32_t sel) {
   return __builtin_amdgcn_perm(s0, s1, sel);
 }
-__device__ __forceinline__ uint32_t pack_rtz(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-}
-__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) * __builtin_bit_cast(f16x2_t, b));
+// fp16 pair {p0 * s0, p1 * s1} from fp32 weights p and fp16 scales taken from
+// half `hi` of the words w0 and w1, each product rounded once to nearest even
+// (v_fma_mixlo_f16 / v_fma_mixhi_f16 with a zero addend). Unbiased: the
+// residual PV's weights then carry no systematic error.
+__device__ __forceinline__ uint32_t mix_pair(float p0, uint32_t w0, float p1, uint32_t w1, bool hi) {
+  uint32_t r;
+  if (hi) {
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(p0), "v"(w0));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(p1), "v"(w1));
+  } else {
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(p0), "v"(w0));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(r) : "v"(p1), "v"(w1));
+  }
+  return r;
 }
 // 2^x by v_exp_f32 alone (no denormal-range fix-up): softmax weights below
 // 2^-126 of the running maximum count as zero. 2^-inf = 0.
@@ -100,6 +110,9 @@ constexpr int kStreamPolicy = 2;  // nt
 __device__ __forceinline__ void dma16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, kStreamPolicy);
 }
+__device__ __forceinline__ void dma16_keep(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+}
 __device__ __forceinline__ void dma4(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 4, 0, 0);
 }
@@ -112,6 +125,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, uint
 }
 __device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voff, soff, 0, kStreamPolicy);
+}
+__device__ __forceinline__ void bdma16_keep(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voff, soff, 0, 0);
 }
 __device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 4, voff, soff, 0, 0);
@@ -156,7 +172,9 @@ struct MfmaGeom {
   static __device__ __forceinline__ int vt_offset(int tok) {
     return (tok / VT_TOK) * VT_STRIDE + (tok % VT_TOK) * 2 * D;
   }
-  static constexpr int PREP_BYTES = (2 * D + 4 * NG + 15) / 16 * 16;  // rotated query record
+  // rotated query record: fp16 hi parts in operand order, then the fp16 lo
+  // parts, then the per-group offsets
+  static constexpr int PREP_BYTES = (4 * D + 4 * NG + 15) / 16 * 16;
 };
 
 // LDS bytes of one residual loop's tile data: K code words [token][W],
@@ -166,15 +184,16 @@ __host__ __device__ constexpr int loop_lds_bytes(int d, int bits) {
 }
 
 // LDS offset of residual slot li's tile data inside a wave's buffer: the V
-// tile, then the slots in the launcher's order INT8, INT4, INT3, INT2.
+// tile, then the slots in the launcher's order INT8, INT4, INT3, INT2 (after
+// the other set's slots in a paired launch, lds_res_base).
 template <int D, bool WIDE>
 __device__ __forceinline__ int slot_lds_offset(const DecodeArgs& a, int li) {
   constexpr int L4 = loop_lds_bytes(D, 4), L2 = loop_lds_bytes(D, 2);
   if constexpr (!WIDE) {
-    return MfmaGeom<D>::VT_BYTES + (li < a.n4 ? li * L4 : a.n4 * L4 + (li - a.n4) * L2);
+    return MfmaGeom<D>::VT_BYTES + a.lds_res_base + (li < a.n4 ? li * L4 : a.n4 * L4 + (li - a.n4) * L2);
   } else {
     constexpr int L8 = loop_lds_bytes(D, 8), L3 = loop_lds_bytes(D, 3);
-    int off = MfmaGeom<D>::VT_BYTES;
+    int off = MfmaGeom<D>::VT_BYTES + a.lds_res_base;
     int k = min(li, a.n8);
     off += k * L8;
     li -= k;
@@ -200,16 +219,44 @@ __host__ __device__ constexpr int rs_coord(int ks, int g, int e) {
   return 32 * ks + 16 * (g >> 1) + 4 * (g & 1) + (e >> 1) + 8 * (e & 1);
 }
 
-// fp16 of x / sqrt(D), rounded twice as written (the fp32 product, then fp16).
-// The code generator fuses a product and its fp16 conversion into one
-// mixed-precision fma (a single rounding) at some sites and not at others, so
-// two kernels computing the same operand could disagree by one fp16 ulp. The
-// empty asm statement hands the conversion a finished fp32 value.
+// y = fp32(x / sqrt(D)) as an fp16 pair hi + lo: hi = fp16(y), lo = fp16(y - hi)
+// (y - hi is exact in fp32), so hi + lo carries y to about 2^-23 relative. The
+// residual scores run two fp16 products, one per part: one fp16 operand alone
+// (2^-12 relative) moved heavy-tailed rows with residuals as large as the
+// reference past 2e-3 in a CPU emulation of the kernel's roundings.
+// The product is rounded to fp32 as written: the code generator fuses a
+// product and its fp16 conversion into one mixed-precision fma (a single
+// rounding) at some sites and not at others, and two kernels computing the
+// same operand could then disagree by one fp16 ulp. The empty asm statement
+// hands the conversions a finished fp32 value.
 template <int D>
-__device__ __forceinline__ _Float16 scaled_f16(float x) {
+__device__ __forceinline__ void scaled_f16_pair(float x, _Float16& hi, _Float16& lo) {
   float y = x * RsqrtD<D>::v;
   asm volatile("" : "+v"(y));
-  return (_Float16)y;
+  hi = (_Float16)y;
+  lo = (_Float16)(y - (float)hi);
+}
+
+// One 8-coordinate operand chunk of the rotated query (x[p][i]: coordinate
+// base + i + 8p) as fp16 hi and lo words in MFMA operand order; returns the
+// chunk's sum of hi + lo. The prep kernel and the partial kernel's own
+// rotation share this, so both give identical operands and offsets.
+template <int D>
+__device__ __forceinline__ float rotated_chunk(const float (&x)[2][4], uint4& hi, uint4& lo) {
+  uint32_t wh[4], wl[4];
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    _Float16 h0, l0, h1, l1;
+    scaled_f16_pair<D>(x[0][i], h0, l0);
+    scaled_f16_pair<D>(x[1][i], h1, l1);
+    wh[i] = __builtin_bit_cast(uint32_t, f16x2_t{h0, h1});
+    wl[i] = __builtin_bit_cast(uint32_t, f16x2_t{l0, l1});
+    sum += ((float)h0 + (float)l0) + ((float)h1 + (float)l1);
+  }
+  hi = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+  lo = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+  return sum;
 }
 
 // Four lanes per query row (loop, b, hq), sixteen rows per wave. Lane g of a
@@ -217,9 +264,10 @@ __device__ __forceinline__ _Float16 scaled_f16(float x) {
 // rs_coord(ks, g, 2i + p) = base + i + 8p (base = 32 ks + 16 (g >> 1) + 4 (g & 1))
 // as x[ks][p][i]. The normalised Walsh-Hadamard transform runs over coordinate
 // bits 0, 1, 3 and the k-step bits in registers and over bits 2 and 4 (lane
-// bits 0 and 1) by DPP quad permutes. The record holds the fp16 rotated values
-// in operand order (16 bytes per (ks, g)) and
-// qoff[ks] = -(2^b + 2^(b-1) - 1/2) * (sum of the group's fp16 values).
+// bits 0 and 1) by DPP quad permutes. The record holds the fp16 hi parts of
+// the rotated values in operand order (16 bytes per (ks, g)), the fp16 lo
+// parts in the same order, and
+// qoff[ks] = -(2^b + 2^(b-1) - 1/2) * (sum of the group's hi + lo values).
 template <int D>
 __global__ __launch_bounds__(64) void rq_query_prep(QueryPrepArgs a) {
   constexpr int NG = D / 32;
@@ -295,25 +343,64 @@ __global__ __launch_bounds__(64) void rq_query_prep(QueryPrepArgs a) {
   float qo = 0.0f;
 #pragma unroll
   for (int ks = 0; ks < NG; ++ks) {
-    uint32_t w[4];
-    float sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const _Float16 h0 = scaled_f16<D>(x[ks][0][i]), h1 = scaled_f16<D>(x[ks][1][i]);
-      w[i] = __builtin_bit_cast(uint32_t, f16x2_t{h0, h1});
-      sum += (float)h0 + (float)h1;
-    }
+    uint4 hi, lo;
+    float sum = rotated_chunk<D>(x[ks], hi, lo);
     sum += quad_xor<1>(sum);
     sum += quad_xor<2>(sum);
     if (ks % 4 == g) qo = -off * sum;
-    if (active) *reinterpret_cast<uint4*>(rec + 16 * (4 * ks + g)) = make_uint4(w[0], w[1], w[2], w[3]);
+    if (active) {
+      *reinterpret_cast<uint4*>(rec + 16 * (4 * ks + g)) = hi;
+      *reinterpret_cast<uint4*>(rec + 2 * D + 16 * (4 * ks + g)) = lo;
+    }
   }
-  if (active && g < NG) reinterpret_cast<float*>(rec + 2 * D)[g] = qo;
+  if (active && g < NG) reinterpret_cast<float*>(rec + 4 * D)[g] = qo;
 }
 
 // ---------------------------------------------------------------------------
 // partial kernel
 // ---------------------------------------------------------------------------
+
+// The lo parts of the rotated query (the B operands of the second residual
+// score product), by where they live:
+//  * kLoRegs: in registers (one 16-row block without INT3 / INT8 loops);
+//  * kLoPads: INT3 / INT8 at one 16-row block. Those kernels are at their
+//    register limit, so the block copies the lo parts from the prepared
+//    records into the unused 128-byte pads that follow each 1 KB instruction
+//    of the V tile (row r of the 16 in wave r / 4's pads, D / 64 pads a row);
+//  * kLoRecord: 32-row blocks, and INT3 / INT8 in paired launches, read them
+//    from the record at each use (at most 32 rows' records per block, so
+//    these reads hit in the caches).
+enum LoPlace { kLoRegs, kLoPads, kLoRecord };
+template <int NB, bool WIDE, int SETS>
+constexpr LoPlace kLoPlace = NB == 2 || (WIDE && SETS == 2) ? kLoRecord : (WIDE ? kLoPads : kLoRegs);
+
+template <int D, int NB, LoPlace P>
+struct QueryLo;
+template <int D, int NB>
+struct QueryLo<D, NB, kLoRegs> {
+  uint4 v[NB][D / 32];
+  __device__ __forceinline__ uint4 get(int nb, int ks, int) const { return v[nb][ks]; }
+};
+template <int D, int NB>
+struct QueryLo<D, NB, kLoPads> {
+  const unsigned char* row;  // this lane's row: its first pad
+  // byte o of the row's 2D bytes sits in pad o / 128 at offset o % 128
+  __device__ __forceinline__ uint4 get(int, int ks, int g) const {
+    const int o = 16 * (4 * ks + g);
+    return *reinterpret_cast<const uint4*>(row + (o >> 7) * MfmaGeom<D>::VT_STRIDE + (o & 127));
+  }
+  // LDS address of byte 0 of row r's lo parts (the pads of wave r / 4)
+  static __device__ __forceinline__ unsigned char* row_of(unsigned char* smem, int wave_bytes, int r) {
+    return smem + (r >> 2) * wave_bytes + (r & 3) * (D / 64) * MfmaGeom<D>::VT_STRIDE + 1024;
+  }
+};
+template <int D, int NB>
+struct QueryLo<D, NB, kLoRecord> {
+  const unsigned char* rec[NB];  // the row's lo parts: 16 bytes per operand chunk (ks, g)
+  __device__ __forceinline__ uint4 get(int nb, int ks, int g) const {
+    return *reinterpret_cast<const uint4*>(rec[nb] + 16 * (4 * ks + g));
+  }
+};
 
 // Issue the DMA of one residual loop's tile data (codes and scales of K and V).
 template <int D, int BITS, bool FULL>
@@ -398,19 +485,27 @@ struct Consts {
 template <bool WIDE>
 __device__ __forceinline__ Consts make_consts() {
   Consts c{0x03000300u, 0x03C003C0u, 0x3C003C00u, 0x000C000Cu, 0x01800180u, 0x02000200u, 0x04000400u};
-  asm volatile("" : "+v"(c.m2), "+v"(c.m4), "+v"(c.one), "+v"(c.sel0));
-  if constexpr (WIDE) asm volatile("" : "+v"(c.m3lo), "+v"(c.m3hi), "+v"(c.m3s));
+  if constexpr (!WIDE) {
+    asm volatile("" : "+v"(c.m2), "+v"(c.m4), "+v"(c.one), "+v"(c.sel0));
+  } else {
+    // the masks in scalar registers (one per v_and_or_b32 fits the constant
+    // bus), the or-operands in vector registers: the INT3 / INT8 kernels are
+    // at their register limit
+    asm volatile("" : "+s"(c.m2), "+s"(c.m4), "+v"(c.one), "+v"(c.sel0));
+    asm volatile("" : "+s"(c.m3lo), "+s"(c.m3hi), "+s"(c.m3s));
+  }
   return c;
 }
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) { return (x & m) | o; }
 
 // Residual scores of loop li added to this lane's score fragment. Rows of
 // other loops get zero factors (qm = qo = 0), so every lane runs the same code.
-template <int D, int NB, int BITS>
+template <int D, int NB, int BITS, class QL>
 __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, const unsigned char* base,
-                                                const uint4 (&qtB)[NB][D / 32], const float (&qoff)[NB][D / 32],
-                                                const float (&qmul)[NB], const int (&my_loop)[NB],
-                                                f32x4_t (&sc)[2][NB], int m, int g, const Consts& k) {
+                                                const uint4 (&qtB)[NB][D / 32], const QL& qtL,
+                                                const float (&qoff)[NB][D / 32], const float (&qmul)[NB],
+                                                const int (&my_loop)[NB], f32x4_t (&sc)[2][NB], int m, int g,
+                                                const Consts& k) {
   constexpr int NG = D / 32;
   constexpr int W = D * BITS / 32;
   const unsigned char* kc_l = base;
@@ -514,10 +609,13 @@ __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, con
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if (li * G >= 16 * nb + 16 || li * G + G <= 16 * nb) continue;  // no row of loop li here
-      // all group products first, so the MFMAs issue back to back
+      // all group products first, so the MFMAs issue back to back: the hi
+      // parts of the rotated query, then the lo parts into the same sums
       f32x4_t c[NG];
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) c[ks] = mma_f16(kx[ks], qtB[nb][ks], f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) c[ks] = mma_f16(kx[ks], qtL.get(nb, ks, g), c[ks]);
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
 #pragma unroll
@@ -585,17 +683,19 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
     if (li * G >= 16 * nb + 16 || li * G + G <= 16 * nb) continue;
     // INT8 levels enter doubled (2c - 255), so P carries the factor 1/2
     const float mem = my_loop[nb] == li ? (BITS == 8 ? 0.5f : 1.0f) : 0.0f;
-    uint32_t p16[4];
+    float pm[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p16[i] = pack_rtz(p[nb][2 * i] * mem, p[nb][2 * i + 1] * mem);
+    for (int j = 0; j < 8; ++j) pm[j] = p[nb][j] * mem;
 #pragma unroll
     for (int grp = 0; grp < NG; ++grp) {
-      const uint32_t hsel = (grp & 1) ? 0x07060302u : 0x05040100u;
+      // B operand: P s of the lane's eight tokens for this scale group (the
+      // group's scale is half grp & 1 of word grp / 2)
+      const bool hs = (grp & 1) != 0;
       uint4 bop;
-      bop.x = mul_f16x2(p16[0], vperm(vsw[1][grp >> 1], vsw[0][grp >> 1], hsel));
-      bop.y = mul_f16x2(p16[1], vperm(vsw[3][grp >> 1], vsw[2][grp >> 1], hsel));
-      bop.z = mul_f16x2(p16[2], vperm(vsw[5][grp >> 1], vsw[4][grp >> 1], hsel));
-      bop.w = mul_f16x2(p16[3], vperm(vsw[7][grp >> 1], vsw[6][grp >> 1], hsel));
+      bop.x = mix_pair(pm[0], vsw[0][grp >> 1], pm[1], vsw[1][grp >> 1], hs);
+      bop.y = mix_pair(pm[2], vsw[2][grp >> 1], pm[3], vsw[3][grp >> 1], hs);
+      bop.z = mix_pair(pm[4], vsw[4][grp >> 1], pm[5], vsw[5][grp >> 1], hs);
+      bop.w = mix_pair(pm[6], vsw[6][grp >> 1], pm[7], vsw[7][grp >> 1], hs);
       if constexpr (kMant) {
         // the group's weight sum (P s summed over the tile's tokens), in every
         // element of the block: an A operand of fp16 ones
@@ -671,7 +771,8 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
 
 // Issue every load of one tile: the residual loops' codes and scales and the
 // V reference tile by LDS DMA into `buf`, the K reference into registers.
-template <int D, bool RESID, bool WIDE, bool FULL>
+// WITH_K: the K reference into registers; WITH_V: the V tile into LDS.
+template <int D, bool RESID, bool WIDE, bool FULL, bool WITH_K = true, bool WITH_V = true>
 __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* buf, const uint16_t* kbase,
                                            const uint16_t* vbase, int64_t row_base, int t0, int tlast, int lane,
                                            int m, int g, uint4 (&ka)[2][D / 32]) {
@@ -700,29 +801,37 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* b
   if constexpr (FULL) {
     // the tile's 32 vectors are contiguous: 2D bytes each, one 16-byte chunk per lane
     const uint32_t rb = (uint32_t)a.seq_len * 2u * D;
-    const auto v_r = row_rsrc(vbase, rb);
-    const auto k_r = row_rsrc(kbase, rb);
     const uint32_t tb = (uint32_t)t0 * 2u * D;
     const uint32_t lane16 = 16u * (uint32_t)lane;
+    if constexpr (WITH_V) {
+      const auto v_r = row_rsrc(vbase, rb);
 #pragma unroll
-    for (int i = 0; i < Gm::VT_INSTR; ++i) bdma16(v_r, lane16, tb + 1024 * i, buf + i * Gm::VT_STRIDE);
-    const uint32_t koff = 2u * (uint32_t)(m * D + 8 * g);
+      for (int i = 0; i < Gm::VT_INSTR; ++i) bdma16(v_r, lane16, tb + 1024 * i, buf + i * Gm::VT_STRIDE);
+    }
+    if constexpr (WITH_K) {
+      const auto k_r = row_rsrc(kbase, rb);
+      const uint32_t koff = 2u * (uint32_t)(m * D + 8 * g);
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
+      for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-      for (int ks = 0; ks < NG; ++ks) ka[bk][ks] = bload16(k_r, koff, tb + 32 * D * bk + 64 * ks);
+        for (int ks = 0; ks < NG; ++ks) ka[bk][ks] = bload16(k_r, koff, tb + 32 * D * bk + 64 * ks);
+    }
     return;
   }
+  if constexpr (WITH_V) {
 #pragma unroll
-  for (int i = 0; i < Gm::VT_INSTR; ++i) {
-    const int tok = i * Gm::VT_TOK + lane / (D / 8);
-    dma16(vbase + (int64_t)min(t0 + tok, tlast) * D + 8 * (lane % (D / 8)), buf + i * Gm::VT_STRIDE);
+    for (int i = 0; i < Gm::VT_INSTR; ++i) {
+      const int tok = i * Gm::VT_TOK + lane / (D / 8);
+      dma16(vbase + (int64_t)min(t0 + tok, tlast) * D + 8 * (lane % (D / 8)), buf + i * Gm::VT_STRIDE);
+    }
   }
+  if constexpr (WITH_K) {
 #pragma unroll
-  for (int bk = 0; bk < 2; ++bk) {
-    const uint16_t* kp = kbase + (int64_t)min(t0 + 16 * bk + m, tlast) * D + 8 * g;
+    for (int bk = 0; bk < 2; ++bk) {
+      const uint16_t* kp = kbase + (int64_t)min(t0 + 16 * bk + m, tlast) * D + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < NG; ++ks) ka[bk][ks] = *reinterpret_cast<const uint4*>(kp + 32 * ks);
+      for (int ks = 0; ks < NG; ++ks) ka[bk][ks] = *reinterpret_cast<const uint4*>(kp + 32 * ks);
+    }
   }
 }
 
@@ -761,11 +870,74 @@ __device__ __forceinline__ void issue_at(const DecodeArgs& a, unsigned char* buf
   }
 }
 
+// Paired launches: the two waves of a block share each tile's reference. The
+// K tile goes to LDS (ahead of the V tile) in MFMA operand order: the
+// instruction for k-step (bk, ks) has lane l = 16 g + m fetch the 16 bytes
+// of token 16 bk + m at coordinate 32 ks + 8 g, so each wave later reads its
+// A operand at lane * 16 of that instruction's 1 KB (no bank conflicts).
+// Those instructions read half of each 128-byte line, so they keep the default
+// cache policy. Wave 0 issues the K tile and its set's residual loops, wave 1
+// the V tile and its set's.
+template <int D>
+constexpr int kPairKBytes = 2 * (D / 32) * 1024;
+
+template <int D, bool RESID, bool WIDE, bool FULL>
+__device__ __forceinline__ void pair_issue_tile(const DecodeArgs& a, unsigned char* smem, unsigned char* buf,
+                                                const uint16_t* kbase, const uint16_t* vbase, int64_t row_base,
+                                                int t0, int tlast, int lane, int m, int g, int wave) {
+  using Gm = MfmaGeom<D>;
+  constexpr int NG = Gm::NG;
+  uint4 no_k[2][NG];  // issue_tile's K registers, not loaded here
+  if (wave == 1) {
+    // this set's residual loops and the V tile
+    issue_tile<D, RESID, WIDE, FULL, false, true>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, no_k);
+    return;
+  }
+  // wave 0: this set's residual loops, then the K tile in operand order
+  issue_tile<D, RESID, WIDE, FULL, false, false>(a, buf, kbase, vbase, row_base, t0, tlast, lane, m, g, no_k);
+  if constexpr (FULL) {
+    const auto k_r = row_rsrc(kbase, (uint32_t)a.seq_len * 2u * D);
+    const uint32_t voff = (uint32_t)(m * 2 * D + 16 * g);
+    const uint32_t tb = (uint32_t)t0 * 2u * D;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) bdma16_keep(k_r, voff, tb + 32 * D * bk + 64 * ks, smem + (NG * bk + ks) * 1024);
+  } else {
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+      const uint16_t* kp = kbase + (int64_t)min(t0 + 16 * bk + m, tlast) * D + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) dma16_keep(kp + 32 * ks, smem + (NG * bk + ks) * 1024);
+    }
+  }
+}
+
+template <int D, bool RESID, bool WIDE, bool PAGED>
+__device__ __forceinline__ void pair_issue_at(const DecodeArgs& a, unsigned char* smem, unsigned char* buf,
+                                              const uint16_t* kbase, const uint16_t* vbase, int64_t row_base, int b,
+                                              int kvh, int z, int t, int t_end, int lane, int m, int g, int wave) {
+  const bool full = t + kTile <= t_end;
+  const int tlast = t_end - 1;
+  if constexpr (PAGED) {
+    const int blk = a.block_table[(int64_t)b * a.max_blocks + (t >> a.log2_block)];
+    const int64_t tv = (((int64_t)blk * a.n_kv_heads + kvh) << a.log2_block) + (t & ((1 << a.log2_block) - 1));
+    const uint16_t* kt = a.k[z] + tv * D;
+    const uint16_t* vt = a.v[z] + tv * D;
+    if (full) pair_issue_tile<D, RESID, WIDE, true>(a, smem, buf, kt, vt, tv, 0, tlast - t, lane, m, g, wave);
+    else pair_issue_tile<D, RESID, WIDE, false>(a, smem, buf, kt, vt, tv, 0, tlast - t, lane, m, g, wave);
+  } else {
+    if (full) pair_issue_tile<D, RESID, WIDE, true>(a, smem, buf, kbase, vbase, row_base, t, tlast, lane, m, g, wave);
+    else pair_issue_tile<D, RESID, WIDE, false>(a, smem, buf, kbase, vbase, row_base, t, tlast, lane, m, g, wave);
+  }
+}
+
 // Scores, online softmax and PV of one staged tile.
-template <int D, int NB, bool RESID, bool WIDE>
+template <int D, int NB, bool RESID, bool WIDE, class QL>
 __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned char* buf, int t0, int t_end,
                                              int m, int g, const uint4 (&ka)[2][D / 32], const uint4 (&qB)[NB][D / 32],
-                                             const uint4 (&qtB)[NB][D / 32], const float (&qoff)[NB][D / 32],
+                                             const uint4 (&qtB)[NB][D / 32], const QL& qtL,
+                                             const float (&qoff)[NB][D / 32],
                                              const float (&qmul)[NB], const int (&my_loop)[NB],
                                              f32x4_t (&o_ref)[NB][D / 64][4], f32x4_t (&o_res)[NB][kResBlocks<D, NB>],
                                              float (&m_run)[NB], float (&l_run)[NB], const Consts& k) {
@@ -786,18 +958,18 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
     if constexpr (WIDE) {
       const int e8 = a.n8, e4 = e8 + a.n4, e3 = e4 + a.n3, e2 = e3 + a.n2;
       for (int li = 0; li < e8; ++li)
-        residual_scores<D, NB, 8>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 8>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
       for (int li = e8; li < e4; ++li)
-        residual_scores<D, NB, 4>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 4>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
       for (int li = e4; li < e3; ++li)
-        residual_scores<D, NB, 3>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 3>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
       for (int li = e3; li < e2; ++li)
-        residual_scores<D, NB, 2>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 2>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
     } else {
       for (int li = 0; li < a.n4; ++li)
-        residual_scores<D, NB, 4>(a, li, buf + slot_lds_offset<D, false>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 4>(a, li, buf + slot_lds_offset<D, false>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
       for (int li = a.n4; li < a.n4 + a.n2; ++li)
-        residual_scores<D, NB, 2>(a, li, buf + slot_lds_offset<D, false>(a, li), qtB, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 2>(a, li, buf + slot_lds_offset<D, false>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
     }
   }
 
@@ -906,13 +1078,14 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
 // Instantiations that can rotate the queries themselves (DecodeArgs::qprep
 // NULL): one 16-row block of a residual launch over a dense cache with INT2 /
 // INT4 loops.
-template <int NB, bool RESID, bool WIDE, bool PAGED>
-constexpr bool kRotatesQueries = NB == 1 && RESID && !WIDE && !PAGED;
+template <int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
+constexpr bool kRotatesQueries = NB == 1 && RESID && !WIDE && !PAGED && SETS == 1;
 
-// SETS: the launch's argument sets (1 or 2). With two, the block of set s for
-// work item w is 16 (w / 8) + 8 s + w % 8, so the two blocks of a work item go
-// to the same XCD under the round-robin dispatch and are dispatched close
-// together.
+// SETS: the launch's argument sets (1 or 2). With one, a block is four
+// waves over one (batch, kv head, split), each taking every fourth tile. With
+// two (paired launches), a block is two waves over one (batch, kv head,
+// split): wave s computes set s's rows, both walk every tile of the split and
+// share its reference K and V through LDS, each issuing half of the loads.
 template <int D, int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RESID && NB == 2 ? 1 : 2,
                                                                      RESID && NB == 1 ? 2 : 4)))
@@ -926,12 +1099,9 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: tile bases stay scalar
   const int m = lane & 15, g = lane >> 4;
-  // Two sets: the twin blocks of one work item are 8 apart, so with the
-  // round-robin dispatch over the 8 XCDs they share an XCD and its L2.
-  const int bx = blockIdx.x;
-  const DecodeArgs& a = launch.set[SETS == 1 ? 0 : (bx >> 3) & 1];
-  const int work = SETS == 1 ? bx : ((bx >> 4) << 3) | (bx & 7);
-  if (SETS == 2 && work >= a.n_splits * a.batch * a.n_kv_heads) return;
+  constexpr bool PAIR = SETS == 2;
+  const DecodeArgs& a = launch.set[PAIR ? wave : 0];
+  const int work = blockIdx.x;
   const int split = work % a.n_splits;
   const int bh = work / a.n_splits;
   const int z = blockIdx.y;
@@ -944,6 +1114,8 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   // q[row 16nb+m][32ks + 8g .. +8]); fp16 rotated query + offsets (prepared).
   uint4 qB[NB][NG];
   uint4 qtB[NB][NG];
+  constexpr LoPlace LP = kLoPlace<NB, WIDE, SETS>;
+  QueryLo<D, NB, LP> qtL;
   float qoff[NB][NG];
   float qmul[NB];
   int my_loop[NB];
@@ -959,7 +1131,13 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
     for (int ks = 0; ks < NG; ++ks) {
       qB[nb][ks] = qrow >= 0 ? *reinterpret_cast<const uint4*>(a.q + qrow * D + 32 * ks + 8 * g) : make_uint4(0, 0, 0, 0);
       qtB[nb][ks] = make_uint4(0, 0, 0, 0);
+      if constexpr (LP == kLoRegs) qtL.v[nb][ks] = make_uint4(0, 0, 0, 0);
       qoff[nb][ks] = 0.0f;
+    }
+    if constexpr (RESID && LP == kLoRecord) {
+      // rows of other loops and padding rows read a real record too: their
+      // residual score factors are zero, so only finiteness matters
+      qtL.rec[nb] = a.qprep + (qrow >= 0 ? qrow : 0) * Gm::PREP_BYTES + 2 * D;
     }
     if constexpr (RESID) {
       if (qrow >= 0 && lb != 0 && a.qprep != nullptr) {
@@ -967,7 +1145,8 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
 #pragma unroll
         for (int ks = 0; ks < NG; ++ks) {
           qtB[nb][ks] = *reinterpret_cast<const uint4*>(rec + 16 * (4 * ks + g));
-          qoff[nb][ks] = reinterpret_cast<const float*>(rec + 2 * D)[ks];
+          if constexpr (LP == kLoRegs) qtL.v[nb][ks] = *reinterpret_cast<const uint4*>(rec + 2 * D + 16 * (4 * ks + g));
+          qoff[nb][ks] = reinterpret_cast<const float*>(rec + 4 * D)[ks];
         }
       }
     }
@@ -977,7 +1156,22 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   // One tile buffer per wave: with two waves per SIMD, one wave's compute
   // covers the other's load latency. Measured on MI355X, a second buffer per
   // wave (prefetching the next tile) costs more occupancy than it hides.
-  unsigned char* buf = smem + wave * a.lds_wave_bytes;
+  // Paired launches: the shared K tile first, then the shared V tile, then
+  // each set's residual slots (lds_res_base)
+  unsigned char* buf = PAIR ? smem + kPairKBytes<D> : smem + wave * a.lds_wave_bytes;
+  if constexpr (RESID && LP == kLoPads) {
+    // each wave copies the lo parts of rows 4 wave .. 4 wave + 3 into its pads
+    constexpr int kChunks = 2 * D / 16;  // 16-byte chunks per row
+    const int r = 4 * wave + lane / kChunks, j = lane % kChunks;
+    if (lane < 4 * kChunks) {
+      const int64_t qr = r < R ? ((int64_t)(a.loop_id[r / G] + z) * a.batch + b) * a.n_q_heads + kvh * G + r % G : 0;
+      const uint4 v = *reinterpret_cast<const uint4*>(a.qprep + qr * Gm::PREP_BYTES + 2 * D + 16 * j);
+      unsigned char* dst = QueryLo<D, NB, kLoPads>::row_of(smem, a.lds_wave_bytes, r);
+      *reinterpret_cast<uint4*>(dst + (16 * j >> 7) * Gm::VT_STRIDE + (16 * j & 127)) = v;
+    }
+    qtL.row = QueryLo<D, NB, kLoPads>::row_of(smem, a.lds_wave_bytes, m);
+    __syncthreads();
+  }
   f32x4_t o_ref[NB][NH][4];
   f32x4_t o_res[NB][kResBlocks<D, NB>];
   float m_run[NB], l_run[NB];
@@ -999,13 +1193,13 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   const int tlast = t_end - 1;
   const uint16_t* kbase = a.k[z] + row_base * D;
   const uint16_t* vbase = a.v[z] + row_base * D;
-  constexpr int kStep = 4 * kTile;  // tokens between a wave's consecutive tiles
+  constexpr int kStep = PAIR ? kTile : 4 * kTile;  // tokens between a wave's consecutive tiles
 
   const Consts kc = make_consts<WIDE>();
   uint4 ka[2][NG];
-  int t0 = t_begin + wave * kTile;
+  int t0 = t_begin + (PAIR ? 0 : wave * kTile);
   // (only where the extra copy of the tile body adds no register spills)
-  if constexpr (kRotatesQueries<NB, RESID, WIDE, PAGED>) {
+  if constexpr (kRotatesQueries<NB, RESID, WIDE, PAGED, SETS>) {
     if (a.qprep == nullptr) {
       // The residual-score operand is computed here rather than read from
       // prepared records: the block's 16 rows go 16 / NG to a wave, 4 NG lanes
@@ -1058,18 +1252,13 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[pp][i] = fmaf(sg, x[pp][i], __shfl_xor(x[pp][i], st));
       }
-      uint32_t w4[4];
-      float sum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const _Float16 h0 = scaled_f16<D>(x[0][i]), h1 = scaled_f16<D>(x[1][i]);
-        w4[i] = __builtin_bit_cast(uint32_t, f16x2_t{h0, h1});
-        sum += (float)h0 + (float)h1;
-      }
+      uint4 w_hi, w_lo;
+      float sum = rotated_chunk<D>(x, w_hi, w_lo);
       sum += quad_xor<1>(sum);  // the group's four chunks (same k-step)
       sum += quad_xor<2>(sum);
+      // the hi parts and the offsets first, then the lo parts in the same slots
       if (rr < 16) {
-        *reinterpret_cast<uint4*>(qreg + rr * QS + 16 * c) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        *reinterpret_cast<uint4*>(qreg + rr * QS + 16 * c) = w_hi;
         if (cg == 0) {
           const float off = lbr > 0 ? (float)(1 << lbr) + (float)(1 << (lbr - 1)) - 0.5f : 0.0f;
           *reinterpret_cast<float*>(qreg + rr * QS + 2 * D + 4 * cks) = -off * sum;
@@ -1081,11 +1270,16 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
         qtB[0][ks] = *reinterpret_cast<const uint4*>(qreg + m * QS + 16 * (4 * ks + g));
         qoff[0][ks] = *reinterpret_cast<const float*>(qreg + m * QS + 2 * D + 4 * ks);
       }
+      __syncthreads();
+      if (rr < 16) *reinterpret_cast<uint4*>(qreg + rr * QS + 16 * c) = w_lo;
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < NG; ++ks) qtL.v[0][ks] = *reinterpret_cast<const uint4*>(qreg + m * QS + 16 * (4 * ks + g));
       wave_sync_lds();
       // the first tile, already staged (its own copy of the tile body, so the
       // K registers are not live across the loop below)
       if (t0 < t_end) {
-        compute_tile<D, NB, RESID, WIDE>(a, buf, t0, t_end, m, g, ka, qB, qtB, qoff, qmul, my_loop, o_ref, o_res, m_run,
+        compute_tile<D, NB, RESID, WIDE>(a, buf, t0, t_end, m, g, ka, qB, qtB, qtL, qoff, qmul, my_loop, o_ref, o_res, m_run,
                                          l_run, kc);
         wait_lds();
         wave_sync_lds();
@@ -1093,15 +1287,35 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
       }
     }
   }
-  for (; t0 < t_end; t0 += kStep) {
-    if (!tile_valid<PAGED>(a, b, t0)) continue;  // no valid page: the tile takes no weight
-    issue_at<D, RESID, WIDE, PAGED>(a, buf, kbase, vbase, row_base, b, kvh, z, t0, t_end, lane, m, g, ka);
-    wait_vmem();
-    wave_sync_lds();
-    compute_tile<D, NB, RESID, WIDE>(a, buf, t0, t_end, m, g, ka, qB, qtB, qoff, qmul, my_loop, o_ref, o_res, m_run, l_run,
-                               kc);
-    wait_lds();
-    wave_sync_lds();  // the buffer is free for the next tile's DMA
+  if constexpr (PAIR) {
+    // both waves walk every tile; each waits for its own loads, then the
+    // barrier makes the other wave's half visible, and a second barrier
+    // keeps the shared buffers until both have read them
+    for (; t0 < t_end; t0 += kStep) {
+      if (!tile_valid<PAGED>(a, b, t0)) continue;  // both waves see the same table entry
+      pair_issue_at<D, RESID, WIDE, PAGED>(a, smem, buf, kbase, vbase, row_base, b, kvh, z, t0, t_end, lane, m, g,
+                                           wave);
+      wait_vmem();
+      __syncthreads();
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int ks = 0; ks < NG; ++ks) ka[bk][ks] = *reinterpret_cast<const uint4*>(smem + (NG * bk + ks) * 1024 + 16 * lane);
+      compute_tile<D, NB, RESID, WIDE>(a, buf, t0, t_end, m, g, ka, qB, qtB, qtL, qoff, qmul, my_loop, o_ref, o_res,
+                                       m_run, l_run, kc);
+      __syncthreads();
+    }
+  } else {
+    for (; t0 < t_end; t0 += kStep) {
+      if (!tile_valid<PAGED>(a, b, t0)) continue;  // no valid page: the tile takes no weight
+      issue_at<D, RESID, WIDE, PAGED>(a, buf, kbase, vbase, row_base, b, kvh, z, t0, t_end, lane, m, g, ka);
+      wait_vmem();
+      wave_sync_lds();
+      compute_tile<D, NB, RESID, WIDE>(a, buf, t0, t_end, m, g, ka, qB, qtB, qtL, qoff, qmul, my_loop, o_ref, o_res,
+                                       m_run, l_run, kc);
+      wait_lds();
+      wave_sync_lds();  // the buffer is free for the next tile's DMA
+    }
   }
 
   // At NB = 1 the INT2 / INT4 rows accumulated sum P s (1 + c/2^b). The level
@@ -1128,7 +1342,8 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   // merges whole rows (rows wave, wave + 4, ...), its lanes across the record:
   // the slots are summed in wave order (reproducible), each scaled by
   // 2^(m_w - max m), and the result is the row's partial record. The merge
-  // needs 4 * NR * (2D + 2) floats of LDS.
+  // needs 4 * NR * (2D + 2) floats of LDS. In a paired launch each wave holds
+  // whole rows of its own set, and copies its slot out as the rows' records.
   constexpr int SREC = RESID ? 2 * D + 2 : D + 2;  // record floats this launch writes
   __syncthreads();
   float* slots = reinterpret_cast<float*>(smem);
@@ -1159,6 +1374,20 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
     }
   }
   __syncthreads();
+  if constexpr (PAIR) {
+    const float* slot = slots + wave * NR * SREC;
+    for (int r = 0; r < R; ++r) {
+      const int loop = a.loop_id[r / G] + z;
+      const int hq = kvh * G + r % G;
+      float* dst = a.ws + ((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.rec_splits + a.split_base + split) * REC;
+#pragma unroll
+      for (int j = 0; j * 64 < SREC; ++j) {
+        const int e = lane + 64 * j;
+        if (e < SREC) dst[e] = slot[r * SREC + e];
+      }
+    }
+    return;
+  }
   for (int r = wave; r < R; r += 4) {
     const float* s0 = slots + r * SREC;
     float mw[4], mm = -INFINITY;
@@ -1192,7 +1421,7 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   // residual loops): then this launch's rows get a zero one.
   if constexpr (!RESID) {
     if (a.zero_residual) {
-      for (int i = threadIdx.x; i < R * D; i += 256) {
+      for (int i = threadIdx.x; i < R * D; i += blockDim.x) {
         const int r = i / D, e = i % D;
         const int loop = a.loop_id[r / G] + z;
         const int hq = kvh * G + r % G;
@@ -1228,7 +1457,18 @@ static int block_lds_bytes(int d, int nb, int wave_bytes, bool residual, bool ro
   return merge > tiles ? merge : tiles;
 }
 
+// LDS bytes of a paired block: the shared K and V tiles, both sets' residual
+// slots, or (if larger) both waves' record slots for the final copy-out
+static int pair_lds_bytes(int d, const DecodeArgs* sets, bool residual) {
+  const int vt = d == 128 ? MfmaGeom<128>::VT_BYTES : MfmaGeom<64>::VT_BYTES;
+  int tiles = (d == 128 ? kPairKBytes<128> : kPairKBytes<64>) + vt;
+  for (int i = 0; i < 2; ++i) tiles += decode_wave_lds_bytes(d, sets[i].bits, residual ? sets[i].n_loops_launch : 0) - vt;
+  const int merge = 2 * 16 * (residual ? 2 * d + 2 : d + 2) * 4;
+  return merge > tiles ? merge : tiles;
+}
+
 int decode_launch_lds_bytes(const DecodeArgs* sets, int n_sets, int head_dim, bool residual, bool rotate) {
+  if (n_sets == 2) return pair_lds_bytes(head_dim, sets, residual);
   int rows = 0, lds = 0;
   for (int i = 0; i < n_sets; ++i) rows = std::max(rows, sets[i].n_rows);
   const int nb = rows > 16 ? 2 : 1;
@@ -1252,7 +1492,8 @@ static void launch_mfma_kernel(const DecodeLaunch& l, dim3 grid, int lds, hipStr
                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxBlockLds);
     lifted.fetch_or(bit, std::memory_order_relaxed);
   }
-  hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED, SETS>), grid, dim3(256), lds, stream, l);
+  hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED, SETS>), grid, dim3(SETS == 2 ? 128 : 256), lds,
+                     stream, l);
 }
 
 template <int D, int NB, bool PAGED, int SETS>
@@ -1260,7 +1501,7 @@ static hipError_t launch_mfma_dp(const DecodeLaunch& l, dim3 grid, int lds, bool
                                  hipStream_t stream) {
   // a residual launch without prepared records must be one that rotates the queries itself
   if (residual && l.set[0].qprep == nullptr &&
-      (wide ? !kRotatesQueries<NB, true, true, PAGED> : !kRotatesQueries<NB, true, false, PAGED>))
+      (wide ? !kRotatesQueries<NB, true, true, PAGED, SETS> : !kRotatesQueries<NB, true, false, PAGED, SETS>))
     return hipErrorInvalidValue;
   if (!residual) launch_mfma_kernel<D, NB, false, false, PAGED, SETS>(l, grid, lds, stream);
   else if (wide) launch_mfma_kernel<D, NB, true, true, PAGED, SETS>(l, grid, lds, stream);
@@ -1279,7 +1520,10 @@ static hipError_t launch_mfma_d(DecodeLaunch& l, dim3 grid, bool residual, hipSt
     wide = wide || a.n8 + a.n3 > 0;
   }
   const bool paged = l.set[0].block_table != nullptr;
-  if (l.n_sets == 2) {  // two sets of at most 16 rows
+  if (l.n_sets == 2) {  // two sets of at most 16 rows: one wave each, sharing the reference tiles
+    l.set[0].lds_res_base = 0;
+    l.set[1].lds_res_base = l.set[0].lds_wave_bytes - MfmaGeom<D>::VT_BYTES;
+    lds = pair_lds_bytes(D, l.set, residual);
     if (paged) return launch_mfma_dp<D, 1, true, 2>(l, grid, lds, residual, wide, stream);
     return launch_mfma_dp<D, 1, false, 2>(l, grid, lds, residual, wide, stream);
   }
@@ -1299,7 +1543,7 @@ hipError_t launch_decode_partial(const DecodeArgs* sets, int n_sets, int head_di
   }
   const DecodeArgs& a = sets[0];
   const int64_t n_work = (int64_t)a.n_splits * a.batch * a.n_kv_heads;
-  const dim3 grid((unsigned)(n_sets == 1 ? n_work : (n_work + 7) / 8 * 16), n_z);
+  const dim3 grid((unsigned)n_work, n_z);
   const bool two = rows > 16;
   hipError_t e;
   if (head_dim == 128) e = two ? launch_mfma_d<128, 2>(l, grid, residual, stream) : launch_mfma_d<128, 1>(l, grid, residual, stream);

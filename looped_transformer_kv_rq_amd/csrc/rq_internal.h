@@ -82,13 +82,16 @@ struct DecodeArgs {
   int32_t max_blocks, log2_block, n_blocks;
   float scale_log2;                     // softmax scale * log2(e)
   int32_t lds_wave_bytes;               // per-wave LDS stride (set by the launcher)
+  int32_t lds_res_base;                 // paired launches: this set's residual slots start after the
+                                        // other set's (0 otherwise; set by the launcher)
   int32_t zero_residual;                // write a zero residual accumulator (reference-only launch)
 };
 
 // One partial launch holds up to kMaxSets argument sets over the same cache
 // rows, each with its own query rows (at most 16 when there are two) and
-// residual loops. The two blocks of one (batch, kv head, split) run side by
-// side on one XCD.
+// residual loops. With two, a block is a pair of waves, one per set, that
+// share each tile's reference K and V through LDS, so the reference is read
+// once for both sets.
 constexpr int kMaxSets = 2;
 struct DecodeLaunch {
   DecodeArgs set[kMaxSets];

@@ -45,9 +45,10 @@ def test_workspace_and_split_queries():
     # 16 x 8 rows of 4096 tokens: enough splits for ~512 blocks, each a multiple of 64 tokens
     n = rq.decode_splits(16, 8, 4096, 128, 32, 4)
     assert n == 4
-    # split partials (m, l, reference and residual outputs) + one 272-byte rotated-query record per row
+    # split partials (m, l, reference and residual outputs) + one 528-byte rotated-query record per
+    # row (fp16 hi and lo parts of 128 coordinates, 4 group offsets)
     part = 4 * 16 * 32 * n * (2 * 128 + 2) * 4
-    assert rq.decode_workspace_bytes(16, 8, 4096, 128, 32, 4) == (part + 255) // 256 * 256 + 4 * 16 * 32 * 272
+    assert rq.decode_workspace_bytes(16, 8, 4096, 128, 32, 4) == (part + 255) // 256 * 256 + 4 * 16 * 32 * 528
     assert rq.decode_splits(1, 1, 1, 64, 1, 1) == 1
     assert rq.decode_splits(1, 1, 1000, 64, 1, 1, n_splits=3) == 3
     assert rq.decode_splits(1, 1, 100, 64, 1, 1, n_splits=50) == 2  # never below one 64-token tile
@@ -302,3 +303,16 @@ def test_kv_entry_points_check_both_tensors():
     assert papp(pg=None) == rq.RQ_EINVAL
     assert papp(pg=rq._Pages(FAKE, 4, 96, 16)) == rq.RQ_EUNSUPPORTED
     assert papp(vs=_ptrs(FAKE + 2)) == rq.RQ_EALIGN
+
+
+def test_build_refuses_register_spills():
+    """The build's spill guard reads the compiler's resource-usage remarks."""
+    from looped_transformer_kv_rq_amd import build as b
+
+    log = "\n".join([
+        "x.hip:1:1: remark: Function Name: _Z3fooPf [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark: Function Name: _Z3barPf [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 20 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert b.scratch_users(log) == [("_Z3barPf", 20)]
