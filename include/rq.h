@@ -333,7 +333,11 @@ int rq_decode_attn_paged(const rq_shape* shape, int32_t n_q_heads, int32_t n_loo
 
 /* The uncompressed baseline: the same decode attention where loop i attends
  * over its own bf16 K/V, k[i] and v[i] (host arrays of device pointers, each
- * bf16 [B][Hkv][S][D]). Same q / out layout, workspace query and split rule. */
+ * bf16 [B][Hkv][S][D]). ResidualQuant (newx.sg page, Abstract) measures its
+ * decode throughput against a BF16 KV cache; this is that cache, decoded by
+ * the same kernels without residual loops, so the two differ only in the
+ * bytes they stream. Same q / out layout, workspace query and split rule;
+ * errors as rq_decode_attn. */
 int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
                         const uint16_t* const* k, const uint16_t* const* v, float softmax_scale,
                         int32_t n_splits, float* out, void* workspace, size_t workspace_bytes,
