@@ -80,6 +80,7 @@ extern "C" {
 #define RQ_MAX_LOOPS 8
 #define RQ_MAX_REFITS 16
 #define RQ_MAX_LAYERS 4096
+#define RQ_NOALLOC_SCRATCH_BYTES (32u << 20) /* device scratch of rq_decode_attn_noalloc */
 
 typedef enum rq_status {
   RQ_OK = 0,
@@ -292,6 +293,29 @@ int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, co
                    const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
                    float softmax_scale, int32_t n_splits, float* out, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/* rq_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same computation and kernels, with the same results (bit-identical for
+ * the same n_splits), but no workspace argument: the split partials and the
+ * rotated-query records go to a static device array of
+ * RQ_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it
+ * runs on until the process ends. The call allocates nothing and calls no
+ * allocating routine; it takes the array's device address once per device
+ * (hipGetSymbolAddress) with that device current.
+ *   Arguments, checks and errors as rq_decode_attn; in addition
+ *   RQ_EWORKSPACE when rq_decode_attn_workspace for these arguments exceeds
+ *   RQ_NOALLOC_SCRATCH_BYTES (nothing is enqueued), and RQ_EHIP if the
+ *   array's address cannot be had.
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's contents (no part of it needs to start at zero: every value a call
+ * reads back, the same call wrote first). Calls on one GPU whose kernels
+ * overlap (different streams, or different host threads) race on the array
+ * and give undefined results: serialise them, or use rq_decode_attn with a
+ * workspace per stream. */
+int rq_decode_attn_noalloc(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                           const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
+                           float softmax_scale, int32_t n_splits, float* out, void* stream);
 
 /* Decode attention over a partly filled residual cache, plus the positions
  * not yet encoded: the serving-loop form of rq_decode_attn (paperaft JSON

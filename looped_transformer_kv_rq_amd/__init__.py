@@ -21,7 +21,8 @@ __all__ = [
     "encode_rotonly", "reconstruct_rotonly", "encode_append", "decode_attn_varlen", "encode_layers",
     "encode_append_paged", "decode_attn_paged",
     "decode_varlen_workspace_bytes",
-    "decode_workspace_bytes", "decode_splits", "format_version", "library_path",
+    "decode_workspace_bytes", "decode_splits", "format_version", "library_path", "decode_attn_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "RQ_OK", "RQ_EINVAL", "RQ_EUNSUPPORTED", "RQ_EALIGN", "RQ_EWORKSPACE", "RQ_EHIP", "MAX_LOOPS",
     "WIDTHS",
 ]
@@ -30,6 +31,7 @@ RQ_OK, RQ_EINVAL, RQ_EUNSUPPORTED, RQ_EALIGN, RQ_EWORKSPACE, RQ_EHIP = 0, -1, -2
 RQ_OUT_F32, RQ_OUT_BF16 = 0, 1
 MAX_LOOPS = 8
 MAX_LAYERS = 4096
+NOALLOC_SCRATCH_BYTES = 32 << 20  # RQ_NOALLOC_SCRATCH_BYTES
 GROUP = 32
 WIDTHS = (2, 3, 4, 8)  # residual code widths
 
@@ -103,6 +105,8 @@ def _load():
         "rq_decode_attn": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, P, P, ctypes.POINTER(_LoopView),
                                           F, I32, P, P, SZ, P]),
         "rq_decode_attn_bf16": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, PP, PP, F, I32, P, P, SZ, P]),
+        "rq_decode_attn_noalloc": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, P, P,
+                                                  ctypes.POINTER(_LoopView), F, I32, P, P]),
         "rq_encode_kv": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, PP, PP, ctypes.POINTER(I32), P, P, PP, PP, PP,
                                         PP, P]),
         "rq_encode_append_kv": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, PP, PP, ctypes.POINTER(I32), P, P,
@@ -627,6 +631,34 @@ def decode_attn(q: torch.Tensor, k_ref: torch.Tensor, v_ref: torch.Tensor, loops
                             float(softmax_scale), int(n_splits), _ptr(out), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(k_ref.device, stream))
     _check(st, "rq_decode_attn")
+    return out
+
+
+def decode_attn_noalloc(q: torch.Tensor, k_ref: torch.Tensor, v_ref: torch.Tensor, loops: Sequence[LoopView],
+                        softmax_scale: Optional[float] = None, n_splits: int = 0, out: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """rq_decode_attn_noalloc: decode_attn without a workspace argument; the
+    library's static device scratch (NOALLOC_SCRATCH_BYTES per GPU) holds the
+    split partials. With `out` given, the call allocates no device memory.
+    Calls on one GPU must not overlap (they share the scratch)."""
+    lib = _load()
+    shp = _shape_of(k_ref)
+    b, h, s, d = k_ref.shape
+    if q.dim() != 4:
+        raise ValueError("q must be [n_loops, batch, n_q_heads, head_dim]")
+    n_loops, _, hq, _ = q.shape
+    _need(q, "q", torch.bfloat16, (n_loops, b, hq, d), k_ref.device)
+    _need(k_ref, "k_ref", torch.bfloat16, k_ref.shape)
+    _need(v_ref, "v_ref", torch.bfloat16, k_ref.shape, k_ref.device)
+    views = _loop_views(loops, n_loops, k_ref)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((n_loops, b, hq, d), dtype=torch.float32, device=k_ref.device)
+    _need(out, "out", torch.float32, (n_loops, b, hq, d), k_ref.device)
+    st = lib.rq_decode_attn_noalloc(ctypes.byref(shp), hq, n_loops, _ptr(q), _ptr(k_ref), _ptr(v_ref), views,
+                                    float(softmax_scale), int(n_splits), _ptr(out), _stream(k_ref.device, stream))
+    _check(st, "rq_decode_attn_noalloc")
     return out
 
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "rq.h"
 #include "rq_internal.h"
@@ -640,6 +641,59 @@ int rq_decode_attn_paged(const rq_shape* shape, int32_t n_q_heads, int32_t n_loo
   if (seq_lens != nullptr && !aligned16(seq_lens)) return RQ_EALIGN;
   return decode_impl(shape, n_q_heads, n_loops, q, k_ref, v_ref, loops, seq_lens, tail_len, tail_k, tail_v,
                      softmax_scale, n_splits, out, workspace, workspace_bytes, stream, pages);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of rq_decode_attn_noalloc: the decode workspace (split partials and
+// rotated-query records) in a static device array, so that the call allocates
+// nothing. Each GPU the library runs on holds its own copy until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory:
+// its device address comes from hipGetSymbolAddress, taken once per device
+// with that device current.
+__device__ __align__(256) unsigned char scratch[RQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's address of `scratch`, or nullptr if it cannot be had.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  if (dev >= kMaxScratchDevices) {
+    void* ptr = nullptr;
+    return hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess ? ptr : nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int rq_decode_attn_noalloc(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
+                           const uint16_t* k_ref, const uint16_t* v_ref, const rq_loop_view* loops,
+                           float softmax_scale, int32_t n_splits, float* out, void* stream) {
+  // rq_decode_attn's checks first, without a workspace: they run on the host
+  // and stop at the workspace check at the latest, before any HIP call
+  const int st = decode_impl(shape, n_q_heads, n_loops, q, k_ref, v_ref, loops, nullptr, 0, nullptr, nullptr,
+                             softmax_scale, n_splits, out, nullptr, 0, stream);
+  if (st != RQ_EWORKSPACE) return st;
+  if (rq_decode_attn_workspace(shape, n_q_heads, n_loops, n_splits) > (size_t)RQ_NOALLOC_SCRATCH_BYTES)
+    return RQ_EWORKSPACE;
+  void* ws = scratch_address();
+  if (ws == nullptr) return RQ_EHIP;
+  return decode_impl(shape, n_q_heads, n_loops, q, k_ref, v_ref, loops, nullptr, 0, nullptr, nullptr,
+                     softmax_scale, n_splits, out, ws, (size_t)RQ_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,

@@ -305,6 +305,34 @@ def test_kv_entry_points_check_both_tensors():
     assert papp(vs=_ptrs(FAKE + 2)) == rq.RQ_EALIGN
 
 
+def test_noalloc_argument_checks_and_size_limit():
+    """rq_decode_attn_noalloc: rq_decode_attn's checks (no workspace argument),
+    and a call whose workspace would exceed RQ_NOALLOC_SCRATCH_BYTES is
+    RQ_EWORKSPACE; every case fails before any HIP call."""
+    lib = rq._load()
+    views = (rq._LoopView * 2)()
+    views[0].bits, views[0].k_codes, views[0].k_scales, views[0].v_codes, views[0].v_scales = 2, FAKE, FAKE, FAKE, FAKE
+
+    def call(shape, hq=4, n=2, q=FAKE, out=FAKE, splits=0, vs=views):
+        return lib.rq_decode_attn_noalloc(ctypes.byref(shape), hq, n, q, FAKE, FAKE, vs, 0.125, splits, out, None)
+
+    sh = _shape(b=2, h=2, s=64, d=64)
+    assert call(sh, q=None) == rq.RQ_EINVAL
+    assert call(sh, hq=3) == rq.RQ_EINVAL
+    assert call(sh, n=9) == rq.RQ_EINVAL
+    assert call(sh, splits=-1) == rq.RQ_EINVAL
+    assert call(_shape(b=2, h=2, s=64, d=96)) == rq.RQ_EUNSUPPORTED
+    assert call(sh, out=FAKE + 4) == rq.RQ_EALIGN
+    bad = (rq._LoopView * 2)()
+    bad[0].bits = 5
+    assert call(sh, vs=bad) == rq.RQ_EUNSUPPORTED
+    # the largest size: 4 loops x 64 batch x 32 query heads x 16 splits needs more than 32 MiB
+    big = _shape(b=64, h=8, s=8192, d=128)
+    need = lib.rq_decode_attn_workspace(ctypes.byref(big), 32, 2, 16)
+    assert need > rq.NOALLOC_SCRATCH_BYTES
+    assert call(big, hq=32, n=2, splits=16) == rq.RQ_EWORKSPACE
+
+
 def test_build_refuses_register_spills():
     """The build's spill guard reads the compiler's resource-usage remarks."""
     from looped_transformer_kv_rq_amd import build as b
