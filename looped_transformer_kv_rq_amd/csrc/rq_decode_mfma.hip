@@ -16,23 +16,28 @@
 // Partial kernel: one block is four independent waves over one split of one
 // (batch, kv head) row. A wave takes 32-token tiles (tiles w, w+4, ...). Every
 // query row of the kv head (loops x G query heads, at most 32 = two 16-row
-// blocks) is one MFMA column; a launch with more than 16 rows whose loops fit
-// 16 each runs as two argument sets of one 16-row block. All products run on
-// v_mfma_f32_16x16x32:
+// blocks) is one MFMA column. A launch with more than 16 rows whose loops fit
+// 16 each runs as two argument sets of one 16-row block, paired: a block is
+// then two waves, one per set, that walk the same tiles and share each tile's
+// reference K and V through LDS. All products run on v_mfma_f32_16x16x32:
 //  * reference scores S^T = K_ref Q^T (bf16; exact products, fp32 sums). The
 //    K tile is loaded straight into the A operand;
-//  * residual scores per loop and scale group (fp16). A code becomes the fp16
-//    value 1 + c / 2^b when it is masked into the mantissa of 1.0. The per-row
-//    constant of that offset is taken out afterwards:
-//    q . (c - o) = 2^b (q . val) - (2^b + o) sum(q);
+//  * residual scores per loop and scale group (fp16), two products: one with
+//    the hi and one with the lo half of the rotated query (hi + lo carries it
+//    to about 2^-22). A code becomes the fp16 value 1 + c / 2^b when it is
+//    masked into the mantissa of 1.0. The per-row constant of that offset is
+//    taken out afterwards: q . (c - o) = 2^b (q . val) - (2^b + o) sum(q);
 //  * reference PV, O_ref^T += V^T P^T (bf16). P is split into bf16 hi + lo
 //    halves (error ~2^-16), and V^T is read from the LDS tile;
 //  * residual PV, O_res^T += lev^T (P s)^T (fp16; each weight P s is the
-//    fp32 P times the fp16 scale, rounded once to nearest). Levels decode exactly
-//    through a v_perm byte table (INT2: {-1.5,-0.5,0.5,1.5}; INT4 as
-//    4 lev_hi + lev_lo; INT3 from an eight-entry table). INT8 levels are
-//    formed as 2 lev = (1024 + 2c) - 1279 in fp16 against P s / 2. Rows of
-//    other loops carry P s = 0, so every loop shares one accumulator.
+//    fp32 P times the fp16 scale, rounded once to nearest). In 16-row blocks
+//    INT2 and INT4 levels enter as the mantissa value 1 + c / 2^b, and one
+//    more product with an operand of ones gives each group's sum of P s for
+//    the offset, taken out once per row after the token loop. INT3 levels
+//    (and every width in 32-row blocks) decode exactly through a v_perm byte
+//    table; INT8 levels are formed as 2 lev = (1024 + 2c) - 1279 in fp16
+//    against P s / 2. Rows of other loops carry P s = 0, so every loop shares
+//    one accumulator.
 // The MFMA output layout (lane l holds rows 4 (l / 16) + i of column l % 16)
 // gives each lane one query row and four tokens per 16-token block. The
 // softmax statistics of a row therefore stay within the row's four lanes,
@@ -1190,7 +1195,6 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   const int t_begin = split * a.tokens_per_split;
   int t_end = min(S, t_begin + a.tokens_per_split);
   if (a.seq_lens != nullptr) t_end = min(t_end, max(0, a.seq_lens[b]));  // this sequence's prefix
-  const int tlast = t_end - 1;
   const uint16_t* kbase = a.k[z] + row_base * D;
   const uint16_t* vbase = a.v[z] + row_base * D;
   constexpr int kStep = PAIR ? kTile : 4 * kTile;  // tokens between a wave's consecutive tiles
