@@ -40,10 +40,10 @@ int check_heads(const rq_shape* s, int32_t n_q_heads, int32_t n_loops) {
   return RQ_OK;
 }
 
-// Target number of partial blocks per launch (two resident blocks per CU on
-// 256 CUs, the best point of a split sweep on l4_b16_s4k and mixed_s32k); a
-// split never holds fewer tokens than one tile.
-constexpr int64_t kTargetBlocks = 512;
+// kTargetBlocks (rq_internal.h) is the number of partial blocks a launch aims
+// at: two resident blocks per CU on 256 CUs, the best point of a split sweep
+// on l4_b16_s4k and mixed_s32k. A split never holds fewer tokens than one
+// tile.
 
 struct SplitPlan {
   int32_t n_splits;
@@ -75,16 +75,32 @@ size_t workspace_bytes_for(const rq_shape* s, int32_t n_q_heads, int32_t n_loops
          (size_t)n_loops * s->batch * n_q_heads * query_prep_bytes(s->head_dim);
 }
 
+// A ragged decode with an automatic split count balances its splits over the
+// actual prefix lengths (see DecodeArgs::balance_target): up to
+// balanced_max_row_splits records per row, plus the split count of every
+// sequence (int32 [B]) after the query records.
+int32_t balanced_rec_splits(const rq_shape* s, int32_t tail_len) {
+  return balanced_max_row_splits((int64_t)s->batch * s->n_kv_heads, s->seq_len) + (tail_len > 0 ? 1 : 0);
+}
+size_t balanced_workspace_bytes(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int32_t tail_len) {
+  return workspace_bytes_for(s, n_q_heads, n_loops, balanced_rec_splits(s, tail_len)) + 4 * (size_t)s->batch;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? RQ_OK : RQ_EHIP; }
 
 int run_combine(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int32_t n_splits, const float* ws,
-                float* out, bool residual, hipStream_t stream) {
+                float* out, bool residual, hipStream_t stream, const int32_t* row_splits = nullptr,
+                int32_t tail_slot = -1) {
   CombineArgs c{};
   c.ws = ws;
   c.out = out;
   c.n_out = (int64_t)n_loops * s->batch * n_q_heads;
   c.n_splits = n_splits;
   c.residual = residual ? 1 : 0;
+  c.row_splits = row_splits;
+  c.batch = s->batch;
+  c.n_q_heads = n_q_heads;
+  c.tail_slot = tail_slot;
   return hip_status(launch_combine(c, s->head_dim, stream));
 }
 
@@ -438,15 +454,25 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
       if (!aligned16(tail_k[i]) || !aligned16(tail_v[i])) return RQ_EALIGN;
     }
   }
+  // Ragged prefixes with an automatic split count: length-balanced splits.
+  const bool balanced = seq_lens != nullptr && n_splits == 0;
   const SplitPlan plan = plan_splits(shape, n_splits);
-  const int32_t rec_splits = plan.n_splits + (tail_len > 0 ? 1 : 0);
-  if (workspace == nullptr || workspace_bytes < workspace_bytes_for(shape, n_q_heads, n_loops, rec_splits))
-    return RQ_EWORKSPACE;
+  const int32_t prefix_recs =
+      balanced ? balanced_max_row_splits((int64_t)shape->batch * shape->n_kv_heads, shape->seq_len) : plan.n_splits;
+  const int32_t rec_splits = prefix_recs + (tail_len > 0 ? 1 : 0);
+  const size_t need = balanced ? balanced_workspace_bytes(shape, n_q_heads, n_loops, tail_len)
+                               : workspace_bytes_for(shape, n_q_heads, n_loops, rec_splits);
+  if (workspace == nullptr || workspace_bytes < need) return RQ_EWORKSPACE;
   if (!aligned16(workspace)) return RQ_EALIGN;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int G = n_q_heads / shape->n_kv_heads;
   unsigned char* prep = static_cast<unsigned char*>(workspace) + partial_bytes(shape, n_q_heads, n_loops, rec_splits);
+  // balanced: the split count of every sequence, after the query records
+  int32_t* row_splits =
+      balanced ? reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) +
+                                            workspace_bytes_for(shape, n_q_heads, n_loops, rec_splits))
+               : nullptr;
   bool any_residual = false;
   for (int i = 0; i < n_loops; ++i) any_residual = any_residual || loops[i].bits != 0;
   struct Launch {
@@ -503,6 +529,12 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
       fill_common(a, shape, n_q_heads, q, softmax_scale, plan, workspace);
       a.rec_splits = rec_splits;
       a.seq_lens = seq_lens;
+      if (balanced) {
+        a.balance_target =
+            (int32_t)balanced_spread((int64_t)shape->batch * shape->n_kv_heads, shape->n_kv_heads);
+        a.max_row_splits = prefix_recs;
+        a.row_splits = row_splits;
+      }
       a.qprep = prep;
       a.k[0] = k_ref;
       a.v[0] = v_ref;
@@ -587,7 +619,7 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
     DecodeArgs a{};
     fill_common(a, &ts, n_q_heads, q, softmax_scale, tp, workspace);
     a.rec_splits = rec_splits;
-    a.split_base = plan.n_splits;
+    a.split_base = prefix_recs;
     for (int i = 0; i < n_loops; ++i) {
       a.k[i] = tail_k[i];
       a.v[i] = tail_v[i];
@@ -600,7 +632,7 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
     if (st != RQ_OK) return st;
   }
   return run_combine(shape, n_q_heads, n_loops, rec_splits, static_cast<const float*>(workspace), out,
-                     any_residual, s);
+                     any_residual, s, row_splits, balanced && tail_len > 0 ? prefix_recs : -1);
 }
 
 }  // namespace
@@ -618,6 +650,7 @@ int rq_decode_attn(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, co
 size_t rq_decode_attn_varlen_workspace(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops,
                                        int32_t n_splits, int32_t tail_len) {
   if (check_heads(shape, n_q_heads, n_loops) != RQ_OK || n_splits < 0 || tail_len < 0) return 0;
+  if (n_splits == 0) return balanced_workspace_bytes(shape, n_q_heads, n_loops, tail_len);
   return workspace_bytes_for(shape, n_q_heads, n_loops,
                              plan_splits(shape, n_splits).n_splits + (tail_len > 0 ? 1 : 0));
 }

@@ -26,6 +26,14 @@ __global__ __launch_bounds__(256) void rq_combine_kernel(CombineArgs a) {
   const int lane = threadIdx.x & 63;
   if (row >= a.n_out) return;
   const float* src = a.ws + row * a.n_splits * REC;
+  // Records to merge: all n_splits, or (length-balanced splits) sequence b's
+  // own split count, then the tail record if there is one.
+  int n_pre = a.n_splits, n_vis = a.n_splits;
+  if (a.row_splits != nullptr) {
+    const int bb = (int)((row / a.n_q_heads) % a.batch);
+    n_pre = min(a.row_splits[bb], a.n_splits);
+    n_vis = n_pre + (a.tail_slot >= 0 ? 1 : 0);
+  }
   // Splits go in chunks of kChunk whose loads are all issued before any is
   // used; the running maximum and the sums are rescaled chunk by chunk, in
   // split order, so the result does not depend on scheduling.
@@ -33,12 +41,13 @@ __global__ __launch_bounds__(256) void rq_combine_kernel(CombineArgs a) {
   float mm = -INFINITY, lsum = 0.0f, o[DJ], r[DJ];
 #pragma unroll
   for (int j = 0; j < DJ; ++j) o[j] = r[j] = 0.0f;
-  for (int s0 = 0; s0 < a.n_splits; s0 += kChunk) {
+  for (int s0 = 0; s0 < n_vis; s0 += kChunk) {
     float pm[kChunk], pl[kChunk], po[kChunk][DJ], pr[kChunk][DJ];
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
-      const bool in = s0 + c < a.n_splits;
-      const float* p = src + (in ? s0 + c : s0) * REC;
+      const bool in = s0 + c < n_vis;
+      const int v = in ? s0 + c : s0;
+      const float* p = src + (v < n_pre ? v : a.tail_slot) * REC;
       pm[c] = in ? p[0] : -INFINITY;
       pl[c] = p[1];
 #pragma unroll

@@ -1083,6 +1083,69 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
 // Instantiations that can rotate the queries themselves (DecodeArgs::qprep
 // NULL): one 16-row block of a residual launch over a dense cache with INT2 /
 // INT4 loops.
+// Where a partial block works: sequence b, kv head, split index and its
+// position range [t_begin, t_end); n_b is sequence b's split count.
+struct SplitPos {
+  int b, kvh, split, t_begin, t_end, n_b;
+};
+
+__device__ __forceinline__ int units_of(int len, int S) {
+  return (min(max(len, 0), S) + kDecodeTile - 1) / kDecodeTile;
+}
+
+// Length-balanced splits of a ragged decode (DecodeArgs::balance_target > 0).
+// Sequence b holds u_b = ceil(min(len_b, S) / 64) units of 64 positions. With
+// U = sum_b u_b and per = max(1, ceil(U * Hkv / spread)), spread =
+// balance_target, sequence b gets n_b = min(max(1, ceil(u_b / per)),
+// max_row_splits) splits of ceil(u_b / n_b) units each, so the blocks stream
+// about the same number of positions whatever the lengths. Blocks enumerate
+// (b, kv head, split) in that order; since sum_b n_b <= U / per + B, there are
+// at most spread + B * Hkv of them, and a block past the last returns false.
+// The lengths are read 64 at a time and summed and scanned across the wave, so
+// every wave of a block computes the same answer.
+__device__ __forceinline__ bool balanced_split(const DecodeArgs& a, int work, int lane, SplitPos& sp) {
+  const int B = a.batch, S = a.seq_len, H = a.n_kv_heads, cap = a.max_row_splits;
+  long long u = 0;
+  for (int i = lane; i < B; i += 64) u += units_of(a.seq_lens[i], S);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) u += __shfl_xor(u, o);
+  const long long per = max(1ll, (u * H + a.balance_target - 1) / a.balance_target);
+  long long base = 0;  // blocks of the sequences before this chunk
+  for (int c = 0; c < B; c += 64) {
+    const int i = c + lane;
+    int ub = 0, nb = 0;
+    if (i < B) {
+      ub = units_of(a.seq_lens[i], S);
+      nb = (int)min((long long)cap, max(1ll, (ub + per - 1) / per));
+    }
+    int incl = nb * H;  // inclusive scan of the blocks per sequence
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    const long long chunk = __shfl(incl, 63);
+    if (work < base + chunk) {
+      const int excl = incl - nb * H;
+      const bool mine = i < B && work >= base + excl && work < base + incl;
+      const int src = __ffsll((long long)__ballot(mine)) - 1;
+      const int n_b = __shfl(nb, src), u_b = __shfl(ub, src);
+      const int local = work - (int)(base + __shfl(excl, src));
+      const int len = min(max(a.seq_lens[c + src], 0), S);
+      const int upb = (u_b + n_b - 1) / n_b;  // units per split
+      sp.b = c + src;
+      sp.kvh = local / n_b;
+      sp.split = local % n_b;
+      sp.n_b = n_b;
+      sp.t_begin = sp.split * upb * kDecodeTile;
+      sp.t_end = min(len, sp.t_begin + upb * kDecodeTile);
+      return true;
+    }
+    base += chunk;
+  }
+  return false;
+}
+
 template <int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
 constexpr bool kRotatesQueries = NB == 1 && RESID && !WIDE && !PAGED && SETS == 1;
 
@@ -1107,11 +1170,26 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   constexpr bool PAIR = SETS == 2;
   const DecodeArgs& a = launch.set[PAIR ? wave : 0];
   const int work = blockIdx.x;
-  const int split = work % a.n_splits;
-  const int bh = work / a.n_splits;
   const int z = blockIdx.y;
-  const int b = bh / a.n_kv_heads, kvh = bh % a.n_kv_heads;
-  const int G = a.group, R = a.n_rows, S = a.seq_len;
+  const int S = a.seq_len;
+  SplitPos sp;
+  if (a.balance_target > 0) {
+    // every wave of the block gets the same answer, so a surplus block exits whole
+    if (!balanced_split(a, work, lane, sp)) return;
+    if (a.row_splits != nullptr && sp.kvh == 0 && sp.split == 0 && threadIdx.x == 0) a.row_splits[sp.b] = sp.n_b;
+  } else {
+    sp.split = work % a.n_splits;
+    const int bh0 = work / a.n_splits;
+    sp.b = bh0 / a.n_kv_heads;
+    sp.kvh = bh0 % a.n_kv_heads;
+    sp.t_begin = sp.split * a.tokens_per_split;
+    sp.t_end = min(S, sp.t_begin + a.tokens_per_split);
+    if (a.seq_lens != nullptr) sp.t_end = min(sp.t_end, max(0, a.seq_lens[sp.b]));  // this sequence's prefix
+  }
+  const int split = __builtin_amdgcn_readfirstlane(sp.split);
+  const int b = __builtin_amdgcn_readfirstlane(sp.b), kvh = __builtin_amdgcn_readfirstlane(sp.kvh);
+  const int bh = b * a.n_kv_heads + kvh;
+  const int G = a.group, R = a.n_rows;
   const int64_t row_base = (int64_t)bh * S;  // first cached vector of this (b, kv head)
 
   // ------------------------------------------------------------------ setup
@@ -1192,9 +1270,8 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
     for (int k = 0; k < kResBlocks<D, NB>; ++k) o_res[nb][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int t_begin = split * a.tokens_per_split;
-  int t_end = min(S, t_begin + a.tokens_per_split);
-  if (a.seq_lens != nullptr) t_end = min(t_end, max(0, a.seq_lens[b]));  // this sequence's prefix
+  const int t_begin = __builtin_amdgcn_readfirstlane(sp.t_begin);
+  const int t_end = __builtin_amdgcn_readfirstlane(sp.t_end);
   const uint16_t* kbase = a.k[z] + row_base * D;
   const uint16_t* vbase = a.v[z] + row_base * D;
   constexpr int kStep = PAIR ? kTile : 4 * kTile;  // tokens between a wave's consecutive tiles
@@ -1546,7 +1623,9 @@ hipError_t launch_decode_partial(const DecodeArgs* sets, int n_sets, int head_di
     rows = std::max(rows, sets[i].n_rows);
   }
   const DecodeArgs& a = sets[0];
-  const int64_t n_work = (int64_t)a.n_splits * a.batch * a.n_kv_heads;
+  const int64_t rows_kv = (int64_t)a.batch * a.n_kv_heads;
+  const int64_t n_work =
+      a.balance_target > 0 ? balanced_max_blocks(rows_kv, a.n_kv_heads, a.seq_len) : a.n_splits * rows_kv;
   const dim3 grid((unsigned)n_work, n_z);
   const bool two = rows > 16;
   hipError_t e;

@@ -76,6 +76,13 @@ struct DecodeArgs {
   int32_t n_splits, tokens_per_split;
   int32_t rec_splits, split_base;       // records per row in the workspace; this launch's first split
   const int32_t* seq_lens;              // device [B] prefix lengths, or NULL (all seq_len)
+  // Length-balanced splits (balance_target > 0, seq_lens given): the launch
+  // spreads the prefixes' 64-position units over about balance_target more
+  // blocks than one per row (balanced_spread), in splits of about equal length
+  // whatever the prefix lengths, at most max_row_splits per (batch, kv head)
+  // row, and writes sequence b's split count to row_splits[b] for the combine.
+  int32_t balance_target, max_row_splits;
+  int32_t* row_splits;
   // paged cache (block_table != NULL): tensors are [n_blocks][Hkv][2^log2_block][row];
   // position t of sequence b is in block block_table[b * max_blocks + (t >> log2_block)]
   const int32_t* block_table;
@@ -102,8 +109,13 @@ struct CombineArgs {
   const float* ws;
   float* out;
   int64_t n_out;       // n_loops * B * Hq
-  int32_t n_splits;
+  int32_t n_splits;    // records per output row in the workspace
   int32_t residual;    // records carry a rotated-domain residual accumulator
+  // Length-balanced splits: row_splits[b] (device) prefix records are valid
+  // for sequence b, then the tail record at tail_slot (-1: none). NULL: all
+  // n_splits records are valid.
+  const int32_t* row_splits;
+  int32_t batch, n_q_heads, tail_slot;
 };
 
 struct QueryPrepArgs {
@@ -132,6 +144,31 @@ int query_prep_bytes(int head_dim);
 
 // tile of tokens one decode block iteration covers; split boundaries are multiples of it
 constexpr int kDecodeTile = 64;
+
+// blocks a decode launch aims at (enough to fill the chip twice over at two
+// blocks per CU)
+constexpr int kTargetBlocks = 512;
+
+// Largest split count a length-balanced plan gives one (batch, kv head) row:
+// twice the even share of kTargetBlocks, plus one, within the positions.
+inline int balanced_max_row_splits(int64_t rows, int64_t seq_len) {
+  const int64_t even = (kTargetBlocks + rows - 1) / rows;
+  const int64_t units = (seq_len + kDecodeTile - 1) / kDecodeTile;
+  const int64_t n = 2 * even + 1;
+  return (int)(n < units ? n : (units < 1 ? 1 : units));
+}
+// Blocks a length-balanced plan may spread its units over beyond one per
+// sequence and kv head: what keeps the whole launch within kTargetBlocks (all
+// of it resident at once), and at least one split's worth per kv head.
+inline int64_t balanced_spread(int64_t rows, int64_t n_kv_heads) {
+  const int64_t a = kTargetBlocks - rows;
+  return a > n_kv_heads ? a : n_kv_heads;
+}
+// Blocks a length-balanced launch needs at most (the surplus ones exit).
+inline int64_t balanced_max_blocks(int64_t rows, int64_t n_kv_heads, int64_t seq_len) {
+  const int64_t a = balanced_spread(rows, n_kv_heads) + rows, b = rows * balanced_max_row_splits(rows, seq_len);
+  return a < b ? a : b;
+}
 
 // LDS one decode block may use (gfx950: 160 KB per workgroup)
 constexpr int kMaxBlockLds = 160 * 1024;

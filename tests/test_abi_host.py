@@ -61,6 +61,22 @@ def test_workspace_and_split_queries():
     assert rq.decode_workspace_bytes(1, 1, 2 ** 23, 128, 1, 1) == 0
 
 
+def test_varlen_workspace_of_the_length_balanced_plan():
+    # Ragged decode, automatic splits: up to 2 * ceil(512 / rows) + 1 prefix records per row
+    # (rows = B * Hkv = 64 here: 17), one tail record, the query records, then one int32 split
+    # count per sequence.
+    B, H, S, D, HQ, L = 8, 8, 32768, 128, 32, 4
+    part = L * B * HQ * (17 + 1) * (2 * D + 2) * 4
+    expect = (part + 255) // 256 * 256 + L * B * HQ * 528 + 4 * B
+    assert rq.decode_varlen_workspace_bytes(B, H, S, D, HQ, L, 0, 1) == expect
+    # an explicit split count keeps the plain plan: n_splits prefix records and the tail record
+    part4 = L * B * HQ * (4 + 1) * (2 * D + 2) * 4
+    assert rq.decode_varlen_workspace_bytes(B, H, S, D, HQ, L, 4, 1) == (part4 + 255) // 256 * 256 + L * B * HQ * 528
+    # the cap never exceeds the sequence's 64-position units
+    part1 = 1 * 2 * 1 * 1 * (2 * 64 + 2) * 4
+    assert rq.decode_varlen_workspace_bytes(2, 1, 64, 64, 1, 1, 0, 0) == (part1 + 255) // 256 * 256 + 2 * 1 * 272 + 8
+
+
 def _shape(b=1, h=1, s=4, d=64):
     return rq._Shape(b, h, s, d)
 
@@ -143,7 +159,8 @@ def test_append_and_varlen_argument_checks():
     assert ap(sh, 1, 1, x, (ctypes.c_int32 * 1)(0), FAKE, FAKE, FAKE, c, s, None) == rq.RQ_EUNSUPPORTED
     assert ap(sh, 1, 1, x, bits, FAKE, FAKE, FAKE + 2, c, s, None) == rq.RQ_EALIGN
     ws = lib.rq_decode_attn_varlen_workspace
-    assert ws(sh, 4, 2, 0, 1) > ws(sh, 4, 2, 0, 0) == lib.rq_decode_attn_workspace(sh, 4, 2, 0)
+    assert ws(sh, 4, 2, 0, 1) > ws(sh, 4, 2, 0, 0) >= lib.rq_decode_attn_workspace(sh, 4, 2, 0)
+    assert ws(sh, 4, 2, 1, 0) == lib.rq_decode_attn_workspace(sh, 4, 2, 1)  # an explicit split count
     assert ws(sh, 4, 2, 0, -1) == 0
     need = ws(sh, 4, 2, 0, 1)
     views = (rq._LoopView * 2)()

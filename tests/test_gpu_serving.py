@@ -125,6 +125,41 @@ def test_varlen_decode_matches_oracle(d, hq, tail):
         assert_attn_close(out, expect)
 
 
+@pytest.mark.parametrize("case", ["many_rows", "one_long"])
+@pytest.mark.parametrize("tail", [0, 1])
+def test_varlen_balanced_splits_match_oracle(case, tail):
+    """The automatic split plan of a ragged decode balances its splits over the
+    actual lengths. many_rows: 70 sequences (more than one 64-wide scan chunk),
+    lengths from 0 to the capacity. one_long: one sequence at the capacity and
+    fifteen short ones, so the long row's split count reaches its cap and its
+    splits grow instead."""
+    print(f"varlen balanced case={case} tail={tail}", flush=True)
+    rng = np.random.default_rng(7 + tail + (0 if case == "many_rows" else 100))
+    if case == "many_rows":
+        bits_per_loop, B, H, S, d, hq = [4, 2, 0], 70, 2, 512, 128, 8
+        lens = rng.integers(0, S + 1, size=B).astype(np.int32)
+        lens[:4] = [0, S, 1, 64]
+    else:
+        bits_per_loop, B, H, S, d, hq = [2, 0], 16, 4, 4096, 64, 16
+        lens = np.array([S, 0, 1, 5, 63, 64, 65, 100, 2, 3, 40, 17, 0, 9, 128, 33], dtype=np.int32)
+    L = len(bits_per_loop)
+    kref, vref, res = _cache(rng, B, H, S, d, bits_per_loop)
+    q = _bf16(rng, (L, B, hq, d))
+    tk = tv = None
+    if tail:
+        tk = [_bf16(rng, (B, H, tail, d)) for _ in range(L)]
+        tv = [_bf16(rng, (B, H, tail, d)) for _ in range(L)]
+    out = rq.decode_attn_varlen(to_dev(q), to_dev(kref), to_dev(vref), _views(res, bits_per_loop),
+                                seq_lens=torch.from_numpy(lens).to(DEV),
+                                tail_k=None if tk is None else [to_dev(x) for x in tk],
+                                tail_v=None if tv is None else [to_dev(x) for x in tv]).cpu().numpy()
+    kh, vh = _hat(kref, vref, res, bits_per_loop)
+    expect = oracle.decode_attn_varlen(q, kh, vh, lens, tk, tv)
+    empty = (lens == 0) if not tail else np.zeros(B, dtype=bool)
+    assert np.all(out[:, empty] == 0)  # a sequence with no position at all
+    assert_attn_close(out[:, ~empty], expect[:, ~empty])
+
+
 def test_varlen_with_full_lengths_equals_the_plain_decode():
     rng = np.random.default_rng(31)
     bits_per_loop = [2, 2, 0]
