@@ -12,8 +12,10 @@ batch * seq_len * n_loops / step time, with K steps timed between two device
 synchronisations after W untimed ones.
 
 Every input of every leg is drawn on the host and uploaded before the first
-GPU leg, and the timed steps run last, right after the other GPU legs, so the
-device is busy before them rather than idle while the host draws inputs.
+GPU work, so the device is not idle while the host draws inputs. The main
+step runs first: its W warm-up steps, the K timed steps, the marked pass and
+the roofline calls, on a device that has run nothing but its own warm-up;
+the other legs follow.
 
 `roofline` covers the fused decode (rq_decode_attn: the split-S partial
 kernel plus the small combine), the kernel the method is about. Its achieved
@@ -731,18 +733,6 @@ def main():
     del host_main, host_side
     torch.cuda.synchronize()
 
-    result_side = {}
-    peak = None
-    if not args.only_step:
-        if peak_tiles is not None:
-            peak = peak_batch_leg(g, peak_tiles, 7)
-        for n, case in side_cases.items():
-            result_side[n] = side_workload_leg(g, case, args.reps)
-            del case
-        side_cases.clear()
-        torch.cuda.empty_cache()
-        main_side = main_side_legs(g, main_case, args.reps)
-
     # ---- the main step: W untimed steps, then K steps between one pair of
     # events with nothing between the launches
     Ev = torch.cuda.Event
@@ -777,6 +767,20 @@ def main():
     n_rl = max(10, args.steps // 2)
     dec_ms = g.back_to_back(main_case.dec, n_rl)
     enc_ms = g.back_to_back(main_case.enc_kv, n_rl)
+
+    # The other legs after the main step's figures, so that the step runs on a
+    # device that has only run its own warm-up.
+    result_side = {}
+    peak = None
+    if not args.only_step:
+        if peak_tiles is not None:
+            peak = peak_batch_leg(g, peak_tiles, 7)
+        for n, case in side_cases.items():
+            result_side[n] = side_workload_leg(g, case, args.reps)
+            del case
+        side_cases.clear()
+        torch.cuda.empty_cache()
+        main_side = main_side_legs(g, main_case, args.reps)
 
     c = main_case
     dec_gbps = c.dec_b / (dec_ms * 1e-3) / 1e9
