@@ -530,8 +530,8 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
       a.rec_splits = rec_splits;
       a.seq_lens = seq_lens;
       if (balanced) {
-        a.balance_target =
-            (int32_t)balanced_spread((int64_t)shape->batch * shape->n_kv_heads, shape->n_kv_heads);
+        a.balance_target = (int32_t)balanced_max_blocks((int64_t)shape->batch * shape->n_kv_heads,
+                                                        shape->n_kv_heads, shape->seq_len);
         a.max_row_splits = prefix_recs;
         a.row_splits = row_splits;
       }

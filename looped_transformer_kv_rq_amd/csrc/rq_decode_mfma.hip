@@ -1093,23 +1093,44 @@ __device__ __forceinline__ int units_of(int len, int S) {
   return (min(max(len, 0), S) + kDecodeTile - 1) / kDecodeTile;
 }
 
+// Blocks of a length-balanced plan with `per` units per split:
+// Hkv * sum_b min(cap, max(1, ceil(u_b / per))), summed across the wave.
+__device__ __forceinline__ long long balanced_blocks(const DecodeArgs& a, long long per, int lane) {
+  const int B = a.batch, S = a.seq_len, cap = a.max_row_splits;
+  long long n = 0;
+  for (int i = lane; i < B; i += 64) n += min((long long)cap, max(1ll, (units_of(a.seq_lens[i], S) + per - 1) / per));
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) n += __shfl_xor(n, o);
+  return n * a.n_kv_heads;
+}
+
 // Length-balanced splits of a ragged decode (DecodeArgs::balance_target > 0).
-// Sequence b holds u_b = ceil(min(len_b, S) / 64) units of 64 positions. With
-// U = sum_b u_b and per = max(1, ceil(U * Hkv / spread)), spread =
-// balance_target, sequence b gets n_b = min(max(1, ceil(u_b / per)),
-// max_row_splits) splits of ceil(u_b / n_b) units each, so the blocks stream
-// about the same number of positions whatever the lengths. Blocks enumerate
-// (b, kv head, split) in that order; since sum_b n_b <= U / per + B, there are
-// at most spread + B * Hkv of them, and a block past the last returns false.
-// The lengths are read 64 at a time and summed and scanned across the wave, so
-// every wave of a block computes the same answer.
+// Sequence b holds u_b = ceil(min(len_b, S) / 64) units of 64 positions and
+// gets n_b = min(max(1, ceil(u_b / per)), max_row_splits) splits of
+// ceil(u_b / n_b) units each, so the blocks stream about the same number of
+// positions whatever the lengths. `per` is the smallest unit count per split
+// whose plan needs at most balance_target blocks (the launch's grid, all of it
+// resident at once): found by bisection between ceil(U * Hkv / target) and
+// ceil(U * Hkv / (target - B * Hkv)), U = sum_b u_b, since the block count
+// falls as `per` grows and is at most U * Hkv / per + B * Hkv. Blocks
+// enumerate (b, kv head, split) in that order; a block past the last returns
+// false. The lengths are read 64 at a time and summed and scanned across the
+// wave, so every wave of every block computes the same plan.
 __device__ __forceinline__ bool balanced_split(const DecodeArgs& a, int work, int lane, SplitPos& sp) {
   const int B = a.batch, S = a.seq_len, H = a.n_kv_heads, cap = a.max_row_splits;
+  const long long target = a.balance_target;
   long long u = 0;
   for (int i = lane; i < B; i += 64) u += units_of(a.seq_lens[i], S);
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) u += __shfl_xor(u, o);
-  const long long per = max(1ll, (u * H + a.balance_target - 1) / a.balance_target);
+  const long long spread = max((long long)H, target - (long long)B * H);
+  long long lo = max(1ll, (u * H + target - 1) / target), hi = max(lo, (u * H + spread - 1) / spread);
+  while (lo < hi) {  // the smallest per in [lo, hi] whose plan fits the target
+    const long long mid = (lo + hi) / 2;
+    if (balanced_blocks(a, mid, lane) <= target) hi = mid;
+    else lo = mid + 1;
+  }
+  const long long per = lo;
   long long base = 0;  // blocks of the sequences before this chunk
   for (int c = 0; c < B; c += 64) {
     const int i = c + lane;

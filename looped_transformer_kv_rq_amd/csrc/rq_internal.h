@@ -77,10 +77,10 @@ struct DecodeArgs {
   int32_t rec_splits, split_base;       // records per row in the workspace; this launch's first split
   const int32_t* seq_lens;              // device [B] prefix lengths, or NULL (all seq_len)
   // Length-balanced splits (balance_target > 0, seq_lens given): the launch
-  // spreads the prefixes' 64-position units over about balance_target more
-  // blocks than one per row (balanced_spread), in splits of about equal length
+  // cuts the prefixes' 64-position units into splits of about equal length
   // whatever the prefix lengths, at most max_row_splits per (batch, kv head)
-  // row, and writes sequence b's split count to row_splits[b] for the combine.
+  // row and at most balance_target blocks (its grid) in all, and writes
+  // sequence b's split count to row_splits[b] for the combine.
   int32_t balance_target, max_row_splits;
   int32_t* row_splits;
   // paged cache (block_table != NULL): tensors are [n_blocks][Hkv][2^log2_block][row];
@@ -157,16 +157,13 @@ inline int balanced_max_row_splits(int64_t rows, int64_t seq_len) {
   const int64_t n = 2 * even + 1;
   return (int)(n < units ? n : (units < 1 ? 1 : units));
 }
-// Blocks a length-balanced plan may spread its units over beyond one per
-// sequence and kv head: what keeps the whole launch within kTargetBlocks (all
-// of it resident at once), and at least one split's worth per kv head.
-inline int64_t balanced_spread(int64_t rows, int64_t n_kv_heads) {
-  const int64_t a = kTargetBlocks - rows;
-  return a > n_kv_heads ? a : n_kv_heads;
-}
-// Blocks a length-balanced launch needs at most (the surplus ones exit).
+// Grid of a length-balanced launch, the most blocks its plan may use (the
+// surplus ones exit): kTargetBlocks, so that all of it is resident at once
+// (at least one block per row and kv head more than one per row), or every
+// row at its cap.
 inline int64_t balanced_max_blocks(int64_t rows, int64_t n_kv_heads, int64_t seq_len) {
-  const int64_t a = balanced_spread(rows, n_kv_heads) + rows, b = rows * balanced_max_row_splits(rows, seq_len);
+  const int64_t spread = kTargetBlocks - rows > n_kv_heads ? kTargetBlocks - rows : n_kv_heads;
+  const int64_t a = spread + rows, b = rows * balanced_max_row_splits(rows, seq_len);
   return a < b ? a : b;
 }
 
