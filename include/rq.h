@@ -348,8 +348,15 @@ int rq_decode_attn_noalloc(const rq_shape* shape, int32_t n_q_heads, int32_t n_l
  *   tail_k[i], tail_v[i]  bf16 [B][Hkv][tail_len][D] for loop i (host arrays of
  *              device pointers; ignored when tail_len = 0)
  * A row with no position at all (seq_lens[b] = 0 and no tail) is all zeros.
+ * With seq_lens given and n_splits = 0 the splits follow the actual lengths:
+ * each sequence's prefix is cut into equal splits, sized so that every block
+ * of the launch streams about the same number of positions (at most
+ * 2 * ceil(512 / (B * Hkv)) + 1 splits per sequence). An explicit n_splits
+ * cuts the capacity S_cap instead, as rq_decode_attn does. Results are
+ * identical from run to run for the same lengths and n_splits.
  * Other arguments, the output and the errors are as in rq_decode_attn. The
- * workspace size comes from rq_decode_attn_varlen_workspace. */
+ * workspace size comes from rq_decode_attn_varlen_workspace (n_splits = 0:
+ * room for the length-following plan, whatever the lengths). */
 size_t rq_decode_attn_varlen_workspace(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops,
                                        int32_t n_splits, int32_t tail_len);
 int rq_decode_attn_varlen(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
