@@ -125,20 +125,26 @@ def test_varlen_decode_matches_oracle(d, hq, tail):
         assert_attn_close(out, expect)
 
 
-@pytest.mark.parametrize("case", ["many_rows", "one_long"])
+@pytest.mark.parametrize("case", ["many_rows", "one_long", "rows_past_target"])
 @pytest.mark.parametrize("tail", [0, 1])
 def test_varlen_balanced_splits_match_oracle(case, tail):
     """The automatic split plan of a ragged decode balances its splits over the
     actual lengths. many_rows: 70 sequences (more than one 64-wide scan chunk),
     lengths from 0 to the capacity. one_long: one sequence at the capacity and
     fifteen short ones, so the long row's split count reaches its cap and its
-    splits grow instead."""
+    splits grow instead. rows_past_target: 300 sequences x 2 KV heads, more
+    (batch, kv head) rows than the 512 blocks a launch aims at, so every
+    sequence keeps one split."""
     print(f"varlen balanced case={case} tail={tail}", flush=True)
-    rng = np.random.default_rng(7 + tail + (0 if case == "many_rows" else 100))
+    rng = np.random.default_rng(7 + tail + {"many_rows": 0, "one_long": 100, "rows_past_target": 200}[case])
     if case == "many_rows":
         bits_per_loop, B, H, S, d, hq = [4, 2, 0], 70, 2, 512, 128, 8
         lens = rng.integers(0, S + 1, size=B).astype(np.int32)
         lens[:4] = [0, S, 1, 64]
+    elif case == "rows_past_target":
+        bits_per_loop, B, H, S, d, hq = [2, 0], 300, 2, 192, 64, 4
+        lens = rng.integers(0, S + 1, size=B).astype(np.int32)
+        lens[:3] = [0, S, 65]
     else:
         bits_per_loop, B, H, S, d, hq = [2, 0], 16, 4, 4096, 64, 16
         lens = np.array([S, 0, 1, 5, 63, 64, 65, 100, 2, 3, 40, 17, 0, 9, 128, 33], dtype=np.int32)
