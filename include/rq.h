@@ -268,7 +268,12 @@ int rq_encode_layers(const rq_shape* shape, int32_t n_layers, int32_t n_loops, c
                      uint16_t* const* scales, void* stream);
 
 /* Split count rq_decode_attn / rq_decode_attn_bf16 will use for a request of
- * n_splits (0 = automatic). Host only. Returns <= 0 on invalid arguments. */
+ * n_splits (0 = automatic). Splits hold whole 64-position units. The automatic
+ * count depends on the shape, n_q_heads and n_loops only: it is the one with
+ * the least modelled time ceil(B*Hkv*n / R) * (1/n + 384/seq_len), R being the
+ * partial blocks the device holds at once (512 for at most 16 query rows per
+ * kv head, 1024 for more rows of at most 16 heads each, 256 above 16 heads).
+ * Host only. Returns <= 0 on invalid arguments. */
 int32_t rq_decode_attn_splits(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits);
 
 /* Workspace bytes needed by rq_decode_attn and rq_decode_attn_bf16 for these

@@ -40,26 +40,60 @@ int check_heads(const rq_shape* s, int32_t n_q_heads, int32_t n_loops) {
   return RQ_OK;
 }
 
-// kTargetBlocks (rq_internal.h) is the number of partial blocks a launch aims
-// at: two resident blocks per CU on 256 CUs, the best point of a split sweep
-// on l4_b16_s4k and mixed_s32k. A split never holds fewer tokens than one
-// tile.
+// Automatic split count. The partial blocks of a launch run in rounds of as
+// many as the device holds at once: two 4-wave blocks per CU (one 16-row set),
+// four 2-wave blocks (paired sets, more than 16 query rows of at most 16 per
+// kv head) or one (32-row blocks, more than 16 query heads per kv head), on
+// 256 CUs. A round that is only partly full leaves CUs idle for a whole block
+// time, and every block also pays a fixed start and merge (taken as 6 tiles of
+// tokens). The plan takes the split count with the least modelled time,
+//   ceil(rows * n / round) * (1 / n + 6 * 64 / seq_len)   (in row times),
+// the smallest such n on ties. This keeps the best points of split sweeps on
+// l4_b16_s4k (4) and mixed_s32k (8), and at the peak batch (10,720 rows in
+// rounds of 1,024 blocks) takes 2 splits, whose 21 rounds of half-length
+// blocks end 5% sooner than 11 full-length ones. A split never holds fewer
+// tokens than one 64-token unit.
 
 struct SplitPlan {
   int32_t n_splits;
   int32_t tokens_per_split;
 };
 
-SplitPlan plan_splits(const rq_shape* s, int32_t requested) {
-  const int64_t rows = (int64_t)s->batch * s->n_kv_heads;
-  const int64_t max_splits = (s->seq_len + kDecodeTile - 1) / kDecodeTile;
-  int64_t n = requested > 0 ? requested : (kTargetBlocks + rows - 1) / rows;
+int64_t round_blocks(const rq_shape* s, int32_t n_q_heads, int32_t n_loops) {
+  const int64_t G = n_q_heads / s->n_kv_heads;
+  if (G > 16) return 256;
+  if (G * n_loops > 16) return 1024;
+  return 512;
+}
+
+// The split count a request of n gives: splits of a whole number of 64-token
+// units, as few as hold the positions.
+static SplitPlan realize_splits(int64_t seq_len, int64_t n) {
+  const int64_t max_splits = (seq_len + kDecodeTile - 1) / kDecodeTile;
   if (n < 1) n = 1;
   if (n > max_splits) n = max_splits;
-  int64_t tps = (s->seq_len + n - 1) / n;
+  int64_t tps = (seq_len + n - 1) / n;
   tps = (tps + kDecodeTile - 1) / kDecodeTile * kDecodeTile;
-  n = (s->seq_len + tps - 1) / tps;
-  return {(int32_t)n, (int32_t)tps};
+  return {(int32_t)((seq_len + tps - 1) / tps), (int32_t)tps};
+}
+
+SplitPlan plan_splits(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int32_t requested) {
+  if (requested > 0) return realize_splits(s->seq_len, requested);
+  const int64_t rows = (int64_t)s->batch * s->n_kv_heads;
+  const int64_t round = round_blocks(s, n_q_heads, n_loops);
+  const double fixed = 6.0 * kDecodeTile / (double)s->seq_len;
+  SplitPlan best_plan = realize_splits(s->seq_len, 1);
+  double best = 0.0;
+  for (int64_t c = 1; c <= 64; ++c) {
+    const SplitPlan p = realize_splits(s->seq_len, c);
+    const int64_t n = p.n_splits;
+    const double t = (double)((rows * n + round - 1) / round) * (1.0 / (double)n + fixed);
+    if (c == 1 || t < best * (1.0 - 1e-9)) {
+      best = t;
+      best_plan = p;
+    }
+  }
+  return best_plan;
 }
 
 // Workspace: split partials [n_loops][B][Hq][n_splits][2D + 2] floats, padded
@@ -398,12 +432,12 @@ int rq_reconstruct_rotonly(const rq_shape* shape, int32_t bits, const uint32_t* 
 
 int32_t rq_decode_attn_splits(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits) {
   if (check_heads(shape, n_q_heads, n_loops) != RQ_OK || n_splits < 0) return 0;
-  return plan_splits(shape, n_splits).n_splits;
+  return plan_splits(shape, n_q_heads, n_loops, n_splits).n_splits;
 }
 
 size_t rq_decode_attn_workspace(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits) {
   if (check_heads(shape, n_q_heads, n_loops) != RQ_OK || n_splits < 0) return 0;
-  return workspace_bytes_for(shape, n_q_heads, n_loops, plan_splits(shape, n_splits).n_splits);
+  return workspace_bytes_for(shape, n_q_heads, n_loops, plan_splits(shape, n_q_heads, n_loops, n_splits).n_splits);
 }
 
 }  // extern "C"
@@ -456,7 +490,7 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
   }
   // Ragged prefixes with an automatic split count: length-balanced splits.
   const bool balanced = seq_lens != nullptr && n_splits == 0;
-  const SplitPlan plan = plan_splits(shape, n_splits);
+  const SplitPlan plan = plan_splits(shape, n_q_heads, n_loops, n_splits);
   const int32_t prefix_recs =
       balanced ? balanced_max_row_splits((int64_t)shape->batch * shape->n_kv_heads, shape->seq_len) : plan.n_splits;
   const int32_t rec_splits = prefix_recs + (tail_len > 0 ? 1 : 0);
@@ -652,7 +686,7 @@ size_t rq_decode_attn_varlen_workspace(const rq_shape* shape, int32_t n_q_heads,
   if (check_heads(shape, n_q_heads, n_loops) != RQ_OK || n_splits < 0 || tail_len < 0) return 0;
   if (n_splits == 0) return balanced_workspace_bytes(shape, n_q_heads, n_loops, tail_len);
   return workspace_bytes_for(shape, n_q_heads, n_loops,
-                             plan_splits(shape, n_splits).n_splits + (tail_len > 0 ? 1 : 0));
+                             plan_splits(shape, n_q_heads, n_loops, n_splits).n_splits + (tail_len > 0 ? 1 : 0));
 }
 
 int rq_decode_attn_varlen(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
@@ -744,7 +778,7 @@ int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loop
   for (int i = 0; i < n_loops; ++i) {
     if (!aligned16(k[i]) || !aligned16(v[i])) return RQ_EALIGN;
   }
-  const SplitPlan plan = plan_splits(shape, n_splits);
+  const SplitPlan plan = plan_splits(shape, n_q_heads, n_loops, n_splits);
   if (workspace == nullptr || workspace_bytes < workspace_bytes_for(shape, n_q_heads, n_loops, plan.n_splits))
     return RQ_EWORKSPACE;
   if (!aligned16(workspace)) return RQ_EALIGN;

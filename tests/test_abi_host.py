@@ -361,3 +361,42 @@ def test_build_refuses_register_spills():
         "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 20 [-Rpass-analysis=kernel-resource-usage]",
     ])
     assert b.scratch_users(log) == [("_Z3barPf", 20)]
+
+
+def _modelled_splits(rows, seq_len, round_blocks):
+    """The automatic split count's rule written out: a request of c splits
+    becomes splits of whole 64-token units (as few as hold the positions); of
+    c = 1 .. 64, the one whose split count n has the least modelled time
+    ceil(rows * n / round) * (1 / n + 6 * 64 / seq_len), the first on ties."""
+    units = -(-seq_len // 64)
+    best, best_n = None, 1
+    for c in range(1, 65):
+        c = min(c, units)
+        tps = -(-(-(-seq_len // c)) // 64) * 64
+        n = -(-seq_len // tps)
+        t = -(-rows * n // round_blocks) * (1.0 / n + 6.0 * 64 / seq_len)
+        if best is None or t < best * (1 - 1e-9):
+            best, best_n = t, n
+    return best_n
+
+
+def test_automatic_splits_fill_whole_rounds():
+    """The automatic split count follows the rounds of resident blocks: 512 for one
+    16-row set, 1,024 for paired sets (more than 16 query rows per kv head, at most
+    16 heads each), 256 for 32-row blocks. The sweep points of the 16-row kernel
+    stay (4 splits at 16 x 8 rows of 4K, 8 at 8 x 8 rows of 32K), and the peak-batch
+    cache (10,720 rows of 16K positions, 32 rows per kv head) takes 2 splits: 21
+    rounds of half-length blocks instead of 11 rounds whose last one is half empty."""
+    assert rq.decode_splits(16, 8, 4096, 128, 32, 4) == 4
+    assert rq.decode_splits(8, 8, 32768, 128, 32, 4) == 8
+    assert rq.decode_splits(32, 8, 8192, 128, 32, 4) == 2
+    assert rq.decode_splits(2680, 4, 16384, 128, 16, 8) == 2
+    assert rq.decode_splits(744, 4, 16384, 128, 16, 8) == 1
+    # a paired launch at a small batch fills 1,024 slots, not 512
+    assert rq.decode_splits(4, 4, 16384, 128, 16, 8) * 16 == 1024
+    cases = [(b, h, s, g, nl) for b in (1, 3, 8, 16, 64, 300, 1072, 2680) for h in (1, 4, 8)
+             for s in (64, 1000, 4096, 16384) for g, nl in ((4, 4), (4, 8), (16, 2), (20, 1), (32, 2))]
+    for b, h, s, g, nl in cases:
+        round_blocks = 256 if g > 16 else (1024 if g * nl > 16 else 512)
+        got = rq.decode_splits(b, h, s, 128, g * h, nl)
+        assert got == _modelled_splits(b * h, s, round_blocks), (b, h, s, g, nl, got)
