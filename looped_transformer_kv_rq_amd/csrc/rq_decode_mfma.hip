@@ -188,6 +188,17 @@ __host__ __device__ constexpr int loop_lds_bytes(int d, int bits) {
   return bits == 0 ? 0 : 256 * (d * bits / 32) + 128 * (d / 32);
 }
 
+// K code words sit in LDS as [token][W] in 16-byte chunks. With SWZ (the
+// kernels without INT3 / INT8 loops) the chunks of token t are rotated by
+// ((t * W/4) >> 4) & (W/4 - 1) for INT2 / INT4: the 16 tokens of one MFMA row
+// block, each read at one chunk index, then fall on different LDS banks.
+// Unrotated, INT4 tokens m, m+4, m+8 and m+12 (and INT2 tokens m and m+8)
+// share banks: 257 conflict cycles per tile and wave at mixed_s32k, against
+// 1 rotated, and the decode 3% faster. The INT3 / INT8 kernels, at their
+// register limit, spill with the rotation and keep the plain order.
+template <int D, int BITS, bool SWZ>
+constexpr int kKcSwz = SWZ && (BITS == 2 || BITS == 4) ? D * BITS / 128 - 1 : 0;
+
 // LDS offset of residual slot li's tile data inside a wave's buffer: the V
 // tile, then the slots in the launcher's order INT8, INT4, INT3, INT2 (after
 // the other set's slots in a paired launch, lds_res_base).
@@ -408,7 +419,7 @@ struct QueryLo<D, NB, kLoRecord> {
 };
 
 // Issue the DMA of one residual loop's tile data (codes and scales of K and V).
-template <int D, int BITS, bool FULL>
+template <int D, int BITS, bool FULL, bool SWZ>
 __device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned char* base, int64_t row_base,
                                            int t0, int tlast, int lane) {
   constexpr int NG = D / 32;
@@ -426,10 +437,10 @@ __device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned
     const auto ks_r = row_rsrc(a.ks[li] + row_base * NG, S * 2u * NG);
     const auto vs_r = row_rsrc(a.vs[li] + row_base * NG, S * 2u * NG);
     const uint32_t tc = (uint32_t)t0 * 4u * W, ts = (uint32_t)t0 * 2u * NG;
-    const uint32_t lane16 = 16u * (uint32_t)lane;
+    const uint32_t kc_lane = 16u * (uint32_t)(lane ^ ((lane >> 4) & kKcSwz<D, BITS, SWZ>));
 #pragma unroll
     for (int i = 0; i * 64 < 8 * W; ++i) {
-      if (8 * W >= 64 * (i + 1) || 64 * i + lane < 8 * W) bdma16(kc_r, lane16, tc + 1024 * i, kc_l + 1024 * i);
+      if (8 * W >= 64 * (i + 1) || 64 * i + lane < 8 * W) bdma16(kc_r, kc_lane, tc + 1024 * i, kc_l + 1024 * i);
     }
     if (16 * NG >= 64 || lane < 16 * NG) {
       bdma4(ks_r, 4u * (uint32_t)lane, ts, ks_l);
@@ -446,7 +457,7 @@ __device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned
     for (int i = 0; i * 64 < 8 * W; ++i) {
       const int c = 64 * i + lane;
       if (8 * W >= 64 * (i + 1) || c < 8 * W) {
-        const int tok = c / (W / 4), q4 = c % (W / 4);
+        const int tok = c / (W / 4), q4 = (c % (W / 4)) ^ ((c >> 4) & kKcSwz<D, BITS, SWZ>);
         dma16(a.kc[li] + (row_base + min(t0 + tok, tlast)) * W + 4 * q4, kc_l + 1024 * i);
       }
     }
@@ -505,7 +516,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
 
 // Residual scores of loop li added to this lane's score fragment. Rows of
 // other loops get zero factors (qm = qo = 0), so every lane runs the same code.
-template <int D, int NB, int BITS, class QL>
+template <int D, int NB, int BITS, bool SWZ, class QL>
 __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, const unsigned char* base,
                                                 const uint4 (&qtB)[NB][D / 32], const QL& qtL,
                                                 const float (&qoff)[NB][D / 32], const float (&qmul)[NB],
@@ -528,16 +539,17 @@ __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, con
   for (int bk = 0; bk < 2; ++bk) {
     // code words of token 16bk + m (this lane's A-operand row)
     const unsigned char* cw = kc_l + (16 * bk + m) * W * 4;
+    const int kcr = (((16 * bk + m) * (W / 4)) >> 4) & kKcSwz<D, BITS, SWZ>;  // this token's chunk rotation
     uint4 kx[NG];
     if constexpr (BITS == 2) {
       // element 2i <- field 4(g&1) + i of word 2ks + (g>>1), element 2i+1 <- the field 8 later
       uint32_t wsel[NG];
       const bool hi = (g >> 1) != 0;
-      const uint4 w0 = *reinterpret_cast<const uint4*>(cw);
+      const uint4 w0 = *reinterpret_cast<const uint4*>(cw + 16 * (0 ^ kcr));
       wsel[0] = hi ? w0.y : w0.x;
       wsel[1] = hi ? w0.w : w0.z;
       if constexpr (NG == 4) {
-        const uint4 w1 = *reinterpret_cast<const uint4*>(cw + 16);
+        const uint4 w1 = *reinterpret_cast<const uint4*>(cw + 16 * (1 ^ kcr));
         wsel[2] = hi ? w1.y : w1.x;
         wsel[3] = hi ? w1.w : w1.z;
       }
@@ -591,7 +603,7 @@ __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, con
       const uint32_t selB = ((b0 + 1u) << 8) | ((5u + b0) << 24);
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
-        const uint2 w = *reinterpret_cast<const uint2*>(cw + (4 * ks + 2 * (g >> 1)) * 4);
+        const uint2 w = *reinterpret_cast<const uint2*>(cw + 16 * (ks ^ kcr) + 8 * (g >> 1));
         const uint32_t tA = vperm(w.y, w.x, selA), tB = vperm(w.y, w.x, selB);
         kx[ks].x = and_or(tA >> 2, k.m4, k.one);
         kx[ks].y = and_or(tA >> 6, k.m4, k.one);
@@ -789,18 +801,18 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* b
       // slots INT8, INT4, INT3, INT2
       const int e8 = a.n8, e4 = e8 + a.n4, e3 = e4 + a.n3, e2 = e3 + a.n2;
       for (int li = 0; li < e8; ++li)
-        stage_loop<D, 8, FULL>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
+        stage_loop<D, 8, FULL, false>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
       for (int li = e8; li < e4; ++li)
-        stage_loop<D, 4, FULL>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
+        stage_loop<D, 4, FULL, false>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
       for (int li = e4; li < e3; ++li)
-        stage_loop<D, 3, FULL>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
+        stage_loop<D, 3, FULL, false>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
       for (int li = e3; li < e2; ++li)
-        stage_loop<D, 2, FULL>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
+        stage_loop<D, 2, FULL, false>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
     } else {
       for (int li = 0; li < a.n4; ++li)
-        stage_loop<D, 4, FULL>(a, li, buf + slot_lds_offset<D, false>(a, li), row_base, t0, tlast, lane);
+        stage_loop<D, 4, FULL, true>(a, li, buf + slot_lds_offset<D, false>(a, li), row_base, t0, tlast, lane);
       for (int li = a.n4; li < a.n4 + a.n2; ++li)
-        stage_loop<D, 2, FULL>(a, li, buf + slot_lds_offset<D, false>(a, li), row_base, t0, tlast, lane);
+        stage_loop<D, 2, FULL, true>(a, li, buf + slot_lds_offset<D, false>(a, li), row_base, t0, tlast, lane);
     }
   }
   if constexpr (FULL) {
@@ -963,18 +975,18 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
     if constexpr (WIDE) {
       const int e8 = a.n8, e4 = e8 + a.n4, e3 = e4 + a.n3, e2 = e3 + a.n2;
       for (int li = 0; li < e8; ++li)
-        residual_scores<D, NB, 8>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 8, false>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
       for (int li = e8; li < e4; ++li)
-        residual_scores<D, NB, 4>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 4, false>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
       for (int li = e4; li < e3; ++li)
-        residual_scores<D, NB, 3>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 3, false>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
       for (int li = e3; li < e2; ++li)
-        residual_scores<D, NB, 2>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 2, false>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
     } else {
       for (int li = 0; li < a.n4; ++li)
-        residual_scores<D, NB, 4>(a, li, buf + slot_lds_offset<D, false>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 4, true>(a, li, buf + slot_lds_offset<D, false>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
       for (int li = a.n4; li < a.n4 + a.n2; ++li)
-        residual_scores<D, NB, 2>(a, li, buf + slot_lds_offset<D, false>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 2, true>(a, li, buf + slot_lds_offset<D, false>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
     }
   }
 
