@@ -188,16 +188,18 @@ __host__ __device__ constexpr int loop_lds_bytes(int d, int bits) {
   return bits == 0 ? 0 : 256 * (d * bits / 32) + 128 * (d / 32);
 }
 
-// K code words sit in LDS as [token][W] in 16-byte chunks. With SWZ (the
-// kernels without INT3 / INT8 loops) the chunks of token t are rotated by
-// ((t * W/4) >> 4) & (W/4 - 1) for INT2 / INT4: the 16 tokens of one MFMA row
-// block, each read at one chunk index, then fall on different LDS banks.
+// K code words sit in LDS as [token][W] in 16-byte chunks. With SWZ the chunks
+// of token t are rotated by ((t * W/4) >> 4) & min(W/4 - 1, 3) as the DMA lands
+// them: the 16 tokens of one MFMA row block, each read at one chunk index,
+// then fall on different LDS banks (on two at most for INT8 at head_dim 128).
 // Unrotated, INT4 tokens m, m+4, m+8 and m+12 (and INT2 tokens m and m+8)
 // share banks: 257 conflict cycles per tile and wave at mixed_s32k, against
-// 1 rotated, and the decode 3% faster. The INT3 / INT8 kernels, at their
-// register limit, spill with the rotation and keep the plain order.
+// 1 rotated, and the decode 3% faster; INT8 tokens two apart share them
+// (eight ways). The kernels with INT3 / INT8 loops, at their register limit,
+// rotate only the INT8 loops (the 32-row ones not at all): the per-lane
+// offsets of every width spill them.
 template <int D, int BITS, bool SWZ>
-constexpr int kKcSwz = SWZ && (BITS == 2 || BITS == 4) ? D * BITS / 128 - 1 : 0;
+constexpr int kKcSwz = SWZ && BITS != 3 ? (D * BITS / 128 - 1 < 3 ? D * BITS / 128 - 1 : 3) : 0;
 
 // LDS offset of residual slot li's tile data inside a wave's buffer: the V
 // tile, then the slots in the launcher's order INT8, INT4, INT3, INT2 (after
@@ -569,8 +571,9 @@ __device__ __forceinline__ void residual_scores(const DecodeArgs& a, int li, con
       const uint32_t* row = reinterpret_cast<const uint32_t*>(cw);
 #pragma unroll
       for (int ks = 0; ks < NG; ++ks) {
-        const uint32_t wa = row[8 * ks + 4 * (g >> 1) + (g & 1)];
-        const uint32_t wb = row[8 * ks + 4 * (g >> 1) + (g & 1) + 2];
+        const int cb = 4 * ((2 * ks + (g >> 1)) ^ kcr) + (g & 1);  // the word's rotated place
+        const uint32_t wa = row[cb];
+        const uint32_t wb = row[cb + 2];
         kx[ks].x = (vperm(wb, wa, 0x0C040C00u) << 2) | k.one;
         kx[ks].y = (vperm(wb, wa, 0x0C050C01u) << 2) | k.one;
         kx[ks].z = (vperm(wb, wa, 0x0C060C02u) << 2) | k.one;
@@ -789,7 +792,7 @@ __device__ __forceinline__ void residual_pv(const DecodeArgs& a, int li, const u
 // Issue every load of one tile: the residual loops' codes and scales and the
 // V reference tile by LDS DMA into `buf`, the K reference into registers.
 // WITH_K: the K reference into registers; WITH_V: the V tile into LDS.
-template <int D, bool RESID, bool WIDE, bool FULL, bool WITH_K = true, bool WITH_V = true>
+template <int D, bool RESID, bool WIDE, bool FULL, bool WITH_K = true, bool WITH_V = true, bool SWZ8 = true>
 __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* buf, const uint16_t* kbase,
                                            const uint16_t* vbase, int64_t row_base, int t0, int tlast, int lane,
                                            int m, int g, uint4 (&ka)[2][D / 32]) {
@@ -801,7 +804,7 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, unsigned char* b
       // slots INT8, INT4, INT3, INT2
       const int e8 = a.n8, e4 = e8 + a.n4, e3 = e4 + a.n3, e2 = e3 + a.n2;
       for (int li = 0; li < e8; ++li)
-        stage_loop<D, 8, FULL, false>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
+        stage_loop<D, 8, FULL, SWZ8>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
       for (int li = e8; li < e4; ++li)
         stage_loop<D, 4, FULL, false>(a, li, buf + slot_lds_offset<D, true>(a, li), row_base, t0, tlast, lane);
       for (int li = e4; li < e3; ++li)
@@ -867,7 +870,7 @@ __device__ __forceinline__ bool tile_valid(const DecodeArgs& a, int b, int t) {
 // Issue the tile at token t of sequence b, kv head kvh (blockIdx.y = z), dense
 // or paged. Unclamped loads only when every token of the tile is one of this
 // call's positions: positions past a sequence's length may hold any bits.
-template <int D, bool RESID, bool WIDE, bool PAGED>
+template <int D, bool RESID, bool WIDE, bool PAGED, bool SWZ8 = true>
 __device__ __forceinline__ void issue_at(const DecodeArgs& a, unsigned char* buf, const uint16_t* kbase,
                                          const uint16_t* vbase, int64_t row_base, int b, int kvh, int z, int t,
                                          int t_end, int lane, int m, int g, uint4 (&ka)[2][D / 32]) {
@@ -879,11 +882,11 @@ __device__ __forceinline__ void issue_at(const DecodeArgs& a, unsigned char* buf
     const int64_t tv = (((int64_t)blk * a.n_kv_heads + kvh) << a.log2_block) + (t & ((1 << a.log2_block) - 1));
     const uint16_t* kt = a.k[z] + tv * D;
     const uint16_t* vt = a.v[z] + tv * D;
-    if (full) issue_tile<D, RESID, WIDE, true>(a, buf, kt, vt, tv, 0, tlast - t, lane, m, g, ka);
-    else issue_tile<D, RESID, WIDE, false>(a, buf, kt, vt, tv, 0, tlast - t, lane, m, g, ka);
+    if (full) issue_tile<D, RESID, WIDE, true, true, true, SWZ8>(a, buf, kt, vt, tv, 0, tlast - t, lane, m, g, ka);
+    else issue_tile<D, RESID, WIDE, false, true, true, SWZ8>(a, buf, kt, vt, tv, 0, tlast - t, lane, m, g, ka);
   } else {
-    if (full) issue_tile<D, RESID, WIDE, true>(a, buf, kbase, vbase, row_base, t, tlast, lane, m, g, ka);
-    else issue_tile<D, RESID, WIDE, false>(a, buf, kbase, vbase, row_base, t, tlast, lane, m, g, ka);
+    if (full) issue_tile<D, RESID, WIDE, true, true, true, SWZ8>(a, buf, kbase, vbase, row_base, t, tlast, lane, m, g, ka);
+    else issue_tile<D, RESID, WIDE, false, true, true, SWZ8>(a, buf, kbase, vbase, row_base, t, tlast, lane, m, g, ka);
   }
 }
 
@@ -975,7 +978,7 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
     if constexpr (WIDE) {
       const int e8 = a.n8, e4 = e8 + a.n4, e3 = e4 + a.n3, e2 = e3 + a.n2;
       for (int li = 0; li < e8; ++li)
-        residual_scores<D, NB, 8, false>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
+        residual_scores<D, NB, 8, NB == 1>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
       for (int li = e8; li < e4; ++li)
         residual_scores<D, NB, 4, false>(a, li, buf + slot_lds_offset<D, true>(a, li), qtB, qtL, qoff, qmul, my_loop, sc, m, g, k);
       for (int li = e4; li < e3; ++li)
@@ -1331,7 +1334,7 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
       const uint16_t* qs = a.q + (qr >= 0 ? qr : 0) * D + 32 * cks + 16 * (cg >> 1) + 4 * (cg & 1);
       const uint2 q0 = qr >= 0 ? *reinterpret_cast<const uint2*>(qs) : make_uint2(0, 0);
       const uint2 q1 = qr >= 0 ? *reinterpret_cast<const uint2*>(qs + 8) : make_uint2(0, 0);
-      if (t0 < t_end) issue_at<D, RESID, WIDE, PAGED>(a, buf, kbase, vbase, row_base, b, kvh, z, t0, t_end, lane, m, g, ka);
+      if (t0 < t_end) issue_at<D, RESID, WIDE, PAGED, NB == 1>(a, buf, kbase, vbase, row_base, b, kvh, z, t0, t_end, lane, m, g, ka);
       wait_vmem();
       // x[p][i]: coordinate base + i + 8p. Butterflies on coordinate bits 0, 1
       // and 3 in the lane, then across the row's lanes: the k-step bits (lane
@@ -1422,7 +1425,7 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   } else {
     for (; t0 < t_end; t0 += kStep) {
       if (!tile_valid<PAGED>(a, b, t0)) continue;  // no valid page: the tile takes no weight
-      issue_at<D, RESID, WIDE, PAGED>(a, buf, kbase, vbase, row_base, b, kvh, z, t0, t_end, lane, m, g, ka);
+      issue_at<D, RESID, WIDE, PAGED, NB == 1>(a, buf, kbase, vbase, row_base, b, kvh, z, t0, t_end, lane, m, g, ka);
       wait_vmem();
       wave_sync_lds();
       compute_tile<D, NB, RESID, WIDE>(a, buf, t0, t_end, m, g, ka, qB, qtB, qtL, qoff, qmul, my_loop, o_ref, o_res,
