@@ -590,10 +590,7 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
           if (lv.bits != want) continue;
           a.loop_id[li] = l;
           a.bits[li] = lv.bits;
-          a.kc[li] = lv.k_codes;
-          a.ks[li] = lv.k_scales;
-          a.vc[li] = lv.v_codes;
-          a.vs[li] = lv.v_scales;
+          a.slot[li] = SlotPtrs{lv.k_codes, lv.k_scales, lv.v_codes, lv.v_scales};
           if (want == 8) ++a.n8;
           if (want == 4) ++a.n4;
           if (want == 3) ++a.n3;

@@ -430,14 +430,15 @@ __device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned
   unsigned char* ks_l = kc_l + 128 * W;
   unsigned char* vc_l = ks_l + 64 * NG;
   unsigned char* vs_l = vc_l + 128 * W;
+  const SlotPtrs sp = a.slot[li];
   if constexpr (FULL) {
     // All 32 tokens lie inside the sequence: buffer loads with the row as the
     // resource, the tile start as the scalar offset and per-lane constants.
     const uint32_t S = (uint32_t)a.seq_len;
-    const auto kc_r = row_rsrc(a.kc[li] + row_base * W, S * 4u * W);
-    const auto vc_r = row_rsrc(a.vc[li] + row_base * W, S * 4u * W);
-    const auto ks_r = row_rsrc(a.ks[li] + row_base * NG, S * 2u * NG);
-    const auto vs_r = row_rsrc(a.vs[li] + row_base * NG, S * 2u * NG);
+    const auto kc_r = row_rsrc(sp.kc + row_base * W, S * 4u * W);
+    const auto vc_r = row_rsrc(sp.vc + row_base * W, S * 4u * W);
+    const auto ks_r = row_rsrc(sp.ks + row_base * NG, S * 2u * NG);
+    const auto vs_r = row_rsrc(sp.vs + row_base * NG, S * 2u * NG);
     const uint32_t tc = (uint32_t)t0 * 4u * W, ts = (uint32_t)t0 * 2u * NG;
     const uint32_t kc_lane = 16u * (uint32_t)(lane ^ ((lane >> 4) & kKcSwz<D, BITS, SWZ>));
 #pragma unroll
@@ -460,7 +461,7 @@ __device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned
       const int c = 64 * i + lane;
       if (8 * W >= 64 * (i + 1) || c < 8 * W) {
         const int tok = c / (W / 4), q4 = (c % (W / 4)) ^ ((c >> 4) & kKcSwz<D, BITS, SWZ>);
-        dma16(a.kc[li] + (row_base + min(t0 + tok, tlast)) * W + 4 * q4, kc_l + 1024 * i);
+        dma16(sp.kc + (row_base + min(t0 + tok, tlast)) * W + 4 * q4, kc_l + 1024 * i);
       }
     }
   } else {
@@ -470,7 +471,7 @@ __device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned
       const int idx = 64 * i + lane;
       if (32 * W >= 64 * (i + 1) || idx < 32 * W) {
         const int tok = idx / W, wd = idx % W;
-        dma4(a.kc[li] + (row_base + min(t0 + tok, tlast)) * W + wd, kc_l + 256 * i);
+        dma4(sp.kc + (row_base + min(t0 + tok, tlast)) * W + wd, kc_l + 256 * i);
       }
     }
   }
@@ -478,14 +479,14 @@ __device__ __forceinline__ void stage_loop(const DecodeArgs& a, int li, unsigned
   if (16 * NG >= 64 || lane < 16 * NG) {
     const int tok = lane / (NG / 2), pr = lane % (NG / 2);
     const int64_t vec = row_base + min(t0 + tok, tlast);
-    dma4(a.ks[li] + vec * NG + 2 * pr, ks_l);
-    dma4(a.vs[li] + vec * NG + 2 * pr, vs_l);
+    dma4(sp.ks + vec * NG + 2 * pr, ks_l);
+    dma4(sp.vs + vec * NG + 2 * pr, vs_l);
   }
   // V code words transposed: slot idx -> word idx / 32 of token idx % 32
 #pragma unroll
   for (int i = 0; i < W / 2; ++i) {
     const int idx = 64 * i + lane;
-    dma4(a.vc[li] + (row_base + min(t0 + (idx & 31), tlast)) * W + (idx >> 5), vc_l + 256 * i);
+    dma4(sp.vc + (row_base + min(t0 + (idx & 31), tlast)) * W + (idx >> 5), vc_l + 256 * i);
   }
 }
 

@@ -55,15 +55,21 @@ struct ReconstructArgs {
 // reads the query of loop loop_id[li] + blockIdx.y, query head kvh * G + j.
 // Slots are ordered INT8, INT4, INT3, INT2, reference-only. In the bf16
 // baseline each launch has one slot (loop_id 0) and blockIdx.y picks the loop.
+// One residual slot's tensors, together: a tile's issue loads all four with
+// one scalar load.
+struct SlotPtrs {
+  const uint32_t* kc;
+  const uint16_t* ks;
+  const uint32_t* vc;
+  const uint16_t* vs;
+};
+
 struct DecodeArgs {
   const uint16_t* q;                    // [n_loops_total][B][Hq][D]
   const uint16_t* k[kMaxLoops];         // per blockIdx.z: the K this block streams
   const uint16_t* v[kMaxLoops];
   int32_t bits[kMaxLoops];              // per slot li: 8, 4, 3, 2, then 0 (reference only)
-  const uint32_t* kc[kMaxLoops];
-  const uint16_t* ks[kMaxLoops];
-  const uint32_t* vc[kMaxLoops];
-  const uint16_t* vs[kMaxLoops];
+  SlotPtrs slot[kMaxLoops];             // per slot li: its K / V codes and scales
   float* ws;                            // partials [n_loops_total][B][Hq][n_splits][2D + 2]
   const unsigned char* qprep;           // rotated-query records [n_loops_total][B][Hq], or NULL: a
                                         // residual launch at NB = 1 rotates the queries itself
