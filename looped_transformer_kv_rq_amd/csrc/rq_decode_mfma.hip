@@ -97,6 +97,20 @@ __device__ __forceinline__ uint32_t mix_pair(float p0, uint32_t w0, float p1, ui
   }
   return r;
 }
+// Maximum of v over lanes l, l^16, l^32 and l^48 (a row's four lane groups),
+// by the gfx950 row-swap permutes: with both operands v, permlane16_swap gives
+// each lane the values of its even and its odd 16-lane row, permlane32_swap
+// those of its lower and upper 32-lane half. No LDS round trip on the softmax's
+// path, as a bpermute shuffle would take.
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 // 2^x by v_exp_f32 alone (no denormal-range fix-up): softmax weights below
 // 2^-126 of the running maximum count as zero. 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -1009,8 +1023,7 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, const unsigned
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 8; ++j) mx = fmaxf(mx, zz[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor16_32(mx);
     const float m_new = fmaxf(m_run[nb], mx);
     const float alpha = fast_exp2(m_run[nb] - m_new);
     m_run[nb] = m_new;
