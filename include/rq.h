@@ -269,15 +269,23 @@ int rq_encode_layers(const rq_shape* shape, int32_t n_layers, int32_t n_loops, c
 
 /* Split count rq_decode_attn / rq_decode_attn_bf16 will use for a request of
  * n_splits (0 = automatic). Splits hold whole 64-position units. The automatic
- * count depends on the shape, n_q_heads and n_loops only: it is the one with
- * the least modelled time ceil(B*Hkv*n / R) * (1/n + 384/seq_len), R being the
- * partial blocks the device holds at once (512 for at most 16 query rows per
- * kv head, 1024 for more rows of at most 16 heads each, 256 above 16 heads).
+ * count depends on the shape, n_q_heads, n_loops and the loops' widths: it is
+ * the one with the least modelled time ceil(B*Hkv*n / R) * (1/n + 384/seq_len),
+ * R being the partial blocks the device holds at once (512 for at most 16
+ * query rows per kv head, 256 when those rows' loops stage too much per tile
+ * for two blocks per CU (INT8 loops), 1024 for more rows of at most 16 heads
+ * each, 256 above 16 heads).
+ *   bits: host array [n_loops] of the call's widths (0, 2, 3, 4 or 8, as in
+ *         its rq_loop_view array), or NULL for widths that fit two blocks per
+ *         CU; rq_decode_attn_bf16 plans as if NULL.
  * Host only. Returns <= 0 on invalid arguments. */
-int32_t rq_decode_attn_splits(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits);
+int32_t rq_decode_attn_splits(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const int32_t* bits,
+                              int32_t n_splits);
 
 /* Workspace bytes needed by rq_decode_attn and rq_decode_attn_bf16 for these
- * arguments (host only; 0 on invalid arguments). The caller allocates it. */
+ * arguments, whatever the loops' widths (an automatic count sizes for the
+ * larger of its two possible plans). Host only; 0 on invalid arguments. The
+ * caller allocates it. */
 size_t rq_decode_attn_workspace(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits);
 
 /* Fused decode attention over the residual cache (ResidualQuant, newx.sg

@@ -100,7 +100,7 @@ def _load():
         "rq_decode_attn_paged": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, P, P, ctypes.POINTER(_LoopView),
                                                 ctypes.POINTER(_Pages), P, I32, PP, PP, F, I32, P, P, SZ, P]),
         "rq_reconstruct_rotonly": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, P, P, I32, P, P]),
-        "rq_decode_attn_splits": (I32, [ctypes.POINTER(_Shape), I32, I32, I32]),
+        "rq_decode_attn_splits": (I32, [ctypes.POINTER(_Shape), I32, I32, ctypes.POINTER(I32), I32]),
         "rq_decode_attn_workspace": (SZ, [ctypes.POINTER(_Shape), I32, I32, I32]),
         "rq_decode_attn": (ctypes.c_int, [ctypes.POINTER(_Shape), I32, I32, P, P, P, ctypes.POINTER(_LoopView),
                                           F, I32, P, P, SZ, P]),
@@ -320,9 +320,15 @@ def reconstruct(ref: torch.Tensor, codes: Optional[torch.Tensor], scales: Option
 
 
 def decode_splits(batch: int, n_kv_heads: int, seq_len: int, head_dim: int, n_q_heads: int, n_loops: int,
-                  n_splits: int = 0) -> int:
+                  n_splits: int = 0, bits: Optional[Sequence[int]] = None) -> int:
+    """Split count of a decode call; bits: the loops' widths (None: widths that fit two blocks per CU)."""
     shp = _Shape(batch, n_kv_heads, seq_len, head_dim)
-    return _load().rq_decode_attn_splits(ctypes.byref(shp), n_q_heads, n_loops, n_splits)
+    arr = None
+    if bits is not None:
+        if len(bits) != n_loops:
+            raise ValueError("bits needs one width per loop")
+        arr = (ctypes.c_int32 * n_loops)(*bits)
+    return _load().rq_decode_attn_splits(ctypes.byref(shp), n_q_heads, n_loops, arr, n_splits)
 
 
 def decode_workspace_bytes(batch: int, n_kv_heads: int, seq_len: int, head_dim: int, n_q_heads: int,

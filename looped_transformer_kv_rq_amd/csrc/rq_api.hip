@@ -44,25 +44,41 @@ int check_heads(const rq_shape* s, int32_t n_q_heads, int32_t n_loops) {
 // many as the device holds at once: two 4-wave blocks per CU (one 16-row set),
 // four 2-wave blocks (paired sets, more than 16 query rows of at most 16 per
 // kv head) or one (32-row blocks, more than 16 query heads per kv head), on
-// 256 CUs. A round that is only partly full leaves CUs idle for a whole block
-// time, and every block also pays a fixed start and merge (taken as 6 tiles of
-// tokens). The plan takes the split count with the least modelled time,
+// 256 CUs. A 16-row launch whose four waves stage more than half a CU's LDS
+// per tile (INT8 loops) also holds one block per CU. A round that is only
+// partly full leaves CUs idle for a whole block time, and every block also
+// pays a fixed start and merge (taken as 6 tiles of tokens). The plan takes
+// the split count with the least modelled time,
 //   ceil(rows * n / round) * (1 / n + 6 * 64 / seq_len)   (in row times),
 // the smallest such n on ties. This keeps the best points of split sweeps on
-// l4_b16_s4k (4) and mixed_s32k (8), and at the peak batch (10,720 rows in
-// rounds of 1,024 blocks) takes 2 splits, whose 21 rounds of half-length
-// blocks end 5% sooner than 11 full-length ones. A split never holds fewer
-// tokens than one 64-token unit.
+// l4_b16_s4k (4) and mixed_s32k (8; 4 with an INT8 loop), and at the peak
+// batch (10,720 rows in rounds of 1,024 blocks) takes 2 splits, whose 21
+// rounds of half-length blocks end 5% sooner than 11 full-length ones. A
+// split never holds fewer tokens than one 64-token unit.
 
 struct SplitPlan {
   int32_t n_splits;
   int32_t tokens_per_split;
 };
 
-int64_t round_blocks(const rq_shape* s, int32_t n_q_heads, int32_t n_loops) {
+// Blocks per round for a call with these loop widths (bits: host [n_loops],
+// or nullptr for widths whose 16-row blocks fit two to a CU). Of a 16-row
+// call the first launch decides: it holds as many loops as four waves' tiles
+// fit in one block's LDS.
+int64_t round_blocks(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, const int32_t* bits) {
   const int64_t G = n_q_heads / s->n_kv_heads;
   if (G > 16) return 256;
   if (G * n_loops > 16) return 1024;
+  if (bits != nullptr) {
+    int32_t first[kMaxLoops];
+    int nl = 0;
+    for (int i = 0; i < n_loops && i < kMaxLoops; ++i) {
+      first[nl] = bits[i];
+      if (nl > 0 && 4 * decode_wave_lds_bytes(s->head_dim, first, nl + 1) > kMaxBlockLds) break;
+      ++nl;
+    }
+    if (8 * decode_wave_lds_bytes(s->head_dim, first, nl) > kMaxBlockLds) return 256;
+  }
   return 512;
 }
 
@@ -77,10 +93,8 @@ static SplitPlan realize_splits(int64_t seq_len, int64_t n) {
   return {(int32_t)((seq_len + tps - 1) / tps), (int32_t)tps};
 }
 
-SplitPlan plan_splits(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int32_t requested) {
-  if (requested > 0) return realize_splits(s->seq_len, requested);
+static SplitPlan plan_for_round(const rq_shape* s, int64_t round) {
   const int64_t rows = (int64_t)s->batch * s->n_kv_heads;
-  const int64_t round = round_blocks(s, n_q_heads, n_loops);
   const double fixed = 6.0 * kDecodeTile / (double)s->seq_len;
   SplitPlan best_plan = realize_splits(s->seq_len, 1);
   double best = 0.0;
@@ -94,6 +108,19 @@ SplitPlan plan_splits(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int
     }
   }
   return best_plan;
+}
+
+SplitPlan plan_splits(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, const int32_t* bits, int32_t requested) {
+  if (requested > 0) return realize_splits(s->seq_len, requested);
+  return plan_for_round(s, round_blocks(s, n_q_heads, n_loops, bits));
+}
+
+// The most splits an automatic plan takes for any loop widths: what the
+// workspace query sizes for
+static int32_t max_auto_splits(const rq_shape* s, int32_t n_q_heads, int32_t n_loops, int32_t requested) {
+  const SplitPlan p = plan_splits(s, n_q_heads, n_loops, nullptr, requested);
+  if (requested > 0 || round_blocks(s, n_q_heads, n_loops, nullptr) != 512) return p.n_splits;
+  return std::max(p.n_splits, plan_for_round(s, 256).n_splits);
 }
 
 // Workspace: split partials [n_loops][B][Hq][n_splits][2D + 2] floats, padded
@@ -430,14 +457,20 @@ int rq_reconstruct_rotonly(const rq_shape* shape, int32_t bits, const uint32_t* 
   return reconstruct_common(shape, bits, nullptr, codes, scales, out_dtype, out, stream);
 }
 
-int32_t rq_decode_attn_splits(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits) {
+int32_t rq_decode_attn_splits(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const int32_t* bits,
+                              int32_t n_splits) {
   if (check_heads(shape, n_q_heads, n_loops) != RQ_OK || n_splits < 0) return 0;
-  return plan_splits(shape, n_q_heads, n_loops, n_splits).n_splits;
+  if (bits != nullptr) {
+    for (int i = 0; i < n_loops; ++i) {
+      if (bits[i] != 0 && !residual_width(bits[i])) return 0;
+    }
+  }
+  return plan_splits(shape, n_q_heads, n_loops, bits, n_splits).n_splits;
 }
 
 size_t rq_decode_attn_workspace(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, int32_t n_splits) {
   if (check_heads(shape, n_q_heads, n_loops) != RQ_OK || n_splits < 0) return 0;
-  return workspace_bytes_for(shape, n_q_heads, n_loops, plan_splits(shape, n_q_heads, n_loops, n_splits).n_splits);
+  return workspace_bytes_for(shape, n_q_heads, n_loops, max_auto_splits(shape, n_q_heads, n_loops, n_splits));
 }
 
 }  // extern "C"
@@ -490,7 +523,9 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
   }
   // Ragged prefixes with an automatic split count: length-balanced splits.
   const bool balanced = seq_lens != nullptr && n_splits == 0;
-  const SplitPlan plan = plan_splits(shape, n_q_heads, n_loops, n_splits);
+  int32_t widths[kMaxLoops];
+  for (int i = 0; i < n_loops; ++i) widths[i] = loops[i].bits;
+  const SplitPlan plan = plan_splits(shape, n_q_heads, n_loops, widths, n_splits);
   const int32_t prefix_recs =
       balanced ? balanced_max_row_splits((int64_t)shape->batch * shape->n_kv_heads, shape->seq_len) : plan.n_splits;
   const int32_t rec_splits = prefix_recs + (tail_len > 0 ? 1 : 0);
@@ -683,7 +718,7 @@ size_t rq_decode_attn_varlen_workspace(const rq_shape* shape, int32_t n_q_heads,
   if (check_heads(shape, n_q_heads, n_loops) != RQ_OK || n_splits < 0 || tail_len < 0) return 0;
   if (n_splits == 0) return balanced_workspace_bytes(shape, n_q_heads, n_loops, tail_len);
   return workspace_bytes_for(shape, n_q_heads, n_loops,
-                             plan_splits(shape, n_q_heads, n_loops, n_splits).n_splits + (tail_len > 0 ? 1 : 0));
+                             plan_splits(shape, n_q_heads, n_loops, nullptr, n_splits).n_splits + (tail_len > 0 ? 1 : 0));
 }
 
 int rq_decode_attn_varlen(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const uint16_t* q,
@@ -775,7 +810,7 @@ int rq_decode_attn_bf16(const rq_shape* shape, int32_t n_q_heads, int32_t n_loop
   for (int i = 0; i < n_loops; ++i) {
     if (!aligned16(k[i]) || !aligned16(v[i])) return RQ_EALIGN;
   }
-  const SplitPlan plan = plan_splits(shape, n_q_heads, n_loops, n_splits);
+  const SplitPlan plan = plan_splits(shape, n_q_heads, n_loops, nullptr, n_splits);
   if (workspace == nullptr || workspace_bytes < workspace_bytes_for(shape, n_q_heads, n_loops, plan.n_splits))
     return RQ_EWORKSPACE;
   if (!aligned16(workspace)) return RQ_EALIGN;

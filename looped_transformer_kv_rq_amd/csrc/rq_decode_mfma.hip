@@ -1199,13 +1199,23 @@ __device__ __forceinline__ bool balanced_split(const DecodeArgs& a, int work, in
 template <int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
 constexpr bool kRotatesQueries = NB == 1 && RESID && !WIDE && !PAGED && SETS == 1;
 
+// Blocks of the 16-row INT3 / INT8 kernel take their wave count from the
+// launch (4 to kMaxWaves): an INT8 loop stages so much per wave that two
+// 4-wave blocks do not fit one CU's LDS, and one block of more waves keeps
+// more tiles in flight than one of four. Every other kernel runs four.
+constexpr int kMaxWaves = 8;
+template <int NB, bool RESID, bool WIDE, int SETS>
+constexpr bool kVarWaves = NB == 1 && RESID && WIDE && SETS == 1;
+
 // SETS: the launch's argument sets (1 or 2). With one, a block is four
-// waves over one (batch, kv head, split), each taking every fourth tile. With
+// waves (kVarWaves: blockDim.x / 64) over one (batch, kv head, split), each
+// taking every fourth (every blockDim.x / 64-th) tile. With
 // two (paired launches), a block is two waves over one (batch, kv head,
 // split): wave s computes set s's rows, both walk every tile of the split and
 // share its reference K and V through LDS, each issuing half of the loads.
 template <int D, int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RESID && NB == 2 ? 1 : 2,
+__global__ __launch_bounds__((kVarWaves<NB, RESID, WIDE, SETS> ? 64 * kMaxWaves : 256))
+__attribute__((amdgpu_waves_per_eu(RESID && NB == 2 ? 1 : 2,
                                                                      RESID && NB == 1 ? 2 : 4)))
 void rq_decode_partial_mfma(DecodeLaunch launch) {
   using Gm = MfmaGeom<D>;
@@ -1216,6 +1226,8 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: tile bases stay scalar
+  constexpr bool VW = kVarWaves<NB, RESID, WIDE, SETS>;
+  const int nw = VW ? __builtin_amdgcn_readfirstlane(blockDim.x >> 6) : 4;  // waves of a one-set block
   const int m = lane & 15, g = lane >> 4;
   constexpr bool PAIR = SETS == 2;
   const DecodeArgs& a = launch.set[PAIR ? wave : 0];
@@ -1293,10 +1305,10 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   // each set's residual slots (lds_res_base)
   unsigned char* buf = PAIR ? smem + kPairKBytes<D> : smem + wave * a.lds_wave_bytes;
   if constexpr (RESID && LP == kLoPads) {
-    // each wave copies the lo parts of rows 4 wave .. 4 wave + 3 into its pads
+    // waves 0 .. 3 copy the lo parts of rows 4 wave .. 4 wave + 3 into their pads
     constexpr int kChunks = 2 * D / 16;  // 16-byte chunks per row
     const int r = 4 * wave + lane / kChunks, j = lane % kChunks;
-    if (lane < 4 * kChunks) {
+    if (wave < 4 && lane < 4 * kChunks) {
       const int64_t qr = r < R ? ((int64_t)(a.loop_id[r / G] + z) * a.batch + b) * a.n_q_heads + kvh * G + r % G : 0;
       const uint4 v = *reinterpret_cast<const uint4*>(a.qprep + qr * Gm::PREP_BYTES + 2 * D + 16 * j);
       unsigned char* dst = QueryLo<D, NB, kLoPads>::row_of(smem, a.lds_wave_bytes, r);
@@ -1324,7 +1336,7 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   const int t_end = __builtin_amdgcn_readfirstlane(sp.t_end);
   const uint16_t* kbase = a.k[z] + row_base * D;
   const uint16_t* vbase = a.v[z] + row_base * D;
-  constexpr int kStep = PAIR ? kTile : 4 * kTile;  // tokens between a wave's consecutive tiles
+  const int kStep = PAIR ? kTile : nw * kTile;  // tokens between a wave's consecutive tiles
 
   const Consts kc = make_consts<WIDE>();
   uint4 ka[2][NG];
@@ -1467,13 +1479,13 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
     }
   }
 
-  // ------------------------------------------------ merge the four waves
+  // ------------------------------------------------- merge the block's waves
   // Each wave leaves its record for every row, [m, l, o_ref[D], o_res[D]] (the
   // residual part only with residual loops), in its LDS slot. Then each wave
-  // merges whole rows (rows wave, wave + 4, ...), its lanes across the record:
+  // merges whole rows (rows wave, wave + nw, ...), its lanes across the record:
   // the slots are summed in wave order (reproducible), each scaled by
   // 2^(m_w - max m), and the result is the row's partial record. The merge
-  // needs 4 * NR * (2D + 2) floats of LDS. In a paired launch each wave holds
+  // needs nw * NR * (2D + 2) floats of LDS. In a paired launch each wave holds
   // whole rows of its own set, and copies its slot out as the rows' records.
   constexpr int SREC = RESID ? 2 * D + 2 : D + 2;  // record floats this launch writes
   __syncthreads();
@@ -1519,17 +1531,18 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
     }
     return;
   }
-  for (int r = wave; r < R; r += 4) {
+  constexpr int MW = VW ? kMaxWaves : 4;
+  for (int r = wave; r < R; r += nw) {
     const float* s0 = slots + r * SREC;
-    float mw[4], mm = -INFINITY;
+    float mw[MW], mm = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      mw[w] = s0[w * NR * SREC];
+    for (int w = 0; w < MW; ++w) {
+      mw[w] = w < nw ? s0[w * NR * SREC] : -INFINITY;
       mm = fmaxf(mm, mw[w]);
     }
-    float fw[4];
+    float fw[MW];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) fw[w] = mw[w] == -INFINITY ? 0.0f : exp2f(mw[w] - mm);
+    for (int w = 0; w < MW; ++w) fw[w] = mw[w] == -INFINITY ? 0.0f : exp2f(mw[w] - mm);
     const int loop = a.loop_id[r / G] + z;
     const int hq = kvh * G + r % G;
     float* dst = a.ws + ((((int64_t)loop * a.batch + b) * a.n_q_heads + hq) * a.rec_splits + a.split_base + split) * REC;
@@ -1541,7 +1554,8 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
         if (e > 0) {
           val = 0.0f;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) val = fmaf(fw[w], s0[w * NR * SREC + e], val);
+          for (int w = 0; w < MW; ++w)
+            if (w < nw) val = fmaf(fw[w], s0[w * NR * SREC + e], val);
         }
         dst[e] = val;
       }
@@ -1579,13 +1593,27 @@ int query_prep_bytes(int head_dim) {
   return head_dim == 128 ? MfmaGeom<128>::PREP_BYTES : MfmaGeom<64>::PREP_BYTES;
 }
 
-// LDS bytes of one block: the larger of the merge slots and 4 wave tiles
-// (rotate: plus the 16 rows' rotated-query operands after the wave tiles)
-static int block_lds_bytes(int d, int nb, int wave_bytes, bool residual, bool rotate) {
+// LDS bytes of one block of nw waves: the larger of the merge slots and the
+// wave tiles (rotate: plus the 16 rows' rotated-query operands after them)
+static int block_lds_bytes(int d, int nb, int wave_bytes, bool residual, bool rotate, int nw = 4) {
   const int nr = 16 * nb;
-  const int merge = 4 * nr * (residual ? 2 * d + 2 : d + 2) * 4;  // every wave's records of every row
-  const int tiles = 4 * wave_bytes + (rotate ? 16 * (2 * d + 16) : 0);
+  const int merge = nw * nr * (residual ? 2 * d + 2 : d + 2) * 4;  // every wave's records of every row
+  const int tiles = nw * wave_bytes + (rotate ? 16 * (2 * d + 16) : 0);
   return merge > tiles ? merge : tiles;
+}
+
+// Waves per block of a one-set launch: four, except in the 16-row INT3 / INT8
+// kernel when two 4-wave blocks overflow a CU's LDS: then as many as one
+// block's LDS holds (at most kMaxWaves, two per SIMD), if that is six or
+// more. The waves of a block take equal shares of its tiles, and a wave that
+// shares its SIMD runs a tile about 1.3 times as long as one alone, so five
+// waves (one SIMD with two) measured slower than four on MI355X, while six
+// and seven were 15-28% faster on the mixed_s32k INT8 layers.
+static int block_waves(int d, int nb, int wave_bytes, bool residual, bool wide) {
+  if (!residual || !wide || nb != 1 || 2 * block_lds_bytes(d, nb, wave_bytes, true, false) <= kMaxBlockLds) return 4;
+  int nw = 4;
+  while (nw < kMaxWaves && block_lds_bytes(d, nb, wave_bytes, true, false, nw + 1) <= kMaxBlockLds) ++nw;
+  return nw >= 6 ? nw : 4;
 }
 
 // LDS bytes of a paired block: the shared K and V tiles, both sets' residual
@@ -1611,7 +1639,7 @@ int decode_launch_lds_bytes(const DecodeArgs* sets, int n_sets, int head_dim, bo
 }
 
 template <int D, int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
-static void launch_mfma_kernel(const DecodeLaunch& l, dim3 grid, int lds, hipStream_t stream) {
+static void launch_mfma_kernel(const DecodeLaunch& l, dim3 grid, int lds, int nw, hipStream_t stream) {
   // Lift the default dynamic-LDS cap once per instantiation and device (the
   // attribute belongs to the current device; devices past 63 set it every time).
   static std::atomic<uint64_t> lifted{0};
@@ -1623,43 +1651,47 @@ static void launch_mfma_kernel(const DecodeLaunch& l, dim3 grid, int lds, hipStr
                               hipFuncAttributeMaxDynamicSharedMemorySize, kMaxBlockLds);
     lifted.fetch_or(bit, std::memory_order_relaxed);
   }
-  hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED, SETS>), grid, dim3(SETS == 2 ? 128 : 256), lds,
-                     stream, l);
+  hipLaunchKernelGGL((rq_decode_partial_mfma<D, NB, RESID, WIDE, PAGED, SETS>), grid, dim3(64 * nw), lds, stream, l);
 }
 
 template <int D, int NB, bool PAGED, int SETS>
-static hipError_t launch_mfma_dp(const DecodeLaunch& l, dim3 grid, int lds, bool residual, bool wide,
+static hipError_t launch_mfma_dp(const DecodeLaunch& l, dim3 grid, int lds, int nw, bool residual, bool wide,
                                  hipStream_t stream) {
+  // waves per block: two in a paired launch, four in every one-set kernel
+  // except the 16-row INT3 / INT8 one, which takes 4 .. kMaxWaves
+  const bool var = kVarWaves<NB, true, true, SETS> && residual && wide;
+  if (SETS == 2 ? nw != 2 : (var ? nw < 4 || nw > kMaxWaves : nw != 4)) return hipErrorInvalidValue;
   // a residual launch without prepared records must be one that rotates the queries itself
   if (residual && l.set[0].qprep == nullptr &&
       (wide ? !kRotatesQueries<NB, true, true, PAGED, SETS> : !kRotatesQueries<NB, true, false, PAGED, SETS>))
     return hipErrorInvalidValue;
-  if (!residual) launch_mfma_kernel<D, NB, false, false, PAGED, SETS>(l, grid, lds, stream);
-  else if (wide) launch_mfma_kernel<D, NB, true, true, PAGED, SETS>(l, grid, lds, stream);
-  else launch_mfma_kernel<D, NB, true, false, PAGED, SETS>(l, grid, lds, stream);
+  if (!residual) launch_mfma_kernel<D, NB, false, false, PAGED, SETS>(l, grid, lds, nw, stream);
+  else if (wide) launch_mfma_kernel<D, NB, true, true, PAGED, SETS>(l, grid, lds, nw, stream);
+  else launch_mfma_kernel<D, NB, true, false, PAGED, SETS>(l, grid, lds, nw, stream);
   return hipSuccess;
 }
 
 template <int D, int NB>
 static hipError_t launch_mfma_d(DecodeLaunch& l, dim3 grid, bool residual, hipStream_t stream) {
-  int lds = 0;
   bool wide = false;
   for (int i = 0; i < l.n_sets; ++i) {
     DecodeArgs& a = l.set[i];
     a.lds_wave_bytes = decode_wave_lds_bytes(D, a.bits, residual ? a.n_loops_launch : 0);
-    lds = std::max(lds, block_lds_bytes(D, NB, a.lds_wave_bytes, residual, residual && NB == 1 && a.qprep == nullptr));
     wide = wide || a.n8 + a.n3 > 0;
   }
   const bool paged = l.set[0].block_table != nullptr;
   if (l.n_sets == 2) {  // two sets of at most 16 rows: one wave each, sharing the reference tiles
     l.set[0].lds_res_base = 0;
     l.set[1].lds_res_base = l.set[0].lds_wave_bytes - MfmaGeom<D>::VT_BYTES;
-    lds = pair_lds_bytes(D, l.set, residual);
-    if (paged) return launch_mfma_dp<D, 1, true, 2>(l, grid, lds, residual, wide, stream);
-    return launch_mfma_dp<D, 1, false, 2>(l, grid, lds, residual, wide, stream);
+    const int lds = pair_lds_bytes(D, l.set, residual);
+    if (paged) return launch_mfma_dp<D, 1, true, 2>(l, grid, lds, 2, residual, wide, stream);
+    return launch_mfma_dp<D, 1, false, 2>(l, grid, lds, 2, residual, wide, stream);
   }
-  if (paged) return launch_mfma_dp<D, NB, true, 1>(l, grid, lds, residual, wide, stream);
-  return launch_mfma_dp<D, NB, false, 1>(l, grid, lds, residual, wide, stream);
+  const DecodeArgs& a = l.set[0];
+  const int nw = block_waves(D, NB, a.lds_wave_bytes, residual, wide);
+  const int lds = block_lds_bytes(D, NB, a.lds_wave_bytes, residual, residual && NB == 1 && a.qprep == nullptr, nw);
+  if (paged) return launch_mfma_dp<D, NB, true, 1>(l, grid, lds, nw, residual, wide, stream);
+  return launch_mfma_dp<D, NB, false, 1>(l, grid, lds, nw, residual, wide, stream);
 }
 
 hipError_t launch_decode_partial(const DecodeArgs* sets, int n_sets, int head_dim, int n_z, bool residual,

@@ -400,3 +400,49 @@ def test_automatic_splits_fill_whole_rounds():
         round_blocks = 256 if g > 16 else (1024 if g * nl > 16 else 512)
         got = rq.decode_splits(b, h, s, 128, g * h, nl)
         assert got == _modelled_splits(b * h, s, round_blocks), (b, h, s, g, nl, got)
+
+
+def _wave_tile_bytes_d128(bits):
+    """LDS one wave stages per 32-token tile at D = 128: the V tile (8 rows of
+    1,024 bytes, each with a 128-byte pad), then each residual loop's K and V
+    codes (32 tokens x 128 b / 8 bytes each) and fp16 scales (32 tokens x 4
+    groups x 2 bytes each)."""
+    return 8 * 1152 + sum(256 * (128 * b // 32) + 128 * 4 for b in bits if b)
+
+
+def test_automatic_splits_follow_the_widths():
+    """A 16-row call whose first launch stages more than 20 KB per wave and tile
+    (an INT8 loop beside others) holds one block per CU, so its rounds are 256
+    blocks: the INT8 layers of the mixed_s32k states take 4 splits, not 8. The
+    first launch holds the call's loops, in order, while four waves' tiles fit
+    160 KB. The workspace query sizes for the larger of the two plans."""
+    assert rq.decode_splits(8, 8, 32768, 128, 32, 4, bits=[8, 4, 2, 0]) == 4
+    assert rq.decode_splits(8, 8, 32768, 128, 32, 4, bits=[8, 8, 2, 0]) == 4
+    assert rq.decode_splits(8, 8, 32768, 128, 32, 4, bits=[4, 3, 2, 0]) == 8
+    assert rq.decode_splits(8, 8, 32768, 128, 32, 4, bits=[4, 2, 2, 0]) == 8
+    assert rq.decode_splits(8, 8, 32768, 128, 32, 4, bits=[0, 0, 0, 0]) == 8
+    assert rq.decode_splits(8, 8, 32768, 128, 32, 4, bits=[8, 4, 2, 7]) == 0  # not a width
+    with pytest.raises(ValueError):
+        rq.decode_splits(8, 8, 32768, 128, 32, 4, bits=[8, 4, 2])
+    tables = ([8, 4, 2, 0], [8, 2, 2, 0], [4, 4, 4, 4], [8, 8, 8, 8, 8, 8, 8, 8], [2] * 8, [3, 8, 0, 0],
+              [4, 3, 2, 0], [8, 0, 0, 0])
+    for b in (1, 3, 8, 16, 48, 300):
+        for h in (1, 4, 8):
+            for s in (64, 1000, 4096, 32768):
+                for bits in tables:
+                    nl = len(bits)
+                    g = 16 // nl
+                    first = []
+                    for w in bits:
+                        if first and 4 * _wave_tile_bytes_d128(first + [w]) > 160 * 1024:
+                            break
+                        first.append(w)
+                    one_per_cu = 8 * _wave_tile_bytes_d128(first) > 160 * 1024
+                    want = _modelled_splits(b * h, s, 256 if one_per_cu else 512)
+                    got = rq.decode_splits(b, h, s, 128, g * h, nl, bits=bits)
+                    assert got == want, (b, h, s, bits, got, want)
+                    # the workspace holds either plan's split partials
+                    n_ws = max(_modelled_splits(b * h, s, 512), _modelled_splits(b * h, s, 256))
+                    part = nl * b * g * h * n_ws * (2 * 128 + 2) * 4
+                    assert rq.decode_workspace_bytes(b, h, s, 128, g * h, nl) == \
+                        (part + 255) // 256 * 256 + nl * b * g * h * 528, (b, h, s, nl)
