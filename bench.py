@@ -470,6 +470,54 @@ def peak_batch_leg(g, tiles, reps):
     return out
 
 
+def layer_table_leg(g, c, reps):
+    """Per-(layer, loop) width table: LAYER_BITS_L4 over four layers sharing
+    the case's states, so only the widths differ between layers: one
+    rq_encode_layers call per tensor, then each layer's decode."""
+    rq, torch, w = g.rq, g.torch, c.w
+    table = workloads.LAYER_BITS_L4
+    lt = {}
+    n_lay = len(table)
+
+    def enc_layers():
+        lt["k"] = rq.encode_layers([[c.kx[l] for l in c.res_loops]] * n_lay, [c.kref] * n_lay,
+                                   [row[:-1] for row in table], stream=g.stream)
+        lt["v"] = rq.encode_layers([[c.vx[l] for l in c.res_loops]] * n_lay, [c.vref] * n_lay,
+                                   [row[:-1] for row in table], stream=g.stream)
+
+    st = stats(g.reps(enc_layers, max(5, reps // 4)))
+    lt_enc_b = 2 * sum(encode_bytes(w, row[:-1]) for row in table)
+    layers = []
+    for li_, row in enumerate(table):
+        (lkc, lks), (lvc, lvs) = (lt["k"][0][li_], lt["k"][1][li_]), (lt["v"][0][li_], lt["v"][1][li_])
+        lviews = [rq.LoopView(bl, lkc[i], lks[i], lvc[i], lvs[i]) for i, bl in enumerate(row[:-1])]
+        lviews.append(rq.LoopView(0))
+
+        def dec_layer(lviews=lviews):
+            rq.decode_attn(c.q, c.kref, c.vref, lviews, out=c.out, workspace=c.ws, stream=g.stream)
+
+        dst = stats(g.reps(dec_layer, max(5, reps // 2)))
+        errs = []
+        for i, bl in enumerate(row[:-1]):
+            xq = rq.reconstruct(c.kref, lkc[i], lks[i], bl, stream=g.stream)
+            xl = c.kx[c.res_loops[i]].float()
+            errs.append(torch.linalg.vector_norm(xq - xl).item() /
+                        torch.linalg.vector_norm(xl - c.kref.float()).item())
+            del xq, xl
+        layers.append({"layer": li_, "bits": list(row), "decode": {**dst, **rate(decode_bytes(w, list(row)),
+                                                                                   dst["ms"])},
+                       "kv_tokens_per_s": c.kv_tokens / (dst["ms"] * 1e-3),
+                       "bytes_per_token_head": cache_bytes_per_token_head(w, list(row), True),
+                       "k_residual_rel_error_per_loop": errs})
+    del lt
+    return {
+        "table": [list(r) for r in table], "encode_all_layers": {**st, **rate(lt_enc_b, st["ms"])},
+        "layers": layers,
+        "what": f"rq_encode_layers of K and V over {n_lay} layers sharing the {w.name} states, then "
+                "rq_decode_attn per layer with its row of the table",
+    }
+
+
 def main_side_legs(g, c, reps):
     """Side measurements on the main workload's cache (encoded once here)."""
     torch, rq, w = g.torch, g.rq, c.w
@@ -557,50 +605,9 @@ def main_side_legs(g, c, reps):
     }
     del ro
 
-    # Per-(layer, loop) width table: LAYER_BITS_L4 over four layers sharing
-    # these states, so only the widths differ between layers.
     if w.n_loops == len(workloads.LAYER_BITS_L4[0]):
-        table = workloads.LAYER_BITS_L4
-        lt = {}
-        n_lay = len(table)
+        res["layer_table"] = layer_table_leg(g, c, reps)
 
-        def enc_layers():
-            lt["k"] = rq.encode_layers([[c.kx[l] for l in c.res_loops]] * n_lay, [c.kref] * n_lay,
-                                       [row[:-1] for row in table], stream=g.stream)
-            lt["v"] = rq.encode_layers([[c.vx[l] for l in c.res_loops]] * n_lay, [c.vref] * n_lay,
-                                       [row[:-1] for row in table], stream=g.stream)
-
-        st = stats(g.reps(enc_layers, max(5, reps // 4)))
-        lt_enc_b = 2 * sum(encode_bytes(w, row[:-1]) for row in table)
-        layers = []
-        for li_, row in enumerate(table):
-            (lkc, lks), (lvc, lvs) = (lt["k"][0][li_], lt["k"][1][li_]), (lt["v"][0][li_], lt["v"][1][li_])
-            lviews = [rq.LoopView(bl, lkc[i], lks[i], lvc[i], lvs[i]) for i, bl in enumerate(row[:-1])]
-            lviews.append(rq.LoopView(0))
-
-            def dec_layer(lviews=lviews):
-                rq.decode_attn(c.q, c.kref, c.vref, lviews, out=c.out, workspace=c.ws, stream=g.stream)
-
-            dst = stats(g.reps(dec_layer, max(5, reps // 2)))
-            errs = []
-            for i, bl in enumerate(row[:-1]):
-                xq = rq.reconstruct(c.kref, lkc[i], lks[i], bl, stream=g.stream)
-                xl = c.kx[c.res_loops[i]].float()
-                errs.append(torch.linalg.vector_norm(xq - xl).item() /
-                            torch.linalg.vector_norm(xl - c.kref.float()).item())
-                del xq, xl
-            layers.append({"layer": li_, "bits": list(row), "decode": {**dst, **rate(decode_bytes(w, list(row)),
-                                                                                       dst["ms"])},
-                           "kv_tokens_per_s": c.kv_tokens / (dst["ms"] * 1e-3),
-                           "bytes_per_token_head": cache_bytes_per_token_head(w, list(row), True),
-                           "k_residual_rel_error_per_loop": errs})
-        res["layer_table"] = {
-            "table": [list(r) for r in table], "encode_all_layers": {**st, **rate(lt_enc_b, st["ms"])},
-            "layers": layers,
-            "what": f"rq_encode_layers of K and V over {n_lay} layers sharing the {w.name} states, then "
-                    "rq_decode_attn per layer with its row of the table",
-        }
-        del lt
 
     # Serving step (rq_decode_attn_varlen + rq_encode_append_kv): ragged prefix
     # lengths drawn in [S/2, S), every loop's current position as a one-position
@@ -683,6 +690,8 @@ def main():
     ap.add_argument("--no-peak-batch", action="store_true", help="skip the peak-batch leg (about 200 GB of HBM)")
     ap.add_argument("--only-peak-batch", action="store_true",
                     help="run only the peak-batch leg and print its figures (for profiling runs)")
+    ap.add_argument("--only-layer-table", action="store_true",
+                    help="run only the per-(layer, loop) width table leg and print its figures (for profiling runs)")
     ap.add_argument("--no-side-workloads", action="store_true", help="skip the l4_b16_s4k and heavy_tail legs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 256 MiB device-to-device copy, five times: the reference kernel "
@@ -714,6 +723,24 @@ def main():
         print("the peak-batch workload does not fit bf16 loop states for encode on one GPU; "
               "its decode is the peak-batch leg", file=sys.stderr)
         sys.exit(2)
+    if args.only_layer_table:
+        if w.n_loops != len(workloads.LAYER_BITS_L4[0]):
+            print(f"the width table has {len(workloads.LAYER_BITS_L4[0])} loops per layer; {w.name} has "
+                  f"{w.n_loops}", file=sys.stderr)
+            sys.exit(2)
+        host = host_states(w)
+        import torch
+
+        import looped_transformer_kv_rq_amd as rq
+
+        rq._load()
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        g = Gpu(torch, rq, dev)
+        case = Case(g, w, host)
+        del host
+        print(json.dumps({"layer_table": layer_table_leg(g, case, args.reps)}), flush=True)
+        return
     cpu = None if (args.no_cpu_baseline or args.only_step) else cpu_baseline(w)
 
     # every input of every leg, drawn on the host before the GPU is used
