@@ -1200,7 +1200,7 @@ template <int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
 constexpr bool kRotatesQueries = NB == 1 && RESID && !WIDE && !PAGED && SETS == 1;
 
 // The 16-row INT3 / INT8 kernel has a second instantiation (VARW) whose
-// blocks take their wave count from the launch (5 to kMaxWaves): an INT8 loop
+// blocks take their wave count from the launch (6 to kMaxWaves): an INT8 loop
 // stages so much per wave that two 4-wave blocks do not fit one CU's LDS, and
 // one block of more waves keeps more tiles in flight than one of four. Its
 // 4-wave launches, and every other kernel, run the fixed four-wave code
