@@ -273,8 +273,8 @@ int rq_encode_layers(const rq_shape* shape, int32_t n_layers, int32_t n_loops, c
  * the one with the least modelled time ceil(B*Hkv*n / R) * (1/n + 384/seq_len),
  * R being the partial blocks the device holds at once (512 for at most 16
  * query rows per kv head, 256 when those rows' loops stage too much per tile
- * for two blocks per CU (INT8 loops), 1024 for more rows of at most 16 heads
- * each, 256 above 16 heads).
+ * for two blocks per CU (INT8 loops, or several INT4 loops), 1024 for more
+ * rows of at most 16 heads each, 256 above 16 heads).
  *   bits: host array [n_loops] of the call's widths (0, 2, 3, 4 or 8, as in
  *         its rq_loop_view array), or NULL for widths that fit two blocks per
  *         CU; rq_decode_attn_bf16 plans as if NULL.

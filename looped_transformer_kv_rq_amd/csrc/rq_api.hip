@@ -45,10 +45,10 @@ int check_heads(const rq_shape* s, int32_t n_q_heads, int32_t n_loops) {
 // four 2-wave blocks (paired sets, more than 16 query rows of at most 16 per
 // kv head) or one (32-row blocks, more than 16 query heads per kv head), on
 // 256 CUs. A 16-row launch whose four waves stage more than half a CU's LDS
-// per tile (INT8 loops) also holds one block per CU. A round that is only
-// partly full leaves CUs idle for a whole block time, and every block also
-// pays a fixed start and merge (taken as 6 tiles of tokens). The plan takes
-// the split count with the least modelled time,
+// per tile (INT8 loops, or several INT4 loops) also holds one block per CU. A
+// round that is only partly full leaves CUs idle for a whole block time, and
+// every block also pays a fixed start and merge (taken as 6 tiles of tokens).
+// The plan takes the split count with the least modelled time,
 //   ceil(rows * n / round) * (1 / n + 6 * 64 / seq_len)   (in row times),
 // the smallest such n on ties. This keeps the best points of split sweeps on
 // l4_b16_s4k (4) and mixed_s32k (8; 4 with an INT8 loop), and at the peak
@@ -643,9 +643,10 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
     base += nl;
   }
   // The residual launches rotate the queries themselves when every one of
-  // them can (one 16-row block per set, a dense cache, INT2 / INT4 loops) and
-  // the rotated operands fit their blocks' LDS without costing a block per
-  // CU; otherwise one prep kernel writes every query row's record first.
+  // them can (one 16-row block per set of four waves, a dense cache, INT2 /
+  // INT4 loops) and the rotated operands fit their blocks' LDS without costing
+  // a block per CU; otherwise one prep kernel writes every query row's record
+  // first.
   bool rotate = pages == nullptr;
   for (int i = 0; i < n_launches; ++i) {
     const Launch& ln = launches[i];
@@ -657,7 +658,8 @@ int decode_impl(const rq_shape* shape, int32_t n_q_heads, int32_t n_loops, const
     }
     const int with = decode_launch_lds_bytes(ln.sets, ln.n_sets, shape->head_dim, true, true);
     const int without = decode_launch_lds_bytes(ln.sets, ln.n_sets, shape->head_dim, true, false);
-    if (ln.n_sets == 2 || rows > 16 || with > kMaxBlockLds || kMaxBlockLds / with < kMaxBlockLds / without)
+    if (ln.n_sets == 2 || rows > 16 || with > kMaxBlockLds || kMaxBlockLds / with < kMaxBlockLds / without ||
+        decode_launch_waves(ln.sets, ln.n_sets, shape->head_dim, true) != 4)
       rotate = false;
   }
   if (any_residual && !rotate) {

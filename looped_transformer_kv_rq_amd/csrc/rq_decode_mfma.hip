@@ -1199,15 +1199,16 @@ __device__ __forceinline__ bool balanced_split(const DecodeArgs& a, int work, in
 template <int NB, bool RESID, bool WIDE, bool PAGED, int SETS>
 constexpr bool kRotatesQueries = NB == 1 && RESID && !WIDE && !PAGED && SETS == 1;
 
-// The 16-row INT3 / INT8 kernel has a second instantiation (VARW) whose
-// blocks take their wave count from the launch (6 to kMaxWaves): an INT8 loop
-// stages so much per wave that two 4-wave blocks do not fit one CU's LDS, and
-// one block of more waves keeps more tiles in flight than one of four. Its
+// The 16-row residual kernels have a second instantiation (VARW) whose blocks
+// take their wave count from the launch (6 to kMaxWaves): INT8 loops, or
+// several INT4 loops, stage so much per wave that two 4-wave blocks do not
+// fit one CU's LDS, and one block of more waves keeps more tiles in flight
+// than one of four. It reads prepared query records (no in-kernel rotation).
 // 4-wave launches, and every other kernel, run the fixed four-wave code
 // (measured 1.5-5% faster than the variable-wave code at four waves).
 constexpr int kMaxWaves = 8;
 template <int NB, bool RESID, bool WIDE, int SETS>
-constexpr bool kVarWaves = NB == 1 && RESID && WIDE && SETS == 1;
+constexpr bool kVarWaves = NB == 1 && RESID && SETS == 1;
 
 // SETS: the launch's argument sets (1 or 2). With one, a block is four
 // waves (VARW: blockDim.x / 64) over one (batch, kv head, split), each
@@ -1228,7 +1229,7 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: tile bases stay scalar
-  static_assert(!VARW || kVarWaves<NB, RESID, WIDE, SETS>, "variable waves: the 16-row INT3 / INT8 kernel only");
+  static_assert(!VARW || kVarWaves<NB, RESID, WIDE, SETS>, "variable waves: the 16-row residual kernels only");
   constexpr bool VW = VARW;
   const int nw = VW ? __builtin_amdgcn_readfirstlane(blockDim.x >> 6) : 4;  // waves of a one-set block
   const int m = lane & 15, g = lane >> 4;
@@ -1345,7 +1346,7 @@ void rq_decode_partial_mfma(DecodeLaunch launch) {
   uint4 ka[2][NG];
   int t0 = t_begin + (PAIR ? 0 : wave * kTile);
   // (only where the extra copy of the tile body adds no register spills)
-  if constexpr (kRotatesQueries<NB, RESID, WIDE, PAGED, SETS>) {
+  if constexpr (kRotatesQueries<NB, RESID, WIDE, PAGED, SETS> && !VARW) {
     if (a.qprep == nullptr) {
       // The residual-score operand is computed here rather than read from
       // prepared records: the block's 16 rows go 16 / NG to a wave, 4 NG lanes
@@ -1605,15 +1606,15 @@ static int block_lds_bytes(int d, int nb, int wave_bytes, bool residual, bool ro
   return merge > tiles ? merge : tiles;
 }
 
-// Waves per block of a one-set launch: four, except in the 16-row INT3 / INT8
-// kernel when two 4-wave blocks overflow a CU's LDS: then as many as one
+// Waves per block of a one-set launch: four, except in the 16-row residual
+// kernels when two 4-wave blocks overflow a CU's LDS: then as many as one
 // block's LDS holds (at most kMaxWaves, two per SIMD), if that is six or
 // more. The waves of a block take equal shares of its tiles, and a wave that
 // shares its SIMD runs a tile about 1.3 times as long as one alone, so five
 // waves (one SIMD with two) measured slower than four on MI355X, while six
 // and seven were 15-28% faster on the mixed_s32k INT8 layers.
-static int block_waves(int d, int nb, int wave_bytes, bool residual, bool wide) {
-  if (!residual || !wide || nb != 1 || 2 * block_lds_bytes(d, nb, wave_bytes, true, false) <= kMaxBlockLds) return 4;
+static int block_waves(int d, int nb, int wave_bytes, bool residual) {
+  if (!residual || nb != 1 || 2 * block_lds_bytes(d, nb, wave_bytes, true, false) <= kMaxBlockLds) return 4;
   int nw = 4;
   while (nw < kMaxWaves && block_lds_bytes(d, nb, wave_bytes, true, false, nw + 1) <= kMaxBlockLds) ++nw;
   return nw >= 6 ? nw : 4;
@@ -1627,6 +1628,13 @@ static int pair_lds_bytes(int d, const DecodeArgs* sets, bool residual) {
   for (int i = 0; i < 2; ++i) tiles += decode_wave_lds_bytes(d, sets[i].bits, residual ? sets[i].n_loops_launch : 0) - vt;
   const int merge = 2 * 16 * (residual ? 2 * d + 2 : d + 2) * 4;
   return merge > tiles ? merge : tiles;
+}
+
+int decode_launch_waves(const DecodeArgs* sets, int n_sets, int head_dim, bool residual) {
+  if (n_sets == 2) return 2;
+  if (sets[0].n_rows > 16) return 4;
+  return block_waves(head_dim, 1, decode_wave_lds_bytes(head_dim, sets[0].bits, residual ? sets[0].n_loops_launch : 0),
+                     residual);
 }
 
 int decode_launch_lds_bytes(const DecodeArgs* sets, int n_sets, int head_dim, bool residual, bool rotate) {
@@ -1662,23 +1670,28 @@ template <int D, int NB, bool PAGED, int SETS>
 static hipError_t launch_mfma_dp(const DecodeLaunch& l, dim3 grid, int lds, int nw, bool residual, bool wide,
                                  hipStream_t stream) {
   // waves per block: two in a paired launch, four in every one-set kernel
-  // except the 16-row INT3 / INT8 one, which takes 4 .. kMaxWaves
-  const bool var = kVarWaves<NB, true, true, SETS> && residual && wide;
+  // except the 16-row residual ones, which take 4 .. kMaxWaves
+  const bool var = kVarWaves<NB, true, false, SETS> && residual;
   if (SETS == 2 ? nw != 2 : (var ? nw < 4 || nw > kMaxWaves : nw != 4)) return hipErrorInvalidValue;
-  // a residual launch without prepared records must be one that rotates the queries itself
+  // a residual launch without prepared records must be a 4-wave one that
+  // rotates the queries itself
   if (residual && l.set[0].qprep == nullptr &&
-      (wide ? !kRotatesQueries<NB, true, true, PAGED, SETS> : !kRotatesQueries<NB, true, false, PAGED, SETS>))
+      (nw != 4 ||
+       (wide ? !kRotatesQueries<NB, true, true, PAGED, SETS> : !kRotatesQueries<NB, true, false, PAGED, SETS>)))
     return hipErrorInvalidValue;
-  if (!residual) launch_mfma_kernel<D, NB, false, false, PAGED, SETS>(l, grid, lds, nw, stream);
-  else if (wide) {
-    if constexpr (kVarWaves<NB, true, true, SETS>) {
-      if (nw != 4) {
-        launch_mfma_kernel<D, NB, true, true, PAGED, SETS, true>(l, grid, lds, nw, stream);
-        return hipSuccess;
-      }
+  if (!residual) {
+    launch_mfma_kernel<D, NB, false, false, PAGED, SETS>(l, grid, lds, nw, stream);
+    return hipSuccess;
+  }
+  if constexpr (kVarWaves<NB, true, false, SETS>) {
+    if (nw != 4) {
+      if (wide) launch_mfma_kernel<D, NB, true, true, PAGED, SETS, true>(l, grid, lds, nw, stream);
+      else launch_mfma_kernel<D, NB, true, false, PAGED, SETS, true>(l, grid, lds, nw, stream);
+      return hipSuccess;
     }
-    launch_mfma_kernel<D, NB, true, true, PAGED, SETS>(l, grid, lds, nw, stream);
-  } else launch_mfma_kernel<D, NB, true, false, PAGED, SETS>(l, grid, lds, nw, stream);
+  }
+  if (wide) launch_mfma_kernel<D, NB, true, true, PAGED, SETS>(l, grid, lds, nw, stream);
+  else launch_mfma_kernel<D, NB, true, false, PAGED, SETS>(l, grid, lds, nw, stream);
   return hipSuccess;
 }
 
@@ -1699,7 +1712,7 @@ static hipError_t launch_mfma_d(DecodeLaunch& l, dim3 grid, bool residual, hipSt
     return launch_mfma_dp<D, 1, false, 2>(l, grid, lds, 2, residual, wide, stream);
   }
   const DecodeArgs& a = l.set[0];
-  const int nw = block_waves(D, NB, a.lds_wave_bytes, residual, wide);
+  const int nw = block_waves(D, NB, a.lds_wave_bytes, residual);
   const int lds = block_lds_bytes(D, NB, a.lds_wave_bytes, residual, residual && NB == 1 && a.qprep == nullptr, nw);
   if (paged) return launch_mfma_dp<D, NB, true, 1>(l, grid, lds, nw, residual, wide, stream);
   return launch_mfma_dp<D, NB, false, 1>(l, grid, lds, nw, residual, wide, stream);

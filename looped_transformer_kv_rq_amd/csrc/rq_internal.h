@@ -184,5 +184,7 @@ int decode_loop_lds_bytes(int head_dim, int bits);
 // LDS bytes one block of a partial launch takes (the largest over its sets);
 // rotate: its residual blocks rotate the queries themselves (no prepared records)
 int decode_launch_lds_bytes(const DecodeArgs* sets, int n_sets, int head_dim, bool residual, bool rotate);
+// waves per block of a decode launch (2 for a paired launch, else 4 .. 8)
+int decode_launch_waves(const DecodeArgs* sets, int n_sets, int head_dim, bool residual);
 
 }  // namespace rq

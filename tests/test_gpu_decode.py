@@ -85,6 +85,19 @@ def test_decode_tiny_one_loop(loop):
     _run_case(w, [loop], _all_rows(w))
 
 
+@pytest.mark.parametrize("bits", [(4, 4, 2, 0), (4, 4, 4, 0)])
+@pytest.mark.parametrize("s,n_splits", [(131, 0), (1000, 0), (1000, 3)])
+def test_decode_int4_heavy_tables(bits, s, n_splits):
+    """16 query rows whose INT2 / INT4 loops stage more than 20 KB per wave and
+    tile at D = 128, so two 4-wave blocks do not fit a CU: the call runs
+    seven-wave blocks over prepared query records instead of rotating the
+    queries in the kernel."""
+    print(f"decode int4-heavy bits={bits} s={s} n_splits={n_splits}", flush=True)
+    n = len(bits)
+    w = workloads.Workload("int4_heavy", 91, n, 2, 2, 8, 128, s, bits, tuple([0.2] * (n - 1) + [0.0]))
+    _run_case(w, range(n), _all_rows(w), n_splits=n_splits)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("s", [1, 63, 65, 200])
 def test_decode_ragged_lengths(d, s):

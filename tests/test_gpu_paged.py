@@ -88,7 +88,8 @@ def _hat(kref, vref, res, bits_per_loop):
 # per kv head, so the launch runs two 16-row argument sets
 @pytest.mark.parametrize("d,P,bits_per_loop,tail,hq", [
     (128, 64, (2, 4, 0), 0, 8), (128, 128, (2, 2, 0), 1, 8), (64, 64, (8, 3, 0), 2, 8), (128, 256, (4, 2, 2, 0), 1, 8),
-    (128, 64, (2, 4, 2, 2, 2, 2, 2, 0), 1, 8), (64, 128, (8, 3, 2, 0), 0, 16), (128, 64, (8, 2, 2, 0), 1, 8)])
+    (128, 64, (2, 4, 2, 2, 2, 2, 2, 0), 1, 8), (64, 128, (8, 3, 2, 0), 0, 16), (128, 64, (8, 2, 2, 0), 1, 8),
+    (128, 128, (4, 4, 2, 0), 1, 8)])
 def test_paged_decode_matches_oracle(d, P, bits_per_loop, tail, hq):
     print(f"paged d={d} P={P} bits={bits_per_loop} tail={tail} hq={hq}", flush=True)
     rng = np.random.default_rng(d + P + tail + hq)

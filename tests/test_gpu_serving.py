@@ -101,12 +101,12 @@ def _views(res, bits_per_loop):
 
 @pytest.mark.parametrize("d,hq,tail,bits_per_loop", [
     (128, 8, 0, (4, 2, 0)), (128, 8, 1, (4, 2, 0)), (64, 16, 3, (4, 2, 0)), (128, 4, 2, (4, 2, 0)),
-    (128, 8, 1, (8, 2, 2, 0)), (128, 8, 0, (8, 4, 2, 0))])
+    (128, 8, 1, (8, 2, 2, 0)), (128, 8, 0, (8, 4, 2, 0)), (128, 8, 1, (4, 4, 4, 0))])
 def test_varlen_decode_matches_oracle(d, hq, tail, bits_per_loop):
-    """The last two cases run the INT8 kernel's seven- and six-wave blocks over
-    length-balanced splits."""
+    """The last three cases run seven- and six-wave blocks (INT8, and three
+    INT4 loops) over length-balanced splits."""
     print(f"varlen d={d} hq={hq} tail={tail} bits={bits_per_loop}", flush=True)
-    rng = np.random.default_rng(d + hq + tail + (100 if bits_per_loop[0] == 8 else 0))
+    rng = np.random.default_rng(d + hq + tail + (0 if len(bits_per_loop) == 3 else 100 + bits_per_loop[1]))
     L, B, H, S = len(bits_per_loop), 7, 2, 200
     lens = np.array([0, 1, 63, 64, 65, 131, 200], dtype=np.int32)
     kref, vref, res = _cache(rng, B, H, S, d, bits_per_loop)
