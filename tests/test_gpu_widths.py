@@ -22,14 +22,16 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("bits", [(8, 3, 2, 0), (3, 3, 3, 0), (8, 8, 0), (4, 3, 0), (8, 4, 3, 2, 0), (8, 2, 2, 0),
-                                  (8, 8, 2, 0)])
+                                  (8, 8, 2, 0), (8, 8, 8, 8)])
 @pytest.mark.parametrize("hq", [8, 16])
 def test_decode_wide_tables(d, bits, hq):
     """G = 4 (one 16-row block per launch) and 8 (two blocks once there are
     three or more loops), every width order, both head sizes. At D = 128 and
     G = 4 the INT8 tables stage 20-30 KB per wave and tile: (8, 3, 2, 0) and
     (8, 8, 0) run six-wave blocks, (8, 2, 2, 0) seven, (8, 8, 2, 0) four (one
-    block per CU). With 131 positions (5 tiles) some waves get no tile."""
+    block per CU). (8, 8, 8, 8) has no reference-only loop; at D = 128 its
+    loops need two launches (three loops, then one), at D = 64 one launch of
+    seven-wave blocks. With 131 positions (5 tiles) some waves get no tile."""
     print(f"decode wide d={d} bits={bits} hq={hq}", flush=True)
     n = len(bits)
     sig = tuple([0.1] * (n - 1) + [0.0])
