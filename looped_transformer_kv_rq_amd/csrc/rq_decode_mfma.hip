@@ -1609,10 +1609,10 @@ static int block_lds_bytes(int d, int nb, int wave_bytes, bool residual, bool ro
 // Waves per block of a one-set launch: four, except in the 16-row residual
 // kernels when two 4-wave blocks overflow a CU's LDS: then as many as one
 // block's LDS holds (at most kMaxWaves, two per SIMD), if that is six or
-// more. The waves of a block take equal shares of its tiles, and a wave that
-// shares its SIMD runs a tile about 1.3 times as long as one alone, so five
-// waves (one SIMD with two) measured slower than four on MI355X, while six
-// and seven were 15-28% faster on the mixed_s32k INT8 layers.
+// more. The waves of a block take equal shares of its tiles; on MI355X five
+// waves (one SIMD holding two) ran slower than four, while six and seven ran
+// 15-28% faster on the mixed_s32k INT8 layers and about 20% faster with two
+// or three INT4 loops.
 static int block_waves(int d, int nb, int wave_bytes, bool residual) {
   if (!residual || nb != 1 || 2 * block_lds_bytes(d, nb, wave_bytes, true, false) <= kMaxBlockLds) return 4;
   int nw = 4;
