@@ -179,3 +179,54 @@ def test_layer_table_full_size_sampled_rows():
                 assert_attn_close(out[i, b, h * g:(h + 1) * g], oracle.attention(q, k, v, scale))
     del enc, kc, vc, ksc, vsc
     torch.cuda.empty_cache()
+
+
+def test_int8_layer_mixed_s32k_sampled_row():
+    """The INT8 layer of the bench's width table at its own size: the (8, 4, 2,
+    0) row of LAYER_BITS_L4 over the mixed_s32k states (B = 8, 8 / 32 heads,
+    32K positions), encoded by rq_encode, then decoded with the automatic plan
+    the bench times (six-wave blocks, 4 splits). One sampled (b, kv head) row:
+    codes against the oracle, then the oracle's codes substituted and every
+    loop's rows decoded against the oracle's attention."""
+    w = workloads.WORKLOADS["mixed_s32k"]
+    row = workloads.LAYER_BITS_L4[0]
+    assert tuple(row) == (8, 4, 2, 0)
+    assert rq.decode_splits(w.batch, w.n_kv_heads, w.seq_len, w.head_dim, w.n_q_heads, w.n_loops,
+                            bits=list(row)) == 4
+    b, h = 5, 3
+    print(f"int8 layer mixed_s32k row ({b}, {h})", flush=True)
+    q_bits = workloads.q_tensor(w)
+    enc, oenc = {}, {}
+    for tensor in (workloads.TENSOR_K, workloads.TENSOR_V):
+        xs = workloads.kv_tensors(w, tensor)
+        xd = [to_dev(x) for x in xs]
+        del xs
+        codes, scales = rq.encode(xd[:-1], xd[-1], list(row[:-1]))
+        torch.cuda.synchronize()
+        st = workloads.kv_rows_all_loops(w, b, h, tensor)
+        for i, bl in enumerate(row[:-1]):
+            ow, os_ = oracle.encode(st[i], st[-1], bl)
+            oenc[(tensor, i)] = (ow, os_)
+            compare_codes(to_host_words(codes[i][b, h]), to_host_u16(scales[i][b, h]), ow, os_, st[i], st[-1], bl)
+            codes[i][b, h] = words_to_dev(ow)
+            scales[i][b, h] = to_dev(os_, torch.float16)
+        enc[tensor] = (xd[-1], codes, scales)
+        del xd
+    kref, kc, ksc = enc[workloads.TENSOR_K]
+    vref, vc, vsc = enc[workloads.TENSOR_V]
+    views = [rq.LoopView(bl, kc[i], ksc[i], vc[i], vsc[i]) for i, bl in enumerate(row[:-1])] + [rq.LoopView(0)]
+    out = rq.decode_attn(to_dev(q_bits), kref, vref, views).cpu().numpy()
+    k_st = workloads.kv_rows_all_loops(w, b, h, workloads.TENSOR_K)
+    v_st = workloads.kv_rows_all_loops(w, b, h, workloads.TENSOR_V)
+    g = w.group_size
+    scale = 1.0 / np.sqrt(w.head_dim)
+    for i, bl in enumerate(row):
+        if bl:
+            k = oracle.reconstruct(k_st[-1], *oenc[(workloads.TENSOR_K, i)], bl)
+            v = oracle.reconstruct(v_st[-1], *oenc[(workloads.TENSOR_V, i)], bl)
+        else:
+            k, v = oracle.bf16_to_f64(k_st[-1]), oracle.bf16_to_f64(v_st[-1])
+        q = oracle.bf16_to_f64(q_bits[i, b, h * g:(h + 1) * g])
+        assert_attn_close(out[i, b, h * g:(h + 1) * g], oracle.attention(q, k, v, scale))
+    del enc, kc, vc, ksc, vsc, kref, vref
+    torch.cuda.empty_cache()
