@@ -51,6 +51,22 @@ def test_noalloc_equals_decode_attn_twice_second_smaller():
         assert torch.equal(got3, want3)
 
 
+def test_noalloc_equals_decode_attn_with_many_wave_blocks():
+    """An INT8 table whose 16-row blocks run six waves and whose automatic plan
+    counts rounds of 256 blocks: the scratch holds that plan's partials too."""
+    w = workloads.Workload("noalloc_wide", 84, 4, 4, 4, 16, 128, 2000, (8, 4, 2, 0), (0.2, 0.1, 0.05, 0.0))
+    assert rq.decode_splits(w.batch, w.n_kv_heads, w.seq_len, w.head_dim, w.n_q_heads, w.n_loops,
+                            bits=list(w.bits)) != rq.decode_splits(w.batch, w.n_kv_heads, w.seq_len, w.head_dim,
+                                                                  w.n_q_heads, w.n_loops)
+    print(f"noalloc {w.name}", flush=True)
+    q, kref, vref, views = _case(w)
+    want = rq.decode_attn(q, kref, vref, views)
+    got = rq.decode_attn_noalloc(q, kref, vref, views)
+    torch.cuda.synchronize()
+    assert torch.isfinite(got).all()
+    assert torch.equal(got, want)
+
+
 def test_noalloc_rejects_a_workspace_beyond_the_scratch():
     """A call whose workspace would exceed the scratch is refused before any
     launch, and the output is left as it was."""
