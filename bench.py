@@ -276,7 +276,9 @@ def host_peak_tiles():
     packed = {l: (workloads.packed_tensors(w8, 0, l), workloads.packed_tensors(w8, 1, l))
               for l in range(w8.n_loops) if w8.bits[l]}
     return {"w": w8, "kref": workloads.ref_tensor(w8, workloads.TENSOR_K),
-            "vref": workloads.ref_tensor(w8, workloads.TENSOR_V), "q": workloads.q_tensor(w8), "packed": packed}
+            "vref": workloads.ref_tensor(w8, workloads.TENSOR_V), "q": workloads.q_tensor(w8), "packed": packed,
+            "k_states": workloads.kv_tensors(w8, workloads.TENSOR_K),
+            "v_states": workloads.kv_tensors(w8, workloads.TENSOR_V)}
 
 
 class Gpu:
@@ -417,7 +419,9 @@ def peak_batch_leg(g, tiles, reps):
     (INT4 loop 0, INT2 loops 1-6, bf16 reference) and for the bf16-KV baseline
     at its own largest batch. One decode call produces the next token of every
     sequence (all 8 loops), so tokens/s = batch / call time. The batch repeats
-    eight host-drawn entries (decode time does not depend on the values)."""
+    eight host-drawn entries (decode time does not depend on the values).
+    Then the encode of the seven residual loops of K and V (one rq_encode_kv
+    launch) at the largest batch whose bf16 states and outputs fit the budget."""
     torch, rq = g.torch, g.rq
     w8 = tiles["w"]
     torch.cuda.empty_cache()
@@ -467,6 +471,28 @@ def peak_batch_leg(g, tiles, reps):
     del ks, vs, q, o
     torch.cuda.empty_cache()
     out["rq_over_bf16_tokens_per_s"] = out["rq"]["tokens_per_s"] / out["bf16"]["tokens_per_s"]
+    # encode of all seven residual loops, K and V in one launch, at the largest
+    # batch whose bf16 states and packed outputs fit the same budget
+    b_enc = workloads.peak_batch(workloads.encode_bytes_per_sequence(w8), budget)
+    res = [l for l in range(w8.n_loops) if w8.bits[l]]
+    bits = [w8.bits[l] for l in res]
+    kx = [tile(g.bf16(x), b_enc) for x in tiles["k_states"]]
+    vx = [tile(g.bf16(x), b_enc) for x in tiles["v_states"]]
+    shp = (b_enc, w8.n_kv_heads, w8.seq_len)
+    kc = [torch.empty(shp + (w8.head_dim * b // 32,), dtype=torch.int32, device=g.dev) for b in bits]
+    vc = [torch.empty_like(x) for x in kc]
+    ksc = [torch.empty(shp + (w8.head_dim // 32,), dtype=torch.float16, device=g.dev) for _ in bits]
+    vsc = [torch.empty_like(x) for x in ksc]
+
+    def enc():
+        rq.encode_kv_into([kx[l] for l in res], [vx[l] for l in res], kx[-1], vx[-1], bits, kc, ksc, vc, vsc,
+                          stream=g.stream)
+    st = stats(g.reps(enc, reps, flush=False))
+    nbytes = 2 * encode_bytes(w8.with_batch(b_enc), bits)
+    out["encode_kv"] = {"batch": b_enc, "device_GB": b_enc * workloads.encode_bytes_per_sequence(w8) / 1e9, **st,
+                        **rate(nbytes, st["ms"]), "algorithmic_bytes_per_launch": nbytes}
+    del kx, vx, kc, vc, ksc, vsc
+    torch.cuda.empty_cache()
     return out
 
 

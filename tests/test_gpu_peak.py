@@ -11,7 +11,7 @@ import torch
 import looped_transformer_kv_rq_amd as rq
 import oracle
 import workloads
-from rq_parity import assert_attn_close, to_dev, words_to_dev
+from rq_parity import assert_attn_close, compare_codes, to_dev, to_host_u16, to_host_words, words_to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -101,3 +101,42 @@ def test_peak_batch_bf16_baseline_sampled_rows():
         for l in range(w8.n_loops):
             want[l, j] = oracle.attention(oracle.bf16_to_f64(q8[l, t, h * g:(h + 1) * g]), k, v, scale)
     assert_attn_close(got, want)
+
+
+def test_peak_batch_encode_kv_sampled_rows():
+    """rq_encode_kv of the seven residual loops of K and V in one launch, at the
+    largest batch whose bf16 states and packed outputs fit the budget (element
+    offsets past 2^32 in every state tensor), the launch the benchmark times:
+    codes and scales of sampled rows against the oracle's."""
+    w8 = workloads.WORKLOADS["peak_batch"].with_batch(workloads.PEAK_TILE)
+    batch = workloads.peak_batch(workloads.encode_bytes_per_sequence(w8), _budget())
+    print(f"peak batch encode: B = {batch}", flush=True)
+    assert batch >= 8 * workloads.PEAK_TILE
+    res = [l for l in range(w8.n_loops) if w8.bits[l]]
+    bits = [w8.bits[l] for l in res]
+    tile = workloads.tile_batch
+    st = {}
+    for tensor in (workloads.TENSOR_K, workloads.TENSOR_V):
+        xs8 = workloads.kv_tensors(w8, tensor)
+        st[tensor] = [tile(to_dev(x), batch) for x in xs8]
+        del xs8
+    shp = (batch, w8.n_kv_heads, w8.seq_len)
+    codes = {t: [torch.empty(shp + (w8.head_dim * b // 32,), dtype=torch.int32, device="cuda") for b in bits]
+             for t in st}
+    scales = {t: [torch.empty(shp + (w8.head_dim // 32,), dtype=torch.float16, device="cuda") for _ in bits]
+              for t in st}
+    K, V = workloads.TENSOR_K, workloads.TENSOR_V
+    rq.encode_kv_into([st[K][l] for l in res], [st[V][l] for l in res], st[K][-1], st[V][-1], bits,
+                      codes[K], scales[K], codes[V], scales[V])
+    torch.cuda.synchronize()
+    rows = _rows(batch)
+    got = {(t, i, b, h): (to_host_words(codes[t][i][b, h]), to_host_u16(scales[t][i][b, h]))
+           for t in st for i in range(len(bits)) for (b, h) in rows}
+    del st, codes, scales
+    torch.cuda.empty_cache()
+    for (b, h) in rows:
+        for t in (K, V):
+            row = workloads.kv_rows_all_loops(w8, b % workloads.PEAK_TILE, h, t)
+            for i, l in enumerate(res):
+                ow, os_ = oracle.encode(row[l], row[-1], bits[i])
+                compare_codes(*got[(t, i, b, h)], ow, os_, row[l], row[-1], bits[i])

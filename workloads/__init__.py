@@ -268,6 +268,13 @@ def bf16_cache_bytes_per_sequence(w: Workload, n_loops: int) -> int:
     return 2 * w.n_kv_heads * w.seq_len * 2 * w.head_dim * n_loops
 
 
+def encode_bytes_per_sequence(w: Workload) -> int:
+    """Device bytes one sequence of an all-loop encode call holds: the bf16
+    states of every loop of K and V (the final one is the reference) plus the
+    packed codes and scales the call writes for the residual loops."""
+    return bf16_cache_bytes_per_sequence(w, w.n_loops) + cache_bytes_per_sequence(w, w.bits, with_reference=False)
+
+
 def peak_batch(bytes_per_sequence: int, budget: int = PEAK_CACHE_BUDGET, multiple: int = PEAK_TILE) -> int:
     """The largest batch, a multiple of ``multiple``, whose cache fits ``budget`` bytes."""
     return int(budget // bytes_per_sequence // multiple * multiple)
