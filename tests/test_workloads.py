@@ -75,3 +75,23 @@ def test_packed_rows():
     assert words1.shape == (64, 8)  # INT2 loop
     sv1 = s1.view(np.float16).astype(np.float64)
     assert sv1.min() >= 0.0099 and sv1.max() <= 0.1001
+
+
+def test_peak_batch_bytes_per_sequence():
+    """Per-sequence byte counts of the peak-batch workload (8 loops, 4 KV heads,
+    head_dim 128, 16,384 positions): the residual cache (INT4 loop 0, INT2
+    loops 1-6, the bf16 reference), the bf16 cache of every loop, and what an
+    all-loop encode call holds on the device (all states plus its outputs).
+    Counted by hand: 65,536 vectors per tensor and sequence; a vector costs
+    256 B of bf16, 64 B of INT4 or 32 B of INT2 codes and 8 B of scales."""
+    w = workloads.WORKLOADS["peak_batch"].with_batch(workloads.PEAK_TILE)
+    vec = 2 * 4 * 16384  # K and V
+    residual = vec * (64 + 8 + 6 * (32 + 8))
+    assert workloads.cache_bytes_per_sequence(w, w.bits, with_reference=False) == residual == 40_894_464
+    assert workloads.cache_bytes_per_sequence(w, w.bits) == residual + vec * 256 == 74_448_896
+    assert workloads.bf16_cache_bytes_per_sequence(w, w.n_loops) == 8 * vec * 256 == 268_435_456
+    assert workloads.encode_bytes_per_sequence(w) == 268_435_456 + 40_894_464
+    # batches that fit 200 GB, rounded down to a multiple of the eight drawn entries
+    assert workloads.peak_batch(74_448_896) == 2680
+    assert workloads.peak_batch(268_435_456) == 744
+    assert workloads.peak_batch(268_435_456 + 40_894_464) == 640
